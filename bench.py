@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized paged-KV decode step on one MI355X.
+
+Default workload (the headline metric): INT4 split-KV decode at B=32,
+Hq=32, Hk=8, D=128, block_size=16, seq_len ~ U[1024, 8192], 8 splits.
+One step = write the step's new K/V token of every sequence into the paged
+INT4 cache (tq_reshape_and_cache_int4, 32 tokens x 8 kv heads) + decode
+attention over the whole cache (tq_decode_attention). Inputs are seeded
+synthetic data already resident in HBM; the step rotates over enough cache
+copies (> 512 MB in total) that the 256 MB Infinity Cache cannot serve
+repeats.
+
+Printed: one JSON line (rank 0). `value` is the step's algorithmic HBM
+bytes / step time in TB/s. `roofline` covers the decode call (stage 1 +
+stage 2 kernels), timed with HIP events on the stream it runs on.
+`cpu_baseline` times the CPU oracle (tests' reference implementation) on a
+bounded sample of the same step on the host cores.
+
+Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
+tq_mixed_b, write (65536 tokens x 8 heads x 128 bf16), fwht (1,048,576 rows),
+copy (device copy used to calibrate the HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12  # bytes/s, MI355X HBM3E
+HEADLINE = "INT4 split-KV decode attn: HBM TB/s (% of peak), µs/call at B=32, 8K ctx"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Events:
+    """HIP events recorded on an explicit stream (torch.cuda.Event records on
+    whichever stream it is given)."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def time(self, fn, n):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for i in range(n):
+            fn(i)
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) / n * 1e-3  # seconds per call
+
+
+def decode_bytes(w, splits_nonempty):
+    kv = int(w.seq_lens.astype(np.int64).sum()) * w.hk * (w.d + 8)
+    pages = int(sum((int(s) + w.block_size - 1) // w.block_size for s in w.seq_lens))
+    parts = int(splits_nonempty.sum()) * w.hq * (w.d + 1) * 4 * 2
+    qo = w.B * w.hq * (4 * w.d * 2 + 4) + w.B * 4
+    return dict(kv=kv, partials=parts, q_out=qo, block_table=pages * 4, total=kv + parts + qo + pages * 4)
+
+
+def nonempty_splits(seq_lens, S):
+    out = []
+    for s in seq_lens:
+        s = int(s)
+        if s == 0:
+            out.append(0)
+            continue
+        L = (s + S - 1) // S
+        out.append(sum(1 for k in range(S) if k * L < s))
+    return np.array(out)
+
+
+def run_int4(args, torch, tq, W, name):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = W.decode_workload(name)
+    log("[bench] workload", name, "tokens", w.total_tokens)
+    kb, vb = W.kv_source(w)
+    signs = torch.from_numpy(W.rht_signs(w.d)).to(dev)
+    shape = (w.num_blocks, w.block_size, w.hk, w.d // 2)
+    cache_bytes = int(np.prod(shape)) * 2 + int(np.prod(shape[:3])) * 8
+    ncopies = max(2, -(-512 * 2 ** 20 // cache_bytes) + 1)
+    key = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(dev)
+    val = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    sets = []
+    for c in range(ncopies):
+        kc = torch.empty(shape, dtype=torch.uint8, device=dev)
+        vc = torch.empty_like(kc)
+        ks = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+        vs = torch.empty_like(ks)
+        tq.tq_reshape_and_cache_int4(key, val, kc, vc, slots, k_scale_cache=ks, v_scale_cache=vs,
+                                     rht_signs=signs)
+        sets.append((kc, vc, ks, vs))
+    torch.cuda.synchronize()
+    log("[bench] %d cache copies of %.1f MB written" % (ncopies, cache_bytes / 1e6))
+    # the step's new token per sequence: the last position of each sequence
+    last = np.cumsum(w.seq_lens.astype(np.int64)) - 1
+    new_k, new_v = key[last].contiguous(), val[last].contiguous()
+    new_slots = slots[last].contiguous()
+    q = torch.from_numpy(W.query(w)).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    S = w.num_splits
+    ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.d, S) // 4, dtype=torch.float32,
+                     device=dev)
+    out = torch.empty(w.B, w.hq, w.d, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.B, w.hq, dtype=torch.float32, device=dev)
+    del key, val
+
+    sp = C.c_void_p(stream.cuda_stream)
+    writes, decodes = [], []
+    for kc, vc, ks, vs in sets:
+        writes.append(tq.prepare_reshape(new_k, new_v, kc, vc, new_slots, k_scale_cache=ks,
+                                         v_scale_cache=vs, rht_signs=signs))
+        decodes.append(tq.prepare_decode(q, bt, sl, num_kv_splits=S, key_cache=kc, value_cache=vc,
+                                         k_scale_cache=ks, v_scale_cache=vs, rht_signs=signs,
+                                         workspace=ws, out=out, lse=lse)[0])
+
+    def decode(i):
+        decodes[i % ncopies].run(sp)
+
+    def step(i):
+        writes[i % ncopies].run(sp)
+        decodes[i % ncopies].run(sp)
+
+    ev = Events(torch, stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    # decode call alone, HIP events on its stream
+    t_dec = ev.time(decode, max(args.steps, 20))
+    b = decode_bytes(w, nonempty_splits(w.seq_lens, S))
+    wb = w.B * w.hk * (2 * w.d * 2 + (w.d + 8)) + w.B * 8
+    step_bytes = b["total"] + wb
+    res = dict(w=w, wall=wall, t_dec=t_dec, bytes=b, step_bytes=step_bytes, sets=sets, q=q,
+               signs=signs)
+    return res
+
+
+def cpu_baseline_int4(res, W, budget_s):
+    """Time the oracle on a bounded sample of the step: the decode of whole
+    sequences (all query heads) until about budget_s of CPU work, on a
+    thread pool (ctypes releases the GIL); scaled to TB/s of the same
+    algorithmic bytes."""
+    import concurrent.futures as cf
+
+    import oracle
+    import torch
+    w = res["w"]
+    kc, vc, ks, vs = (t.cpu().numpy() for t in res["sets"][0])
+    q = res["q"].cpu().numpy()
+    signs = res["signs"].cpu().numpy()
+    threads = min(16, os.cpu_count() or 1)
+    order = np.argsort(w.seq_lens)  # start from short sequences
+    done_bytes, t_used, used_seqs = 0, 0.0, 0
+    pool = cf.ThreadPoolExecutor(max_workers=threads)
+    for b in order:
+        rows = np.arange(b * w.hq, (b + 1) * w.hq, dtype=np.int32)
+        chunks = np.array_split(rows, min(threads, len(rows)))
+        t0 = time.perf_counter()
+        list(pool.map(lambda r: oracle.int4_decode(q, kc, vc, ks, vs, w.block_table, w.seq_lens,
+                                                   signs, w.num_splits, w.sm_scale, r), chunks))
+        t_used += time.perf_counter() - t0
+        seq = int(w.seq_lens[b])
+        done_bytes += seq * w.hk * (w.d + 8)
+        used_seqs += 1
+        if t_used >= budget_s:
+            break
+    pool.shutdown()
+    return dict(value=done_bytes / t_used / 1e12, unit="TB/s", cores=threads, kind="oracle",
+                sample="fp64 oracle decode of %d of %d sequences (all %d query heads each), "
+                       "KV bytes only, %.1f s" % (used_seqs, w.B, w.hq, t_used))
+
+
+def _time_loop(torch, stream, fn, warmup, steps):
+    for i in range(warmup):
+        fn(i)
+    ev = Events(torch, stream)
+    return ev.time(fn, steps)
+
+
+def run_other(args, torch, tq, W):
+    """Secondary workloads: one JSON line each (not the headline metric)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = C.c_void_p(stream.cuda_stream)
+    name = args.workload
+    if name == "write":
+        wl = W.write_workload()
+        T, hk, d = wl["key"].shape
+        # enough source/cache copies to exceed the Infinity Cache
+        per = T * hk * d * 2 * 2 + wl["num_blocks"] * 16 * hk * (d // 2 + 4) * 2
+        ncopies = max(2, -(-1024 * 2 ** 20 // per))
+        key = torch.from_numpy(wl["key"].view(np.int16)).view(torch.bfloat16).to(dev)
+        val = torch.from_numpy(wl["value"].view(np.int16)).view(torch.bfloat16).to(dev)
+        slots = torch.from_numpy(wl["slot_mapping"]).to(dev)
+        signs = torch.from_numpy(W.rht_signs(d)).to(dev)
+        calls = []
+        for c in range(ncopies):
+            k2, v2 = key.clone(), val.clone()
+            kc = torch.zeros(wl["num_blocks"], 16, hk, d // 2, dtype=torch.uint8, device=dev)
+            vc = torch.zeros_like(kc)
+            ks = torch.zeros(wl["num_blocks"], 16, hk, dtype=torch.float32, device=dev)
+            vs = torch.zeros_like(ks)
+            calls.append(tq.prepare_reshape(k2, v2, kc, vc, slots, k_scale_cache=ks,
+                                            v_scale_cache=vs, rht_signs=signs))
+        t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
+        valid = int((wl["slot_mapping"] >= 0).sum())
+        nbytes = valid * hk * (2 * d * 2 + (d + 8)) + T * 8
+        line = dict(workload="write: tq_reshape_and_cache_int4 65536 tokens x 8 heads x 128 bf16, "
+                             "5% slots skipped", us=t * 1e6, algorithmic_bytes=nbytes,
+                    TBps=nbytes / t / 1e12, pct_peak=100 * nbytes / t / PEAK_HBM)
+    elif name == "fwht":
+        bits = W.fwht_rows()
+        rows = bits.shape[0]
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        ncopies = 3
+        xs = [x.clone() for _ in range(ncopies)]
+        ys = [torch.empty(rows, 128, dtype=torch.uint8, device=dev) for _ in range(ncopies)]
+        ss = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(ncopies)]
+        fn = tq.lib().fwht128_quant_fp8
+
+        def call(i):
+            j = i % ncopies
+            tq._check(fn(xs[j].data_ptr(), rows, ys[j].data_ptr(), ss[j].data_ptr(), sp))
+        t = _time_loop(torch, stream, call, args.warmup, args.steps)
+        nbytes = rows * (256 + 128 + 4)
+        line = dict(workload="fwht: fwht128_quant_fp8 1048576 rows x 128 bf16", us=t * 1e6,
+                    algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
+                    pct_peak=100 * nbytes / t / PEAK_HBM)
+    elif name == "copy":
+        n = 512 * 2 ** 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        t = _time_loop(torch, stream, lambda i: b.copy_(a), args.warmup, args.steps)
+        line = dict(workload="copy: device-to-device copy of 512 MiB", us=t * 1e6,
+                    read_bytes=n, write_bytes=n, TBps=2 * n / t / 1e12)
+    elif name in ("tq_mixed_a", "tq_mixed_b"):
+        w = W.decode_workload("tq_mixed")
+        fmt = (tq.KEY_FP8, tq.VAL_U4) if name.endswith("a") else (tq.KEY_MSE3, tq.VAL_U3)
+        sb = tq.tq_slot_bytes(w.d, *fmt)
+        shape = (w.num_blocks, w.block_size, w.hk, sb)
+        nbytes_cache = int(np.prod(shape))
+        ncopies = max(2, -(-512 * 2 ** 20 // nbytes_cache) + 1)
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        caches = []
+        for c in range(ncopies):
+            cache = torch.randint(0, 256, shape, dtype=torch.uint8, device=dev, generator=g)
+            if fmt[0] == tq.KEY_FP8:  # no NaN codes in the key bytes
+                cache[..., :w.d] &= 0x77
+            # fp16 scale / zero / norm fields: small positive values
+            kps = w.d if fmt[0] == tq.KEY_FP8 else (w.d * 3 + 7) // 8 + 2
+            vdb = (w.d * (4 if fmt[1] == tq.VAL_U4 else 3) + 7) // 8
+            for off in ([kps + vdb, kps + vdb + 2] + ([kps - 2] if fmt[0] != tq.KEY_FP8 else [])):
+                cache[..., off] = 0x00
+                cache[..., off + 1] = 0x2C
+            caches.append(cache)
+        q = torch.from_numpy(W.query(w, bf16_valued=True)).to(dev)
+        bt = torch.from_numpy(w.block_table).to(dev)
+        sl = torch.from_numpy(w.seq_lens).to(dev)
+        cen = torch.linspace(-0.2, 0.2, 8, device=dev)
+        ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.d, w.num_splits) // 4,
+                         dtype=torch.float32, device=dev)
+        calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
+                                   key_fmt=fmt[0], val_fmt=fmt[1],
+                                   centroids=cen if fmt[0] != tq.KEY_FP8 else None,
+                                   workspace=ws)[0] for c in caches]
+        t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
+        slot_used = (w.d + w.d // 2 + 4) if fmt[0] == tq.KEY_FP8 else (w.d * 3 // 8 + 2 + w.d * 3 // 8 + 4)
+        kv = int(w.seq_lens.sum()) * w.hk * slot_used
+        parts = w.B * w.hq * w.num_splits * (w.d + 1) * 8
+        nbytes = kv + parts + w.B * w.hq * (8 * w.d + 4)
+        line = dict(workload="%s: B=16 Hq=32 Hk=4 D=128 seq 16384 S=32" % name, us=t * 1e6,
+                    algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
+                    pct_peak=100 * nbytes / t / PEAK_HBM)
+    else:
+        raise SystemExit("unknown workload %s" % name)
+    line.update(steps=args.steps, warmup=args.warmup)
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_int4")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU "
+              "component in this build (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_paged_kv_tq_amd as tq
+    from quantized_paged_kv_tq_amd import workloads as W
+    tq.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload in ("llama8b_int4", "llama8b_int4_8k", "long_int4"):
+        res = run_int4(args, torch, tq, W, args.workload)
+        w, b = res["w"], res["bytes"]
+        achieved = b["total"] / res["t_dec"]
+        line = {
+            "metric": HEADLINE,
+            "value": round(res["step_bytes"] / res["wall"] / 1e12, 4),
+            "unit": "TB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(res["wall"] * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "%s: B=%d Hq=%d Hk=%d D=%d block_size=%d seq_len %s "
+                                   "(sum %d) num_kv_splits=%d, INT4 K/V" % (
+                                       w.name, w.B, w.hq, w.hk, w.d, w.block_size,
+                                       "U[1024,8192]" if w.name == "llama8b_int4" else str(int(w.seq_lens[0])),
+                                       int(w.seq_lens.sum()), w.num_splits),
+                       "global_batch": w.B, "seq_len": int(w.seq_lens.max()), "parallelism": "1 GPU"},
+            "decode_us": round(res["t_dec"] * 1e6, 2),
+            "decode_TBps": round(achieved / 1e12, 4),
+            "decode_pct_peak": round(100 * achieved / PEAK_HBM, 2),
+            "kv_only_TBps": round(b["kv"] / res["t_dec"] / 1e12, 4),
+            "roofline": {"bound": "hbm", "kernel": "tq_decode_attention (stage 1 + stage 2)",
+                         "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+                         "algorithmic_bytes": b},
+        }
+        if not args.no_cpu:
+            log("[bench] cpu baseline")
+            line["cpu_baseline"] = cpu_baseline_int4(res, W, args.cpu_budget)
+        print(json.dumps(line), flush=True)
+        return
+    run_other(args, torch, tq, W)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * tq.h -- C ABI of the MI355X (gfx950) quantized paged-KV decode library.
+ *
+ * Three operations, each enqueued on the caller's HIP stream:
+ *   tq_reshape_and_cache_int4  randomized Hadamard rotation + INT4 cache write
+ *   tq_decode_attention        split-KV decode attention over a paged,
+ *                              sub-byte-quantized cache (stage 1 + stage 2)
+ *   fwht128_quant_fp8          Hadamard-128 + power-of-two-scale FP8 quantizer
+ *
+ * Sources (web pages of a vLLM fork, cited by title and section):
+ *   int4_per_token_head.py       reshape_and_cache_int4, unified_attention_int4,
+ *                                _reshape_cache_int4_kernel, _attn_packed,
+ *                                single_rht, fast_hadamard_transform
+ *   triton_turboquant_decode.py  triton_turboquant_decode_attention,
+ *                                _tq_decode_stage1 (and its stage-2 launch)
+ *   kpool_compress.py            fwht128_quant_fp8, _fwht_quant_kernel
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" are HIP device pointers owned by the caller; the
+ *     library never allocates, frees or synchronizes, and keeps no pointer
+ *     after the call returns. `stream` is a hipStream_t (NULL: null stream).
+ *   - Tensors are dense and row-major in the shapes given (C order).
+ *   - Return value: TQ_OK, or a negative code; nothing is launched unless
+ *     TQ_OK is returned (TQ_ELAUNCH: the launch itself failed). The message of
+ *     the last failure on the calling thread is tq_last_error().
+ *   - Calls that write overlapping outputs race if enqueued on different
+ *     streams without ordering; the library adds no ordering of its own.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_OK 0
+#define TQ_EINVAL (-1)  /* invalid argument: null pointer, bad size or shape */
+#define TQ_ENOTSUP (-2) /* valid but unsupported head size / format / dtype   */
+#define TQ_ELAUNCH (-3) /* the HIP launch failed (hipGetLastError)            */
+
+/* source dtypes */
+#define TQ_DTYPE_F32 0
+#define TQ_DTYPE_F16 1
+#define TQ_DTYPE_BF16 2
+
+/* key formats */
+#define TQ_KEY_INT4 0 /* separate INT4 caches + scale words (RHT domain)     */
+#define TQ_KEY_FP8 1  /* combined slot: D bytes of OCP E4M3FN                */
+#define TQ_KEY_MSE3 2 /* combined slot: 3-bit centroid indices + fp16 norm    */
+#define TQ_KEY_MSE4 3 /* combined slot: 4-bit centroid indices + fp16 norm    */
+
+/* value formats */
+#define TQ_VAL_INT4 0 /* separate INT4 cache + scale words (with TQ_KEY_INT4) */
+#define TQ_VAL_U3 1   /* combined slot: 3-bit uniform, fp16 scale and zero    */
+#define TQ_VAL_U4 2   /* combined slot: 4-bit uniform, fp16 scale and zero    */
+
+/* tq_decode_args.flags */
+#define TQ_FLAG_GENERIC 1u /* force the format-generic vector kernel         */
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* tq_last_error(void);
+
+/* Library ABI version (incremented on incompatible changes). */
+int tq_version(void);
+
+/*
+ * INT4 cache write (int4_per_token_head.py: reshape_and_cache_int4 and
+ * _reshape_cache_int4_kernel). For every token t with slot_mapping[t] >= 0,
+ * every kv head h, and for K and V independently:
+ *   x  = fp32(src[t, h, :]) * rht_signs            (exact sign flips)
+ *   x  = FWHT(x) in fp32, butterfly strides 1, 2, ..., D/2 (Sylvester order)
+ *   x  = fp32(round_to_src_dtype(x))                (RNE; no-op for fp32)
+ *   scale = max(fl((max x - min x) / 15), fl(1e-6))
+ *   zp    = clamp(trunc(fl(-min x / scale) +- 0.5), 0, 15)
+ *   q_i   = clamp(trunc(fl(fma(x_i, fl(1/scale), zp)) +- 0.5), 0, 15)
+ *   cache[slot / bs, slot % bs, h, j] = q[2j] | q[2j+1] << 4
+ *   scale_cache[slot / bs, slot % bs, h] = bits(scale) & ~0xF | zp
+ * (+-0.5: half away from zero, as the page's where(t >= 0, t + .5, t - .5)).
+ * The output bytes are a bit-exact function of the inputs.
+ *
+ *   key, value       device, [num_tokens, Hk, D] of kv_dtype (TQ_DTYPE_*)
+ *   slot_mapping     device, [num_tokens] int64; < 0 skips the token; slots
+ *                    >= num_blocks * block_size are skipped as well
+ *   rht_signs        device, [D] fp32, each +1 or -1
+ *   key_cache, value_cache   device, [num_blocks, block_size, Hk, D/2] u8
+ *   k_scale_cache, v_scale_cache device, [num_blocks, block_size, Hk] fp32
+ *   D in {64, 128}. num_tokens == 0 returns TQ_OK without launching.
+ *   Slots must be unique (duplicates race: an unspecified writer wins).
+ */
+int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dtype,
+                              int64_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, const int64_t* slot_mapping,
+                              const float* rht_signs, uint8_t* key_cache,
+                              uint8_t* value_cache, float* k_scale_cache,
+                              float* v_scale_cache, int64_t num_blocks,
+                              int32_t block_size, void* stream);
+
+/*
+ * Decode attention, one query token per sequence.
+ *
+ * Stage 1 (triton_turboquant_decode.py, _tq_decode_stage1): sequence b is
+ * cut into num_kv_splits ranges of split_len = ceil(seq_len / S) tokens;
+ * for every non-empty split s and query head h (kv head h / (Hq / Hk)) it
+ * writes  workspace[b, h, s, 0:D] = sum_t p_t v_t / l  and
+ * workspace[b, h, s, D] = m + ln l  (online softmax, natural exp).
+ * Stage 2 (the merge the pages launch as _fwd_kernel_stage2): log-sum-exp
+ * merge of the non-empty splits into out[b, h, :] and lse[b, h].
+ *
+ * Token t of sequence b lives at page block_table[b, t / bs], row t % bs.
+ * Key / value decoding and scoring per format:
+ *   TQ_KEY_INT4 + TQ_VAL_INT4 (int4_per_token_head.py, unified_attention_int4
+ *     and _attn_packed): q' = FWHT(rht_signs * q); score = sm_scale / D *
+ *     q' . ((n - zp) * scale'), scale' = word & ~0xF, zp = word & 0xF;
+ *     values likewise; out = rht_signs * FWHT(o') / D.
+ *   TQ_KEY_FP8: score = sm_scale * q . e4m3(k).
+ *   TQ_KEY_MSE3 / MSE4: q_rot = FWHT(rot_signs * q) / sqrt(D) (rot_signs may
+ *     be NULL: all +1); score = sm_scale * norm16 * (q_rot . c[idx]), with
+ *     c / sqrt(sum c^2 + 1e-16) when norm_correction != 0.
+ *   TQ_VAL_U3 / U4: v = idx * scale16 + zero16.
+ * Combined slot layout (TQ formats): key region (FP8: D bytes; centroid:
+ * ceil(D*b/8) bytes of LSB-first b-bit indices then the fp16 norm), value
+ * indices (ceil(D*vb/8) bytes, LSB-first), fp16 scale, fp16 zero, padding to
+ * slot_bytes = tq_slot_bytes(D, key_fmt, val_fmt).
+ *
+ * Block-table entries outside [0, num_blocks) are never dereferenced (the
+ * result for that sequence is then unspecified); seq_len is clamped to
+ * max_blocks * block_size; seq_len == 0 gives out = 0 and lse = -inf.
+ * Supported: D in {64, 128}; Hq % Hk == 0 and Hq / Hk <= 16;
+ * 1 <= num_kv_splits <= 256; block_size >= 1.
+ */
+typedef struct tq_decode_args {
+  uint32_t struct_size; /* sizeof(tq_decode_args)                         */
+  uint32_t flags;       /* TQ_FLAG_*                                       */
+  int32_t B, Hq, Hk, D;
+  int32_t block_size;
+  int32_t max_blocks;    /* columns of block_table                        */
+  int32_t num_kv_splits; /* S                                             */
+  int32_t key_fmt, val_fmt;
+  int32_t norm_correction;
+  float sm_scale;        /* softmax scale, e.g. 1/sqrt(D)                 */
+  int64_t num_blocks;    /* pages in the cache(s)                          */
+  const float* query;          /* device [B, Hq, D] fp32                   */
+  const int32_t* block_table;  /* device [B, max_blocks] int32             */
+  const int32_t* seq_lens;     /* device [B] int32                         */
+  /* INT4 format */
+  const uint8_t* key_cache;    /* device [num_blocks, bs, Hk, D/2] u8      */
+  const uint8_t* value_cache;  /* device [num_blocks, bs, Hk, D/2] u8      */
+  const float* k_scale_cache;  /* device [num_blocks, bs, Hk] scale words  */
+  const float* v_scale_cache;  /* device [num_blocks, bs, Hk] scale words  */
+  const float* rht_signs;      /* device [D] +-1                            */
+  /* TurboQuant combined-slot formats */
+  const uint8_t* kv_cache;     /* device [num_blocks, bs, Hk, slot_bytes] u8 */
+  int32_t slot_bytes;
+  const float* centroids;      /* device [2^b] fp32 (centroid keys)        */
+  const float* rot_signs;      /* device [D] +-1 or NULL (centroid keys)   */
+  /* outputs */
+  float* workspace; /* device, tq_decode_workspace_bytes(B, Hq, D, S) bytes */
+  float* out;       /* device [B, Hq, D] fp32                               */
+  float* lse;       /* device [B, Hq] fp32, or NULL                         */
+} tq_decode_args;
+
+/* Bytes of the stage-1 partials ([B, Hq, S, D+1] fp32). */
+size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                 int32_t num_kv_splits);
+
+/* Padded combined-slot size for a TurboQuant format, or -1 if invalid. */
+int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt);
+
+int tq_decode_attention(const tq_decode_args* args, void* stream);
+
+/*
+ * Hadamard-128 + power-of-two-scale FP8 (kpool_compress.py,
+ * fwht128_quant_fp8 and _fwht_quant_kernel). Per row of 128 bf16 values:
+ *   x = FWHT(fp32(row)) in fp32 (strides 1..64); x = fp32(bf16(x * fl(1/sqrt 128)))
+ *   scale = 2^ceil(log2(fl(max(max|x|, 1e-4) * fl(1/448))))   (exact ceiling)
+ *   y = e4m3_rne(clamp(x / scale, -448, 448))    (OCP E4M3FN)
+ * Bit-exact function of the input.
+ *   x_bf16 device [rows, 128] bf16; y_e4m3 device [rows, 128] u8;
+ *   scale device [rows] fp32. rows == 0 returns TQ_OK without launching.
+ */
+int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
+                      float* scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,2 +1,275 @@
-"""MI355X-native quantized paged-KV decode attention (placeholder; the
-binding is filled in with the HIP library)."""
+"""MI355X (gfx950) quantized paged-KV decode attention and cache writers.
+
+Thin Python binding over the C ABI of ``libtq_amd.so`` (declared in
+``include/tq.h``): argument marshalling only -- every step of the path runs
+in the library's HIP kernels. torch supplies device memory and streams.
+
+    tq_reshape_and_cache_int4   RHT + INT4 paged-cache write
+    tq_decode_attention         split-KV decode (stage 1 + stage 2)
+    fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
+
+The library is loaded on first use; when it is missing or cannot be loaded
+the call raises (there is no fallback implementation).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq_amd.so")
+
+TQ_OK, TQ_EINVAL, TQ_ENOTSUP, TQ_ELAUNCH = 0, -1, -2, -3
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+KEY_INT4, KEY_FP8, KEY_MSE3, KEY_MSE4 = 0, 1, 2, 3
+VAL_INT4, VAL_U3, VAL_U4 = 0, 1, 2
+FLAG_GENERIC = 1
+
+
+class TQError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class DecodeArgs(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32), ("flags", C.c_uint32),
+        ("B", C.c_int32), ("Hq", C.c_int32), ("Hk", C.c_int32), ("D", C.c_int32),
+        ("block_size", C.c_int32), ("max_blocks", C.c_int32), ("num_kv_splits", C.c_int32),
+        ("key_fmt", C.c_int32), ("val_fmt", C.c_int32), ("norm_correction", C.c_int32),
+        ("sm_scale", C.c_float), ("num_blocks", C.c_int64),
+        ("query", C.c_void_p), ("block_table", C.c_void_p), ("seq_lens", C.c_void_p),
+        ("key_cache", C.c_void_p), ("value_cache", C.c_void_p),
+        ("k_scale_cache", C.c_void_p), ("v_scale_cache", C.c_void_p), ("rht_signs", C.c_void_p),
+        ("kv_cache", C.c_void_p), ("slot_bytes", C.c_int32),
+        ("centroids", C.c_void_p), ("rot_signs", C.c_void_p),
+        ("workspace", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+# Every entry point the header declares: (name, restype, argtypes).
+SYMBOLS = {
+    "tq_last_error": (C.c_char_p, []),
+    "tq_version": (C.c_int, []),
+    "tq_reshape_and_cache_int4": (C.c_int, [
+        C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
+        C.c_void_p]),
+    "tq_decode_workspace_bytes": (C.c_size_t, [C.c_int32] * 4),
+    "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
+    "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
+    "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+}
+
+
+def lib():
+    """Load libtq_amd.so (raises when it is absent: no fallback path)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    "libtq_amd.so is not built (run quantized_paged_kv_tq_amd/build.py "
+                    "or __graft_entry__.build())")
+            L = C.CDLL(LIB_PATH)
+            for name, (res, args) in SYMBOLS.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().tq_last_error().decode()
+
+
+def _check(code):
+    if code != TQ_OK:
+        raise TQError(code, last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    if isinstance(stream, C.c_void_p):
+        return stream
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, device=None):
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+
+
+_DT = {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16, torch.bfloat16: DTYPE_BF16}
+
+
+def prepare_reshape(key, value, key_cache, value_cache, slot_mapping, *, k_scale_cache,
+                    v_scale_cache, rht_signs):
+    """Validate and marshal a tq_reshape_and_cache_int4 call (see Prepared)."""
+    T, hk, d = key.shape
+    if value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key and value must share shape and dtype")
+    if key.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % key.dtype)
+    for t, n in ((key, "key"), (value, "value")):
+        _need(t, key.dtype, n)
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(rht_signs, torch.float32, "rht_signs")
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, torch.uint8, n)
+    for t, n in ((k_scale_cache, "k_scale_cache"), (v_scale_cache, "v_scale_cache")):
+        _need(t, torch.float32, n)
+    nb, bs = key_cache.shape[0], key_cache.shape[1]
+    if tuple(key_cache.shape) != (nb, bs, hk, d // 2) or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shape must be [NB, bs, Hk, D/2]")
+    if tuple(k_scale_cache.shape) != (nb, bs, hk) or v_scale_cache.shape != k_scale_cache.shape:
+        raise ValueError("scale cache shape must be [NB, bs, Hk]")
+    if slot_mapping.shape != (T,) or rht_signs.shape != (d,):
+        raise ValueError("slot_mapping must be [T], rht_signs [D]")
+    args = (_ptr(key), _ptr(value), _DT[key.dtype], T, hk, d, _ptr(slot_mapping),
+            _ptr(rht_signs), _ptr(key_cache), _ptr(value_cache), _ptr(k_scale_cache),
+            _ptr(v_scale_cache), nb, bs)
+    keep = [key, value, key_cache, value_cache, slot_mapping, k_scale_cache, v_scale_cache,
+            rht_signs]
+    return Prepared(lib().tq_reshape_and_cache_int4, args, keep)
+
+
+def tq_reshape_and_cache_int4(key, value, key_cache, value_cache, slot_mapping, *,
+                              k_scale_cache, v_scale_cache, rht_signs, stream=None):
+    """RHT + INT4 write of key/value [T, Hk, D] into the paged caches
+    ([NB, bs, Hk, D/2] u8 and [NB, bs, Hk] f32 scale words), in place."""
+    prepare_reshape(key, value, key_cache, value_cache, slot_mapping, k_scale_cache=k_scale_cache,
+                    v_scale_cache=v_scale_cache, rht_signs=rht_signs).run(stream, key.device)
+
+
+def tq_decode_workspace_bytes(B, Hq, D, num_kv_splits):
+    return lib().tq_decode_workspace_bytes(B, Hq, D, num_kv_splits)
+
+
+def tq_slot_bytes(D, key_fmt, val_fmt):
+    return lib().tq_slot_bytes(D, key_fmt, val_fmt)
+
+
+class Prepared:
+    """A library call whose arguments are marshalled once: ``run(stream)``
+    re-issues it (used by timing loops, where per-call marshalling would
+    dominate a microsecond-scale kernel)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def run(self, stream=None, device=None):
+        s = _stream(stream, device if device is not None else self._keep[0].device)
+        _check(self._fn(*self._args, s))
+
+
+def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None,
+                   key_cache=None, value_cache=None, k_scale_cache=None, v_scale_cache=None,
+                   rht_signs=None, kv_cache=None, key_fmt=KEY_INT4, val_fmt=VAL_INT4,
+                   centroids=None, rot_signs=None, norm_correction=False, num_kv_heads=None,
+                   workspace=None, out=None, lse=None, flags=0):
+    """Validate and marshal a tq_decode_attention call; returns (Prepared, out, lse)."""
+    B, hq, d = query.shape
+    _need(query, torch.float32, "query")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if key_fmt == KEY_INT4:
+        nb, bs, hk = key_cache.shape[0], key_cache.shape[1], key_cache.shape[2]
+        _need(key_cache, torch.uint8, "key_cache")
+        _need(value_cache, torch.uint8, "value_cache")
+        _need(k_scale_cache, torch.float32, "k_scale_cache")
+        _need(v_scale_cache, torch.float32, "v_scale_cache")
+        _need(rht_signs, torch.float32, "rht_signs")
+        if tuple(key_cache.shape) != (nb, bs, hk, d // 2) or value_cache.shape != key_cache.shape:
+            raise ValueError("INT4 caches must be [NB, bs, Hk, D/2]")
+        if tuple(k_scale_cache.shape) != (nb, bs, hk) or v_scale_cache.shape != k_scale_cache.shape:
+            raise ValueError("scale caches must be [NB, bs, Hk]")
+        slot_bytes = 0
+    else:
+        _need(kv_cache, torch.uint8, "kv_cache")
+        nb, bs, hk, slot_bytes = kv_cache.shape
+        if centroids is not None:
+            _need(centroids, torch.float32, "centroids")
+        if rot_signs is not None:
+            _need(rot_signs, torch.float32, "rot_signs")
+    if num_kv_heads is not None and num_kv_heads != hk:
+        raise ValueError("num_kv_heads does not match the cache")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_blocks], seq_lens [B]")
+    dev = query.device
+    if workspace is None:
+        nbytes = tq_decode_workspace_bytes(B, hq, d, num_kv_splits)
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty(B, hq, d, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
+    _need(workspace, torch.float32, "workspace")
+    _need(out, torch.float32, "out")
+    _need(lse, torch.float32, "lse")
+    if workspace.numel() * 4 < tq_decode_workspace_bytes(B, hq, d, num_kv_splits):
+        raise ValueError("workspace too small")
+    a = DecodeArgs()
+    a.struct_size = C.sizeof(DecodeArgs)
+    a.flags = flags
+    a.B, a.Hq, a.Hk, a.D = B, hq, hk, d
+    a.block_size, a.max_blocks, a.num_kv_splits = bs, block_table.shape[1], num_kv_splits
+    a.key_fmt, a.val_fmt, a.norm_correction = key_fmt, val_fmt, int(bool(norm_correction))
+    a.sm_scale = (1.0 / d ** 0.5) if sm_scale is None else sm_scale
+    a.num_blocks = nb
+    a.query, a.block_table, a.seq_lens = _ptr(query), _ptr(block_table), _ptr(seq_lens)
+    a.key_cache, a.value_cache = _ptr(key_cache), _ptr(value_cache)
+    a.k_scale_cache, a.v_scale_cache = _ptr(k_scale_cache), _ptr(v_scale_cache)
+    a.rht_signs = _ptr(rht_signs)
+    a.kv_cache, a.slot_bytes = _ptr(kv_cache), slot_bytes
+    a.centroids, a.rot_signs = _ptr(centroids), _ptr(rot_signs)
+    a.workspace, a.out, a.lse = _ptr(workspace), _ptr(out), _ptr(lse)
+    keep = [query, block_table, seq_lens, key_cache, value_cache, k_scale_cache, v_scale_cache,
+            rht_signs, kv_cache, centroids, rot_signs, workspace, out, lse]
+    return Prepared(lib().tq_decode_attention, (C.byref(a),), keep + [a]), out, lse
+
+
+def tq_decode_attention(query, block_table, seq_lens, *, stream=None, **kw):
+    """Split-KV decode attention; returns (out [B, Hq, D] f32, lse [B, Hq] f32).
+
+    INT4 format: key_cache/value_cache [NB, bs, Hk, D/2] u8, k/v_scale_cache
+    [NB, bs, Hk] f32, rht_signs [D]. TurboQuant formats: kv_cache
+    [NB, bs, Hk, slot_bytes] u8 (+ centroids for centroid keys).
+    workspace/out/lse may be passed pre-allocated (no allocation then).
+    """
+    call, out, lse = prepare_decode(query, block_table, seq_lens, **kw)
+    call.run(stream, query.device)
+    return out, lse
+
+
+def fwht128_quant_fp8(x, y=None, scale=None, stream=None):
+    """x [rows, 128] bf16 -> (y [rows, 128] float8_e4m3fn, scale [rows, 1] f32)."""
+    if x.dim() != 2 or x.shape[1] != 128:
+        raise ValueError("x must be [rows, 128]")
+    _need(x, torch.bfloat16, "x")
+    rows = x.shape[0]
+    if y is None:
+        y = torch.empty(rows, 128, dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, 1, dtype=torch.float32, device=x.device)
+    if y.shape != (rows, 128) or scale.numel() != rows:
+        raise ValueError("y must be [rows, 128], scale [rows, 1]")
+    _check(lib().fwht128_quant_fp8(_ptr(x), rows, _ptr(y), _ptr(scale), _stream(stream, x.device)))
+    return y, scale

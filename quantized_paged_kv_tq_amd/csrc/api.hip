@@ -1,0 +1,179 @@
+// C ABI of the library (include/tq.h): argument validation, format tables
+// and dispatch to the kernel launchers. Host code only.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  return fail(TQ_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int key_bits(int key_fmt) { return key_fmt == TQ_KEY_MSE3 ? 3 : (key_fmt == TQ_KEY_MSE4 ? 4 : 8); }
+int val_bits(int val_fmt) { return val_fmt == TQ_VAL_U3 ? 3 : 4; }
+
+// Combined TurboQuant slot: key region, value indices, fp16 scale, fp16 zero.
+int key_region_bytes(int d, int key_fmt) {
+  if (key_fmt == TQ_KEY_FP8) return d;
+  return (d * key_bits(key_fmt) + 7) / 8 + 2;
+}
+int value_index_bytes(int d, int val_fmt) { return (d * val_bits(val_fmt) + 7) / 8; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_last_error(void) { return g_err; }
+
+int tq_version(void) { return 1; }
+
+int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt) {
+  if (D <= 0 || D > 1024 || (D & (D - 1)) != 0) return -1;
+  if (key_fmt < TQ_KEY_FP8 || key_fmt > TQ_KEY_MSE4) return -1;
+  if (val_fmt != TQ_VAL_U3 && val_fmt != TQ_VAL_U4) return -1;
+  const int raw = key_region_bytes(D, key_fmt) + value_index_bytes(D, val_fmt) + 4;
+  return (raw + 15) / 16 * 16;
+}
+
+size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t S) {
+  if (B < 0 || Hq < 0 || D < 0 || S < 0) return 0;
+  return (size_t)B * Hq * S * (D + 1) * sizeof(float);
+}
+
+int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dtype,
+                              int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              const int64_t* slot_mapping, const float* rht_signs,
+                              uint8_t* key_cache, uint8_t* value_cache, float* k_scale_cache,
+                              float* v_scale_cache, int64_t num_blocks, int32_t block_size,
+                              void* stream) {
+  if (num_tokens < 0) return fail(TQ_EINVAL, "num_tokens < 0");
+  if (num_kv_heads <= 0) return fail(TQ_EINVAL, "num_kv_heads must be positive");
+  if (head_dim <= 0 || head_dim % 2 != 0 || (head_dim & (head_dim - 1)) != 0)
+    return fail(TQ_EINVAL, "head_dim must be an even power of two (got %d)", head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TQ_ENOTSUP, "head_dim %d not supported (64, 128)", head_dim);
+  if (kv_dtype != TQ_DTYPE_F32 && kv_dtype != TQ_DTYPE_F16 && kv_dtype != TQ_DTYPE_BF16)
+    return fail(TQ_ENOTSUP, "kv_dtype %d not supported", kv_dtype);
+  if (block_size <= 0 || num_blocks < 0) return fail(TQ_EINVAL, "bad block_size / num_blocks");
+  if (num_tokens == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (!key || !value || !slot_mapping || !rht_signs || !key_cache || !value_cache ||
+      !k_scale_cache || !v_scale_cache)
+    return fail(TQ_EINVAL, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(rht_signs, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(key_cache, 4) || !aligned(value_cache, 4) ||
+      !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (key/value/signs 16 B, caches 4 B)");
+  tqk::ReshapeParams p{key, value, slot_mapping, rht_signs, key_cache, value_cache,
+                       k_scale_cache, v_scale_cache, num_tokens, num_blocks, num_kv_heads,
+                       head_dim, kv_dtype, block_size};
+  return launched(tqk::launch_reshape_int4(p, static_cast<hipStream_t>(stream)),
+                  "tq_reshape_and_cache_int4");
+}
+
+int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3, float* scale,
+                      void* stream) {
+  if (rows < 0) return fail(TQ_EINVAL, "rows < 0");
+  if (rows == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (!x_bf16 || !y_e4m3 || !scale) return fail(TQ_EINVAL, "null pointer argument");
+  if (!aligned(x_bf16, 16) || !aligned(y_e4m3, 8) || !aligned(scale, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (x 16 B, y 8 B, scale 4 B)");
+  if (rows > ((int64_t)1 << 36)) return fail(TQ_EINVAL, "rows too large");
+  return launched(tqk::launch_fwht128_fp8(x_bf16, rows, y_e4m3, scale,
+                                          static_cast<hipStream_t>(stream)),
+                  "fwht128_quant_fp8");
+}
+
+int tq_decode_attention(const tq_decode_args* a, void* stream) {
+  if (!a) return fail(TQ_EINVAL, "null args");
+  if (a->struct_size < sizeof(tq_decode_args))
+    return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size, sizeof(tq_decode_args));
+  if (a->B < 0 || a->Hq <= 0 || a->Hk <= 0) return fail(TQ_EINVAL, "bad B / Hq / Hk");
+  if (a->Hq % a->Hk != 0) return fail(TQ_EINVAL, "Hq %% Hk != 0");
+  if (a->Hq / a->Hk > 16) return fail(TQ_ENOTSUP, "Hq / Hk > 16");
+  if (a->D <= 0 || a->D % 2 != 0 || (a->D & (a->D - 1)) != 0)
+    return fail(TQ_EINVAL, "D must be an even power of two (got %d)", a->D);
+  if (a->D != 64 && a->D != 128) return fail(TQ_ENOTSUP, "D %d not supported (64, 128)", a->D);
+  if (a->num_kv_splits < 1 || a->num_kv_splits > 256)
+    return fail(TQ_EINVAL, "num_kv_splits must be in [1, 256]");
+  if (a->block_size <= 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
+    return fail(TQ_EINVAL, "bad block_size / max_blocks / num_blocks");
+  const bool int4 = a->key_fmt == TQ_KEY_INT4;
+  if (int4 != (a->val_fmt == TQ_VAL_INT4))
+    return fail(TQ_ENOTSUP, "INT4 keys pair only with INT4 values");
+  if (a->key_fmt < TQ_KEY_INT4 || a->key_fmt > TQ_KEY_MSE4 || a->val_fmt < TQ_VAL_INT4 ||
+      a->val_fmt > TQ_VAL_U4)
+    return fail(TQ_ENOTSUP, "unknown key/value format");
+  if (a->B == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (!a->query || !a->block_table || !a->seq_lens || !a->workspace || !a->out)
+    return fail(TQ_EINVAL, "null pointer argument");
+  tqk::DecodeParams p{};
+  if (int4) {
+    if (!a->key_cache || !a->value_cache || !a->k_scale_cache || !a->v_scale_cache ||
+        !a->rht_signs)
+      return fail(TQ_EINVAL, "INT4 format needs key/value caches, scale caches and rht_signs");
+    if (!aligned(a->key_cache, 16) || !aligned(a->value_cache, 16) ||
+        !aligned(a->k_scale_cache, 4) || !aligned(a->v_scale_cache, 4))
+      return fail(TQ_EINVAL, "misaligned INT4 cache pointer (16 B / 4 B)");
+  } else {
+    const int sb = tq_slot_bytes(a->D, a->key_fmt, a->val_fmt);
+    if (!a->kv_cache) return fail(TQ_EINVAL, "TurboQuant format needs kv_cache");
+    if (a->slot_bytes < sb || a->slot_bytes % 16 != 0)
+      return fail(TQ_EINVAL, "slot_bytes %d: need a multiple of 16 >= %d", a->slot_bytes, sb);
+    if (!aligned(a->kv_cache, 16)) return fail(TQ_EINVAL, "kv_cache must be 16-byte aligned");
+    if ((a->key_fmt == TQ_KEY_MSE3 || a->key_fmt == TQ_KEY_MSE4) && !a->centroids)
+      return fail(TQ_EINVAL, "centroid keys need the centroid table");
+    p.kps = key_region_bytes(a->D, a->key_fmt);
+    p.vdb = value_index_bytes(a->D, a->val_fmt);
+  }
+  if (!aligned(a->query, 16) || !aligned(a->workspace, 16) || !aligned(a->out, 16))
+    return fail(TQ_EINVAL, "query / workspace / out must be 16-byte aligned");
+  p.B = a->B; p.hq = a->Hq; p.hk = a->Hk; p.d = a->D; p.g = a->Hq / a->Hk;
+  p.block_size = a->block_size; p.max_blocks = a->max_blocks; p.splits = a->num_kv_splits;
+  p.key_fmt = a->key_fmt; p.val_fmt = a->val_fmt; p.norm_correction = a->norm_correction;
+  p.sm_scale = a->sm_scale; p.num_blocks = a->num_blocks;
+  p.q = a->query; p.block_table = a->block_table; p.seq_lens = a->seq_lens;
+  p.kc = a->key_cache; p.vc = a->value_cache; p.ks = a->k_scale_cache; p.vs = a->v_scale_cache;
+  p.rht_signs = a->rht_signs; p.kv = a->kv_cache; p.slot_bytes = a->slot_bytes;
+  p.centroids = a->centroids; p.rot_signs = a->rot_signs;
+  p.ws = a->workspace; p.out = a->out; p.lse = a->lse;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipErrorNotSupported;
+  if (int4 && !(a->flags & TQ_FLAG_GENERIC)) e = tqk::launch_decode_int4_mfma(p, st);
+  if (e == hipErrorNotSupported) e = tqk::launch_decode_generic(p, st);
+  if (e != hipSuccess) return launched(e, "tq_decode_attention stage 1");
+  return launched(tqk::launch_merge(p, st), "tq_decode_attention stage 2");
+}
+
+}  // extern "C"

@@ -1,0 +1,295 @@
+// Format-generic split-KV decode, stage 1, on the vector ALUs.
+//
+// Covers every key/value format of the library: INT4 (int4_per_token_head.py,
+// _attn_packed and unified_attention_int4) and the TurboQuant combined slot
+// (triton_turboquant_decode.py, _tq_decode_stage1): FP8 or 3/4-bit centroid
+// keys, 3/4-bit uniform values.
+//
+// One workgroup (4 waves) per (batch, kv head, head chunk, split). The query
+// heads that share the kv head (up to G of them) are rotated/scaled once into
+// LDS. Each token is handled by D/8 lanes holding 8 dimensions each, so a
+// wave walks 64/(D/8) tokens at a time; every lane group keeps its own online
+// softmax state (running max m, sum l, accumulator) per head, and the groups
+// are merged by log-sum-exp at the end. Scores are kept in base-2 units
+// (log2(e) folded into the query), so p = exp2(s - m).
+#include <type_traits>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqk {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int N>
+__device__ __forceinline__ uint32_t load_bytes_le(const uint8_t* p) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) w |= (uint32_t)p[k] << (8 * k);
+  return w;
+}
+
+__device__ __forceinline__ float load_half_le(const uint8_t* p) {
+  const uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+  return half_lo(w);
+}
+
+template <int D, int KF, int VF, int G>
+__global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
+  constexpr int LPT = D / 8;          // lanes per token
+  constexpr int TPW = 64 / LPT;       // tokens per wave step
+  constexpr int NG = 4 * TPW;         // token groups per workgroup
+  __shared__ float qs[G][D];
+  __shared__ float cen[16];
+  __shared__ float red[4][G][D + 2];
+
+  const int nchunk = (p.g + G - 1) / G;
+  const uint32_t nblk = gridDim.x;
+  const uint32_t lb = xcd_logical_block(blockIdx.x, nblk);
+  // logical order: split fastest, then head chunk, kv head, batch
+  const int s = lb % p.splits;
+  const int hc = (lb / p.splits) % nchunk;
+  const int kvh = (lb / (p.splits * nchunk)) % p.hk;
+  const int b = lb / (p.splits * nchunk * p.hk);
+
+  int64_t seq = p.seq_lens[b];
+  const int64_t cap = (int64_t)p.max_blocks * p.block_size;
+  seq = seq < 0 ? 0 : (seq > cap ? cap : seq);
+  const int64_t split_len = (seq + p.splits - 1) / p.splits;
+  const int64_t t0 = split_len * s;
+  const int64_t t1 = (t0 + split_len < seq) ? t0 + split_len : seq;
+  if (t0 >= t1) return;  // empty split: nothing written (stage 2 skips it)
+
+  const int tid = threadIdx.x;
+  const int h0 = kvh * p.g + hc * G;               // first query head here
+  const int nh = (p.g - hc * G) < G ? (p.g - hc * G) : G;
+
+  // ---- query prologue: load, sign, rotate, fold the score constants ----
+  for (int i = tid; i < G * D; i += 256) {
+    const int hh = i / D, d = i % D;
+    float v = 0.0f;
+    if (hh < nh) {
+      v = p.q[((int64_t)b * p.hq + h0 + hh) * D + d];
+      if constexpr (KF == KF_INT4) v *= p.rht_signs[d];
+      else if constexpr (KF == KF_MSE3 || KF == KF_MSE4) {
+        if (p.rot_signs) v *= p.rot_signs[d];
+      }
+    }
+    qs[hh][d] = v;
+  }
+  if constexpr (KF == KF_MSE3 || KF == KF_MSE4) {
+    if (tid < 16) cen[tid] = tid < (KF == KF_MSE3 ? 8 : 16) ? p.centroids[tid] : 0.0f;
+  }
+  __syncthreads();
+  if constexpr (KF != KF_FP8) {
+    for (int hstride = 1; hstride < D; hstride <<= 1) {
+      for (int i = tid; i < G * D / 2; i += 256) {
+        const int hh = i / (D / 2), k = i % (D / 2);
+        const int lo = (k / hstride) * 2 * hstride + (k % hstride);
+        const float a = qs[hh][lo], c = qs[hh][lo + hstride];
+        qs[hh][lo] = a + c;
+        qs[hh][lo + hstride] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+  float qscale;
+  if constexpr (KF == KF_INT4) qscale = p.sm_scale / (float)D * kLog2e;
+  else if constexpr (KF == KF_FP8) qscale = p.sm_scale * kLog2e;
+  else qscale = p.sm_scale * kLog2e / sqrtf((float)D);
+
+  const int lane = tid & 63;
+  const int li = lane % LPT;
+  const int grp = (tid >> 6) * TPW + lane / LPT;
+  float qv[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qv[hh][j] = qs[hh][li * 8 + j] * qscale;
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[hh][j] = 0.0f;
+  }
+
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
+  constexpr int KB = (KF == KF_MSE3) ? 3 : 4;  // centroid index bits
+  constexpr int VB = (VF == VF_U3) ? 3 : 4;
+  const int mse_bytes = (D * KB + 7) / 8;
+
+  for (int64_t t = t0 + grp; t < t1; t += NG) {
+    const int64_t page = bt[t / p.block_size];
+    if (page < 0 || page >= p.num_blocks) continue;
+    const int64_t row = (page * p.block_size + t % p.block_size) * p.hk + kvh;
+
+    // ---- key: decode 8 dims and score against every head ----
+    float kd[8];
+    float kscale;
+    const uint8_t* slot = nullptr;
+    if constexpr (KF == KF_INT4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.kc + row * (D / 2) + li * 4);
+      const uint32_t sw = f2u(p.ks[row]);
+      const float zp = (float)(sw & 0xFu);
+      kscale = u2f(sw & 0xFFFFFFF0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kd[j] = (float)((w >> (4 * j)) & 0xFu) - zp;
+    } else {
+      slot = p.kv + row * p.slot_bytes;
+      if constexpr (KF == KF_FP8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(slot + li * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kd[j] = e4m3_to_f32((w.x >> (8 * j)) & 0xFFu);
+          kd[j + 4] = e4m3_to_f32((w.y >> (8 * j)) & 0xFFu);
+        }
+        kscale = 1.0f;
+      } else {
+        const uint32_t w = load_bytes_le<KB>(slot + li * KB);
+        float cs = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          kd[j] = cen[(w >> (KB * j)) & ((1u << KB) - 1u)];
+          cs += kd[j] * kd[j];
+        }
+        kscale = load_half_le(slot + mse_bytes);
+        if (p.norm_correction) kscale *= 1.0f / sqrtf(group_sum<LPT>(cs) + 1e-16f);
+      }
+    }
+    float sc[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part += qv[hh][j] * kd[j];
+      sc[hh] = group_sum<LPT>(part) * kscale;
+    }
+
+    // ---- value: decode 8 dims ----
+    float vd[8];
+    if constexpr (VF == VF_INT4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.vc + row * (D / 2) + li * 4);
+      const uint32_t sw = f2u(p.vs[row]);
+      const float zp = (float)(sw & 0xFu);
+      const float vsc = u2f(sw & 0xFFFFFFF0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vd[j] = ((float)((w >> (4 * j)) & 0xFu) - zp) * vsc;
+    } else {
+      const uint8_t* vbase = slot + p.kps;
+      const uint32_t w = load_bytes_le<VB>(vbase + li * VB);
+      const float vsc = load_half_le(vbase + p.vdb);
+      const float vz = load_half_le(vbase + p.vdb + 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        vd[j] = (float)((w >> (VB * j)) & ((1u << VB) - 1u)) * vsc + vz;
+    }
+
+    // ---- online softmax + accumulate ----
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mn = fmaxf(m[hh], sc[hh]);
+      const float alpha = exp2f(m[hh] - mn);
+      const float pr = exp2f(sc[hh] - mn);
+      l[hh] = l[hh] * alpha + pr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[hh][j] = acc[hh][j] * alpha + pr * vd[j];
+      m[hh] = mn;
+    }
+  }
+
+  // ---- merge the lane groups of this wave (log-sum-exp) ----
+  auto merge = [&](auto xorc) {
+    constexpr int M = decltype(xorc)::value;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float mo = xor_lane<M>(m[hh]);
+      const float lo = xor_lane<M>(l[hh]);
+      const float mm = fmaxf(m[hh], mo);
+      const float a = (mm == -INFINITY) ? 0.0f : exp2f(m[hh] - mm);
+      const float ao = (mm == -INFINITY) ? 0.0f : exp2f(mo - mm);
+      l[hh] = l[hh] * a + lo * ao;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[hh][j] = acc[hh][j] * a + xor_lane<M>(acc[hh][j]) * ao;
+      m[hh] = mm;
+    }
+  };
+  if constexpr (LPT <= 8) merge(std::integral_constant<int, 8>{});
+  if constexpr (LPT <= 16) merge(std::integral_constant<int, 16>{});
+  merge(std::integral_constant<int, 32>{});
+
+  const int wave = tid >> 6;
+  if (lane < LPT) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][hh][li * 8 + j] = acc[hh][j];
+      if (li == 0) {
+        red[wave][hh][D] = m[hh];
+        red[wave][hh][D + 1] = l[hh];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * (D + 1); i += 256) {
+    const int hh = i / (D + 1), d = i % (D + 1);
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][hh][D]);
+    float lsum = 0.0f, o = 0.0f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a = exp2f(red[w][hh][D] - mm);
+        lsum += red[w][hh][D + 1] * a;
+        if (d < D) o += red[w][hh][d] * a;
+      }
+    }
+    float* dst = p.ws + (((int64_t)b * p.hq + h0 + hh) * p.splits + s) * (D + 1);
+    if (d < D) dst[d] = lsum > 0.0f ? o / lsum : 0.0f;
+    else dst[D] = lsum > 0.0f ? (mm + log2f(lsum)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int KF, int VF>
+hipError_t launch_g(const DecodeParams& p, hipStream_t st) {
+  const int G = p.g <= 1 ? 1 : (p.g <= 2 ? 2 : (p.g <= 4 ? 4 : 8));
+  const int chunks = (p.g + G - 1) / G;
+  const uint32_t blocks = (uint32_t)p.B * p.hk * chunks * p.splits;
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 1>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 2>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 4>), dim3(blocks), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 8>), dim3(blocks), dim3(256), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
+  switch (p.key_fmt * 4 + p.val_fmt) {
+    case KF_INT4 * 4 + VF_INT4: return launch_g<D, KF_INT4, VF_INT4>(p, st);
+    case KF_FP8 * 4 + VF_U3: return launch_g<D, KF_FP8, VF_U3>(p, st);
+    case KF_FP8 * 4 + VF_U4: return launch_g<D, KF_FP8, VF_U4>(p, st);
+    case KF_MSE3 * 4 + VF_U3: return launch_g<D, KF_MSE3, VF_U3>(p, st);
+    case KF_MSE3 * 4 + VF_U4: return launch_g<D, KF_MSE3, VF_U4>(p, st);
+    case KF_MSE4 * 4 + VF_U3: return launch_g<D, KF_MSE4, VF_U3>(p, st);
+    case KF_MSE4 * 4 + VF_U4: return launch_g<D, KF_MSE4, VF_U4>(p, st);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t st) {
+  if (p.d == 128) return launch_d<128>(p, st);
+  if (p.d == 64) return launch_d<64>(p, st);
+  return hipErrorNotSupported;
+}
+
+}  // namespace tqk

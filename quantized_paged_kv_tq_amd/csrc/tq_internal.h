@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the
+// kernel translation units. Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TQ_DT_F32 0
+#define TQ_DT_F16 1
+#define TQ_DT_BF16 2
+
+namespace tqk {
+
+struct ReshapeParams {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  const float* signs;
+  uint8_t* kc;
+  uint8_t* vc;
+  float* ks;
+  float* vs;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int hk, d, dtype, block_size;
+};
+hipError_t launch_reshape_int4(const ReshapeParams& p, hipStream_t st);
+
+hipError_t launch_fwht128_fp8(const void* x, int64_t rows, uint8_t* y, float* scale,
+                              hipStream_t st);
+
+// Key/value formats (same numbering as the public header).
+enum { KF_INT4 = 0, KF_FP8 = 1, KF_MSE3 = 2, KF_MSE4 = 3 };
+enum { VF_INT4 = 0, VF_U3 = 1, VF_U4 = 2 };
+
+struct DecodeParams {
+  int B, hq, hk, d, g, block_size, max_blocks, splits;
+  int key_fmt, val_fmt, norm_correction;
+  float sm_scale;
+  int64_t num_blocks;
+  const float* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const float* ks;
+  const float* vs;
+  const float* rht_signs;
+  const uint8_t* kv;
+  int slot_bytes;
+  int kps;       // key region bytes of a combined slot
+  int vdb;       // value index bytes of a combined slot
+  const float* centroids;
+  const float* rot_signs;
+  float* ws;     // [B, Hq, S, D+1]
+  float* out;    // [B, Hq, D]
+  float* lse;    // [B, Hq] or null
+};
+
+// Format-generic vector stage 1 (every key/value format).
+hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t st);
+// INT4 stage 1 on the matrix cores; returns hipErrorNotSupported when the
+// shape is outside what it handles (the caller then uses the generic one).
+hipError_t launch_decode_int4_mfma(const DecodeParams& p, hipStream_t st);
+// Stage 2: log-sum-exp merge of the split partials (+ inverse RHT for INT4).
+hipError_t launch_merge(const DecodeParams& p, hipStream_t st);
+
+}  // namespace tqk

@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/tq.h declares, sizes its tables as documented and rejects invalid
+arguments with the documented codes before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import quantized_paged_kv_tq_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tq.LIB_PATH):
+        import quantized_paged_kv_tq_amd.build as b
+        b.build(verbose=False)
+    return tq.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
+                          "tq_decode_workspace_bytes", "tq_slot_bytes",
+                          "tq_decode_attention", "fwht128_quant_fp8"}
+    raw = C.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(tq.SYMBOLS) == set(names)
+
+
+def test_sizes(L):
+    assert L.tq_version() == 1
+    assert tq.tq_slot_bytes(128, tq.KEY_FP8, tq.VAL_U4) == 208
+    assert tq.tq_slot_bytes(128, tq.KEY_MSE3, tq.VAL_U3) == 112
+    assert tq.tq_slot_bytes(128, tq.KEY_INT4, tq.VAL_U4) == -1
+    assert tq.tq_slot_bytes(96, tq.KEY_FP8, tq.VAL_U4) == -1
+    assert tq.tq_decode_workspace_bytes(32, 32, 128, 8) == 32 * 32 * 8 * 129 * 4
+
+
+def test_decode_args_layout_matches_header(tmp_path):
+    """ctypes' view of tq_decode_args has the C compiler's offsets."""
+    fields = [f[0] for f in tq.DecodeArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "tq.h"\nint main(void){\n'
+                   + "".join('printf("%%zu\\n", offsetof(tq_decode_args, %s));\n' % f for f in fields)
+                   + 'printf("%zu\\n", sizeof(tq_decode_args));return 0;}\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [getattr(tq.DecodeArgs, f).offset for f in fields] + [C.sizeof(tq.DecodeArgs)]
+    assert got == want
+
+
+def _args(**kw):
+    a = tq.DecodeArgs()
+    a.struct_size = C.sizeof(tq.DecodeArgs)
+    a.B, a.Hq, a.Hk, a.D = 2, 4, 1, 64
+    a.block_size, a.max_blocks, a.num_kv_splits, a.num_blocks = 16, 16, 4, 32
+    a.key_fmt, a.val_fmt = tq.KEY_INT4, tq.VAL_INT4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=63), tq.TQ_EINVAL),
+    (dict(D=96), tq.TQ_EINVAL),
+    (dict(D=256), tq.TQ_ENOTSUP),
+    (dict(Hq=6, Hk=4), tq.TQ_EINVAL),
+    (dict(Hq=34, Hk=2), tq.TQ_ENOTSUP),
+    (dict(num_kv_splits=0), tq.TQ_EINVAL),
+    (dict(num_kv_splits=257), tq.TQ_EINVAL),
+    (dict(block_size=0), tq.TQ_EINVAL),
+    (dict(key_fmt=tq.KEY_INT4, val_fmt=tq.VAL_U4), tq.TQ_ENOTSUP),
+    (dict(key_fmt=7), tq.TQ_ENOTSUP),
+    (dict(struct_size=8), tq.TQ_EINVAL),
+    (dict(), tq.TQ_EINVAL),  # null device pointers
+])
+def test_decode_rejects_invalid(L, kw, code):
+    a = _args(**kw)
+    assert L.tq_decode_attention(C.byref(a), None) == code
+    assert tq.last_error() != ""
+
+
+def test_decode_null_args_and_empty_batch(L):
+    assert L.tq_decode_attention(None, None) == tq.TQ_EINVAL
+    assert L.tq_decode_attention(C.byref(_args(B=0)), None) == tq.TQ_OK
+    assert tq.last_error() == ""
+
+
+def test_tq_format_checks(L):
+    a = _args(key_fmt=tq.KEY_FP8, val_fmt=tq.VAL_U4, D=128, query=16, block_table=16,
+              seq_lens=16, workspace=16, out=16, kv_cache=16, slot_bytes=192)
+    assert L.tq_decode_attention(C.byref(a), None) == tq.TQ_EINVAL  # slot too small
+    a = _args(key_fmt=tq.KEY_MSE3, val_fmt=tq.VAL_U3, D=128, query=16, block_table=16,
+              seq_lens=16, workspace=16, out=16, kv_cache=16, slot_bytes=112)
+    assert L.tq_decode_attention(C.byref(a), None) == tq.TQ_EINVAL  # no centroids
+
+
+def test_writer_and_fwht_validation(L):
+    f = L.tq_reshape_and_cache_int4
+    assert f(None, None, 0, 0, 8, 128, None, None, None, None, None, None, 4, 16, None) == tq.TQ_OK
+    assert f(None, None, 0, 5, 8, 128, None, None, None, None, None, None, 4, 16, None) == tq.TQ_EINVAL
+    assert f(None, None, 0, 5, 8, 96, None, None, None, None, None, None, 4, 16, None) == tq.TQ_EINVAL
+    assert f(None, None, 0, 5, 8, 32, None, None, None, None, None, None, 4, 16, None) == tq.TQ_ENOTSUP
+    assert f(None, None, 9, 5, 8, 128, None, None, None, None, None, None, 4, 16, None) == tq.TQ_ENOTSUP
+    assert f(None, None, 0, -1, 8, 128, None, None, None, None, None, None, 4, 16, None) == tq.TQ_EINVAL
+    g = L.fwht128_quant_fp8
+    assert g(None, 0, None, None, None) == tq.TQ_OK
+    assert g(None, 3, None, None, None) == tq.TQ_EINVAL
+    assert g(None, -3, None, None, None) == tq.TQ_EINVAL
+    assert g(16, 3, 17, 16, None) == tq.TQ_EINVAL  # misaligned output
+
+
+def test_binding_requires_library(monkeypatch):
+    monkeypatch.setattr(tq, "_lib", None)
+    monkeypatch.setattr(tq, "LIB_PATH", "/nonexistent/libtq_amd.so")
+    with pytest.raises(ImportError):
+        tq.lib()

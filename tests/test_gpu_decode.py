@@ -1,0 +1,155 @@
+"""GPU parity of tq_decode_attention against the CPU oracle (fp64), through
+the C ABI: max |err| <= 1e-3 and relative L2 <= 1e-4 on the output, lse
+within 1e-4. Caches are written by the oracle. Covers the INT4 format on
+both kernels (matrix-core and generic), the TurboQuant formats, ragged and
+degenerate sequence lengths, every split count regime, and the full-size
+workloads on sampled rows."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_paged_kv_tq_amd as tq
+from quantized_paged_kv_tq_amd import workloads as W
+
+from gpu_cases import assert_close, gpu_int4_decode, gpu_tq_decode, int4_caches, tq_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_int4(w, q, c, splits=None, rows=None, seq_lens=None):
+    return oracle.int4_decode(q, c["kc"], c["vc"], c["ks"], c["vs"], w.block_table,
+                              w.seq_lens if seq_lens is None else seq_lens, c["signs"],
+                              w.num_splits if splits is None else splits, w.sm_scale, rows)
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+def test_int4_tiny_workload(flags):
+    w = W.decode_workload("tiny_int4")
+    c = int4_caches(w)
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    got, lse = gpu_int4_decode(w, q, c, flags=flags)
+    assert_close(got, ref, lse, ref_lse, "tiny_int4")
+
+
+SHAPES = [
+    # B, hq, hk, d, bs, seq_lens, splits
+    (3, 8, 2, 128, 16, [1, 70, 333], 4),
+    (2, 32, 8, 128, 16, [1024, 517], 8),
+    (2, 64, 8, 128, 64, [700, 4096], 16),
+    (4, 8, 8, 128, 16, [15, 16, 17, 200], 3),
+    (2, 16, 1, 128, 16, [300, 129], 5),
+    (2, 12, 4, 64, 16, [111, 64], 2),
+    (1, 6, 2, 64, 7, [100], 9),
+    (2, 16, 16, 64, 32, [65, 1], 1),
+    (2, 2, 2, 128, 1, [19, 40], 64),
+    (2, 40, 4, 128, 16, [90, 160], 4),
+]
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_int4_shapes(shape, flags):
+    B, hq, hk, d, bs, seq, S = shape
+    w = W.custom_decode_workload(100 + len(seq) * 7 + hq + d, B, hq, hk, d, bs, S, seq, 5, "bf16")
+    c = int4_caches(w)
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    got, lse = gpu_int4_decode(w, q, c, flags=flags)
+    assert_close(got, ref, lse, ref_lse, str(shape))
+
+
+def test_int4_split_invariance_and_empty_splits():
+    w = W.custom_decode_workload(140, 2, 8, 2, 128, 16, 4, [37, 100], 2, "bf16")
+    c = int4_caches(w)
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c, splits=0)
+    for S in (1, 2, 8, 37, 64, 100, 105, 256):
+        got, lse = gpu_int4_decode(w, q, c, num_splits=S)
+        assert_close(got, ref, lse, ref_lse, "S=%d" % S)
+
+
+def test_int4_zero_and_one_token_sequences():
+    w = W.custom_decode_workload(141, 3, 8, 2, 128, 16, 4, [1, 1, 40], 2, "bf16")
+    c = int4_caches(w)
+    q = W.query(w)
+    seq = np.array([1, 0, 40], np.int32)
+    ref, ref_lse = _oracle_int4(w, q, c, seq_lens=seq)
+    got, lse = gpu_int4_decode(w, q, c, seq_lens=seq)
+    assert_close(got, ref, lse, ref_lse, "seq 1/0")
+    assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
+
+
+def test_int4_random_cache_bytes():
+    """Uniformly random nibbles and scale words (no writer involved)."""
+    w = W.custom_decode_workload(142, 2, 16, 4, 128, 16, 4, [300, 77], 4, "bf16")
+    kc, vc, ks, vs = W.random_int4_cache(w)
+    c = dict(kc=kc, vc=vc, ks=ks, vs=vs, signs=W.rht_signs(128))
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    for flags in (0, tq.FLAG_GENERIC):
+        got, lse = gpu_int4_decode(w, q, c, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "random bytes")
+
+
+def _sampled_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(w.B * w.hq, size=min(n, w.B * w.hq), replace=False)).astype(np.int32)
+
+
+@pytest.mark.parametrize("name", ["llama8b_int4", "long_int4"])
+def test_int4_full_size_sampled(name):
+    w = W.decode_workload(name)
+    c = int4_caches(w)
+    q = W.query(w)
+    got, lse = gpu_int4_decode(w, q, c)
+    rows = _sampled_rows(w, 48, 7)
+    ref, ref_lse = _oracle_int4(w, q, c, rows=rows)
+    assert_close(got[rows], ref, lse[rows], ref_lse, name)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))
+
+
+TQ_FORMATS = [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3),
+              (oracle.KEY_FP8, oracle.VAL_U3), (oracle.KEY_MSE4, oracle.VAL_U4),
+              (oracle.KEY_MSE3, oracle.VAL_U4), (oracle.KEY_MSE4, oracle.VAL_U3)]
+
+
+@pytest.mark.parametrize("fmt", TQ_FORMATS, ids=[str(f) for f in TQ_FORMATS])
+@pytest.mark.parametrize("d", [128, 64])
+def test_tq_formats_small(fmt, d):
+    key_fmt, val_fmt = fmt
+    w = W.custom_decode_workload(150 + d, 2, 8, 2, d, 16, 4, [150, 33], 3, "bf16")
+    cache, cen = tq_case(w, key_fmt, val_fmt)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, key_fmt,
+                                    val_fmt, 0, w.num_splits, w.sm_scale)
+    got, lse = gpu_tq_decode(w, q, cache, cen, key_fmt, val_fmt)
+    assert_close(got, ref, lse, ref_lse, str(fmt))
+
+
+@pytest.mark.parametrize("key_fmt", [oracle.KEY_MSE3, oracle.KEY_MSE4])
+def test_tq_norm_correction_and_rot_signs(key_fmt):
+    w = W.custom_decode_workload(160, 2, 8, 4, 128, 16, 5, [90, 211], 3, "bf16")
+    rs = W.rht_signs(128, round_idx=1)
+    cache, cen = tq_case(w, key_fmt, oracle.VAL_U3, rot_signs=rs)
+    q = W.query(w, bf16_valued=True)
+    for nc in (0, 1):
+        ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, rs, key_fmt,
+                                        oracle.VAL_U3, nc, w.num_splits, w.sm_scale)
+        got, lse = gpu_tq_decode(w, q, cache, cen, key_fmt, oracle.VAL_U3, rot_signs=rs,
+                                 norm_correction=nc)
+        assert_close(got, ref, lse, ref_lse, "nc=%d" % nc)
+
+
+@pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3)],
+                         ids=["A_fp8_u4", "B_mse3_u3"])
+def test_tq_full_size_sampled(fmt):
+    key_fmt, val_fmt = fmt
+    w = W.decode_workload("tq_mixed")
+    cache, cen = tq_case(w, key_fmt, val_fmt)
+    q = W.query(w, bf16_valued=True)
+    got, lse = gpu_tq_decode(w, q, cache, cen, key_fmt, val_fmt)
+    rows = _sampled_rows(w, 24, 8)
+    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, key_fmt,
+                                    val_fmt, 0, w.num_splits, w.sm_scale, rows)
+    assert_close(got[rows], ref, lse[rows], ref_lse, "tq_mixed %s" % (fmt,))

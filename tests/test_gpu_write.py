@@ -1,0 +1,115 @@
+"""GPU parity of the cache writers against the CPU oracle (bit-exact):
+tq_reshape_and_cache_int4 and fwht128_quant_fp8, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_paged_kv_tq_amd import workloads as W
+
+from gpu_cases import DEV, DT_CODE, src_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _write_both(kb, vb, dtype, slots, nb, bs, hk, d, canary=True):
+    import quantized_paged_kv_tq_amd as tq
+    s = W.rht_signs(d)
+    shape = (nb, bs, hk, d // 2)
+    fill = (0xA5, 0x5A, 7.0, 9.0) if canary else (0, 0, 0.0, 0.0)
+    kc_o = np.full(shape, fill[0], np.uint8)
+    vc_o = np.full(shape, fill[1], np.uint8)
+    ks_o = np.full(shape[:3], fill[2], np.float32)
+    vs_o = np.full(shape[:3], fill[3], np.float32)
+    kc, vc, ks, vs = (to_dev(a) for a in (kc_o, vc_o, ks_o, vs_o))
+    oracle.reshape_and_cache_int4(kb, vb, DT_CODE[dtype], slots, s, kc_o, vc_o, ks_o, vs_o)
+    tq.tq_reshape_and_cache_int4(src_to_dev(kb, dtype), src_to_dev(vb, dtype), kc, vc,
+                                 to_dev(slots), k_scale_cache=ks, v_scale_cache=vs,
+                                 rht_signs=to_dev(s))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kc.cpu().numpy(), kc_o)
+    np.testing.assert_array_equal(vc.cpu().numpy(), vc_o)
+    np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32), ks_o.view(np.uint32))
+    np.testing.assert_array_equal(vs.cpu().numpy().view(np.uint32), vs_o.view(np.uint32))
+
+
+def test_write_tiny_f16_d64():
+    w = W.decode_workload("tiny_int4")
+    kb, vb = W.kv_source(w)
+    _write_both(kb, vb, "f16", w.slot_mapping, w.num_blocks, w.block_size, w.hk, w.d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d,hk,T", [(128, 8, 300), (64, 3, 257), (128, 1, 33), (64, 5, 1)])
+def test_write_dtypes_shapes_and_skips(dtype, d, hk, T):
+    wl = W.write_workload(num_tokens=T, hk=hk, d=d, block_size=16, skip_frac=0.1, dtype=dtype,
+                          wid=50 + d + hk)
+    _write_both(wl["key"], wl["value"], dtype, wl["slot_mapping"], wl["num_blocks"], 16, hk, d)
+
+
+def test_write_scaled_and_outlier_rows():
+    # large and tiny magnitudes, constant rows and single spikes
+    rng = np.random.default_rng(9)
+    T, hk, d = 64, 2, 128
+    k = rng.standard_normal((T, hk, d)).astype(np.float32)
+    k[0] = 0.0
+    k[1] = 3.0
+    k[2] *= 1e-6
+    k[3] *= 1e4
+    k[4, :, 7] = 500.0
+    v = np.flip(k, 0).copy()
+    slots = np.arange(T, dtype=np.int64)[::-1].copy()
+    for dtype in ("bf16", "f16", "f32"):
+        kb, vb = W.to_bits(k, dtype), W.to_bits(v, dtype)
+        _write_both(kb, vb, dtype, slots, 4, 16, hk, d)
+
+
+def test_write_out_of_range_slots_are_skipped():
+    wl = W.write_workload(num_tokens=40, hk=2, d=64, block_size=8, skip_frac=0.0, dtype="bf16", wid=58)
+    slots = wl["slot_mapping"].copy()
+    slots[3] = 40 * 1000  # beyond the cache: must not be written
+    slots[5] = -7
+    _write_both(wl["key"], wl["value"], "bf16", slots, wl["num_blocks"], 8, 2, 64)
+
+
+def test_write_full_size_65536x8x128_bf16():
+    wl = W.write_workload()
+    _write_both(wl["key"], wl["value"], "bf16", wl["slot_mapping"], wl["num_blocks"], 16, 8, 128,
+                canary=False)
+
+
+def _fwht_both(bits):
+    import quantized_paged_kv_tq_amd as tq
+    y_o, s_o = oracle.fwht128_quant_fp8(bits)
+    y, s = tq.fwht128_quant_fp8(to_dev(bits.view(np.int16), torch.bfloat16))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.view(torch.uint8).cpu().numpy(), y_o)
+    np.testing.assert_array_equal(s.cpu().numpy().ravel().view(np.uint32), s_o.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", [1, 15, 17, 1000])
+def test_fwht_ragged_rows(rows):
+    _fwht_both(W.fwht_rows(rows=rows, wid=60 + rows))
+
+
+def test_fwht_special_rows():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[0] = 0.0                       # absmax floor
+    x[1] *= 1e-8                     # tiny row: subnormal FP8 codes
+    x[2] *= 3e4                      # large row
+    x[3] = 0.0
+    x[3, 0] = 1.75 * 2 ** 3 * np.sqrt(128)   # transform is constant: exact powers
+    x[4, :] = rng.integers(-3, 4, 128)       # integer row
+    x[5] = x[4] * 2.0 ** -20
+    _fwht_both(W.to_bits(x, "bf16"))
+
+
+def test_fwht_full_size_1m_rows():
+    _fwht_both(W.fwht_rows())
+
+
+def test_fwht_empty():
+    import quantized_paged_kv_tq_amd as tq
+    y, s = tq.fwht128_quant_fp8(torch.empty(0, 128, dtype=torch.bfloat16, device=DEV))
+    assert y.shape == (0, 128) and s.shape == (0, 1)
