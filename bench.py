@@ -84,7 +84,9 @@ def run_int4(args, torch, tq, W, name):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     w = W.decode_workload(name)
-    log("[bench] workload", name, "tokens", w.total_tokens)
+    if args.splits:
+        w.num_splits = args.splits
+    log("[bench] workload", name, "tokens", w.total_tokens, "splits", w.num_splits)
     kb, vb = W.kv_source(w)
     signs = torch.from_numpy(W.rht_signs(w.d)).to(dev)
     shape = (w.num_blocks, w.block_size, w.hk, w.d // 2)
@@ -304,6 +306,7 @@ def main():
     ap.add_argument("--workload", default="llama8b_int4")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--splits", type=int, default=0, help="override num_kv_splits (sweeps)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU "

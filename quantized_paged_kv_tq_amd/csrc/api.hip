@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/tq.h"
+#include "tq.h"
 #include "tq_internal.h"
 
 namespace {

@@ -73,21 +73,67 @@ __device__ __forceinline__ int row16_isum(int v) {
 // 2^e for an integer e in [-126, 127]
 __device__ __forceinline__ float exp2i(int e) { return u2f((uint32_t)(e + 127) << 23); }
 
-template <int NH, int W>
-__global__ __launch_bounds__(64 * W) void decode_int4_mfma_kernel(DecodeParams p) {
-  constexpr int NHEAD = 4 * NH;  // query heads per workgroup (padded)
-  __shared__ __attribute__((aligned(16))) int32_t rows_lds[W][64];
-  __shared__ __attribute__((aligned(16))) uint32_t p8_lds[W][NH][4][4][16];
-  __shared__ int32_t qsum_lds[NHEAD][4];
-  __shared__ float qf_lds[NHEAD];
-  __shared__ int32_t qexp_lds[NHEAD];
-  // prologue: rotated queries; epilogue: per-wave partials (not live together)
-  __shared__ float big[(W * NHEAD * (D + 2) > NHEAD * D) ? W * NHEAD * (D + 2) : NHEAD * D];
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
+// Buffer resource over [base, base + bytes): loads outside return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kMasked = 0x03FFFFFFu;  // row index whose bytes lie past any buffer
+// Headroom of the value-weight fixed point: weights are taken relative to a
+// reference maximum that is raised only when a tile exceeds it by more than
+// 2^kTau, so p = 2^(s - m_ref) <= 2^kTau.
+constexpr int kTau = 4;
+constexpr int kMaxPages = 2048;  // block-table entries staged in LDS
+
+// One workgroup per (split, batch, group of HG kv heads); W = HG * R waves:
+// wave w serves kv head (group * HG + w % HG) and takes every R-th tile of
+// the split starting at tile w / HG. All waves walk the same pages at the
+// same pace, so the HG heads' slices of each token row are requested
+// together (whole rows when HG = Hk), which keeps DRAM pages open.
+template <int NH, int W>
+__global__ __launch_bounds__(64 * W) void decode_int4_mfma_kernel(DecodeParams p, int HG) {
+  constexpr int NHEAD = 4 * NH;  // query heads per kv head (padded)
+  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[W][64];
+  // per wave: MFMA A-operand image of its queries (prologue), then the
+  // per-tile weight digit planes
+  __shared__ __attribute__((aligned(16))) uint32_t wbuf[W][NH][2][64][4];
+  __shared__ int32_t pages_lds[kMaxPages];
+  __shared__ float red[W][NHEAD][D + 2];
+
+  const int R = W / HG;
+  const int ngrp = p.hk / HG;
   const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int kvh = lb % p.hk;
-  const int s_idx = (lb / p.hk) % p.splits;
-  const int b = lb / (p.hk * p.splits);
+  // split slowest: each XCD receives whole split indices of every sequence
+  const int grp = lb % ngrp;
+  const int b = (lb / ngrp) % p.B;
+  const int s_idx = lb / (ngrp * p.B);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int ln = lane & 15;   // n: MFMA column / row within a 16-lane group
+  const int lg = lane >> 4;   // g: 16-lane group
+  const int kvh = grp * HG + wave % HG;
+  const int rsl = wave / HG;  // this wave's tile slice
+  const int g = p.g;
+  const int h0 = kvh * g;
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
+  // the whole block-table row is staged when it fits, independently of the
+  // sequence length, so that it loads in the same round trip as seq_len
+  const bool row_in_lds = p.max_blocks <= kMaxPages;
+  if (row_in_lds)
+    for (int i = tid; i < p.max_blocks; i += 64 * W) pages_lds[i] = bt[i];
+  // this wave's queries, two dims per lane, signs applied
+  float qx[NHEAD][2];
+#pragma unroll
+  for (int hh = 0; hh < NHEAD; ++hh) {
+    const bool ok = hh < g;
+    const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (ok ? hh : 0)) * D;
+    qx[hh][0] = ok ? qrow[lane] * p.rht_signs[lane] : 0.0f;
+    qx[hh][1] = ok ? qrow[lane + 64] * p.rht_signs[lane + 64] : 0.0f;
+  }
 
   int64_t seq = p.seq_lens[b];
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
@@ -95,228 +141,288 @@ __global__ __launch_bounds__(64 * W) void decode_int4_mfma_kernel(DecodeParams p
   const int64_t split_len = (seq + p.splits - 1) / p.splits;
   const int64_t t0 = split_len * s_idx;
   const int64_t t1 = (t0 + split_len < seq) ? t0 + split_len : seq;
-  if (t0 >= t1) return;  // empty split: nothing written (stage 2 skips it)
+  if (t0 >= t1) return;  // empty split (uniform): nothing written, stage 2 skips it
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int ln = lane & 15;   // n: MFMA column / row within a 16-lane group
-  const int lg = lane >> 4;   // g: 16-lane group
-  const int g = p.g;
-  const int h0 = kvh * g;
+  const uint32_t bs = (uint32_t)p.block_size;
+  const bool bs_pow2 = (bs & (bs - 1u)) == 0u;
+  const int bs_shift = __builtin_ctz(bs);
+  const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
+  const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(p.kc, nrows * (uint32_t)(D / 2));
+  const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(p.vc, nrows * (uint32_t)(D / 2));
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ks, nrows * 4u);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(p.vs, nrows * 4u);
+  __syncthreads();  // page list staged
 
-  // ---------------- query prologue ----------------
-  float* qrot = big;  // [NHEAD][D]
-  for (int i = tid; i < NHEAD * D; i += 64 * W) {
-    const int hh = i / D, d = i % D;
-    qrot[i] = hh < g ? p.q[((int64_t)b * p.hq + h0 + hh) * D + d] * p.rht_signs[d] : 0.0f;
-  }
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int i = tid; i < NHEAD * D / 2; i += 64 * W) {
-      const int hh = i / (D / 2), k = i % (D / 2);
-      const int lo = hh * D + (k / hs) * 2 * hs + (k % hs);
-      const float a = qrot[lo], c = qrot[lo + hs];
-      qrot[lo] = a + c;
-      qrot[lo + hs] = a - c;
+  const int64_t ntiles = (t1 - t0 + 63) / 64;
+  // Row index of the tile's token `lane` into rows_lds (masked: kMasked).
+  auto stage_rows = [&](int64_t tile) {
+    const int64_t tok = t0 + tile * 64 + lane;
+    uint32_t row = kMasked;
+    if (tile < ntiles && tok < t1) {
+      const uint32_t t32 = (uint32_t)tok;
+      const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
+      const int64_t page = row_in_lds ? pages_lds[pi] : bt[pi];
+      if (page >= 0 && page < p.num_blocks)
+        row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk + (uint32_t)kvh;
     }
-    __syncthreads();
-  }
-  // per-head power-of-two scale: |q'| * 2^E < 2^27
-  for (int hh = wave; hh < NHEAD; hh += W) {
-    const float amax = group_max<64>(fmaxf(fabsf(qrot[hh * D + lane]), fabsf(qrot[hh * D + 64 + lane])));
-    if (lane == 0) {
-      const int e = amax > 0.0f ? (int)((f2u(amax) >> 23) & 0xFF) - 127 : 0;
-      const int E = amax > 0.0f ? 26 - e : 0;
-      qexp_lds[hh] = E;
-      // score in base-2 units = sm_scale / D * log2(e) * 2^-E * (integer dot)
-      qf_lds[hh] = p.sm_scale / (float)D * kLog2e * exp2i(-E);
+    rows_lds[wave][lane] = row;
+    wave_sync();
+  };
+  // key bytes + both scale words of tokens 16s+n (masked rows read 0)
+  v4u kraw[4];
+  uint32_t ksw[4], vsw[4], live = 0;
+  auto issue_k = [&]() {
+    live = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t r = rows_lds[wave][16 * s + ln];
+      live |= (r != kMasked ? 1u : 0u) << s;
+      kraw[s] = __builtin_amdgcn_raw_buffer_load_b128(rk_, (int)((r << 6) | (16u * lg)), 0, 0);
+      ksw[s] = __builtin_amdgcn_raw_buffer_load_b32(rks, (int)(r << 2), 0, 0);
+      vsw[s] = __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(r << 2), 0, 0);
     }
-  }
-  __syncthreads();
+  };
+  // value dword n of tokens 16s+4g+k
+  uint32_t vraw[4][4];
+  auto issue_v = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 rv = *reinterpret_cast<const uint4*>(&rows_lds[wave][16 * s + 4 * lg]);
+      const uint32_t rr[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vraw[s][k] = __builtin_amdgcn_raw_buffer_load_b32(rv_, (int)((rr[k] << 6) | (4u * ln)), 0, 0);
+    }
+  };
 
-  // A operands of the score MFMA: lane (m = 4*h' + piece, g) holds the digit
-  // `piece` of head 4r+h' for dims 32g + {16c + 8(j/2) + 2b + (j%2)}: the
-  // byte order the K nibble unpack produces.
-  v4i qa[NH][2];
+  stage_rows(rsl);  // the first tile's loads overlap the query prologue
+  issue_k();
+  issue_v();
+
+  // ---------------- query prologue (per wave, no barrier) ----------------
+  // Rotate each head (two dims per lane), scale by a power of two to
+  // integers below 2^27, split into four balanced base-128 digits and
+  // scatter them into the MFMA A-operand image: lane (m = 4h' + piece, g)
+  // holds, for chunk c, dword j, byte b, the digit of dim
+  // 32g + 16c + 8(j/2) + 2b + (j%2) -- the order of the K unpack.
+  float qsum[NH][4], qf[NH];
+  {
+    uint8_t* img = reinterpret_cast<uint8_t*>(&wbuf[wave][0][0][0][0]);
 #pragma unroll
-  for (int r = 0; r < NH; ++r) {
-    const int hh = 4 * r + (ln >> 2);
-    const int piece = ln & 3;
-    const float sc = exp2i(qexp_lds[hh]);
-    int dsum = 0;
+    for (int hh = 0; hh < NHEAD; ++hh) {
+      float x0 = qx[hh][0], x1 = qx[hh][1];
+      {
+        const float a = x0 + x1, c = x0 - x1;
+        x0 = a;
+        x1 = c;
+      }
+      x0 = butterfly_lanes<1>(x0, lane & 1);   x1 = butterfly_lanes<1>(x1, lane & 1);
+      x0 = butterfly_lanes<2>(x0, lane & 2);   x1 = butterfly_lanes<2>(x1, lane & 2);
+      x0 = butterfly_lanes<4>(x0, lane & 4);   x1 = butterfly_lanes<4>(x1, lane & 4);
+      x0 = butterfly_lanes<8>(x0, lane & 8);   x1 = butterfly_lanes<8>(x1, lane & 8);
+      x0 = butterfly_lanes<16>(x0, lane & 16); x1 = butterfly_lanes<16>(x1, lane & 16);
+      x0 = butterfly_lanes<32>(x0, lane & 32); x1 = butterfly_lanes<32>(x1, lane & 32);
+      // x0 = q'[lane], x1 = q'[lane + 64]
+      const float amax = group_max<64>(fmaxf(fabsf(x0), fabsf(x1)));
+      const int E = amax > 0.0f ? 26 - ((int)((f2u(amax) >> 23) & 0xFF) - 127) : 0;
+      const float sc = exp2i(E);
+      const int r = hh >> 2, hp = hh & 3;
+      float dsum[4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      int words[4] = {0, 0, 0, 0};
+      for (int e = 0; e < 2; ++e) {
+        const int dim = lane + 64 * e;
+        int v = (int)__builtin_rintf((e ? x1 : x0) * sc);
+        const int gg = dim >> 5, o = dim & 31;
+        const int c = o >> 4, j = 2 * ((o & 15) >> 3) + (o & 1), bb = (o & 7) >> 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int dim = 32 * lg + 16 * c + 8 * (j >> 1) + 2 * bb + (j & 1);
-          int v = (int)__builtin_rintf(qrot[hh * D + dim] * sc);
-          int dg = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int dk = (k < 3) ? (((v + 64) & 127) - 64) : v;
-            if (k == piece) dg = dk;
-            v = (v - dk) >> 7;
-          }
-          dsum += dg;
-          words[j] |= (dg & 0xFF) << (8 * bb);
+        for (int pc = 0; pc < 4; ++pc) {
+          const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
+          v = (v - dk) >> 7;
+          const int L = 16 * gg + 4 * hp + pc;
+          img[(((r * 2 + c) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
+          dsum[pc] = (e ? dsum[pc] : 0.0f) + (float)dk;
         }
       }
-      qa[r][c] = v4i{words[0], words[1], words[2], words[3]};
+      // lane (n, g) scores head 4r+g: keep that head's digit sums and scale
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const float t = group_sum<64>(dsum[pc]);
+        if (hp == lg) qsum[r][pc] = t;
+      }
+      // score in base-2 units = sm_scale / D * log2(e) * 2^-E * (integer dot)
+      if (hp == lg) qf[r] = p.sm_scale / (float)D * kLog2e * exp2i(-E);
     }
-    // sum of the digits over all D dims: reduce over the four 16-lane groups
-    dsum += __builtin_amdgcn_ds_bpermute((int)((lane ^ 16) << 2), dsum);
-    dsum += __builtin_amdgcn_ds_bpermute((int)((lane ^ 32) << 2), dsum);
-    if (wave == 0 && lg == 0) qsum_lds[hh][piece] = dsum;
   }
-  __syncthreads();
-  // per-lane constants of the score side: lane (n, g) scores head 4r+g
-  int qsum[NH][4];
-  float qf[NH];
+  wave_sync();
+  v4i qa[NH][2];
 #pragma unroll
-  for (int r = 0; r < NH; ++r) {
+  for (int r = 0; r < NH; ++r)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qsum[r][k] = qsum_lds[4 * r + lg][k];
-    qf[r] = qf_lds[4 * r + lg];
-  }
+    for (int c = 0; c < 2; ++c) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(&wbuf[wave][r][c][lane][0]);
+      qa[r][c] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
+    }
+  wave_sync();  // the image region is reused for the weight digit planes
+  uint32_t(*p8)[4][4][16] = reinterpret_cast<uint32_t(*)[4][4][16]>(&wbuf[wave][0][0][0][0]);
 
-  float m[NH], l[NH], acc[NH][8];
+  // Online softmax state, all relative to a reference maximum m_ref (base-2
+  // units) per head and a power-of-two weight scale 2^ev shared by the wave:
+  //   l     per-lane sum of 2^(s - m_ref) over the lane's tokens
+  //   cacc  int32 MFMA sums of the weight digit planes times the value
+  //         nibbles (lane (n, g): head 4r+g, dims 8n+i, planes 0..3)
+  //   zl    per-lane sums of weight digits times value zero points
+  //   acc   fp32 part folded at each flush
+  float mref[NH], l[NH], acc[NH][8];
+  v4i cacc[NH][8];
+  int zl[NH][4];
 #pragma unroll
   for (int r = 0; r < NH; ++r) {
-    m[r] = -INFINITY;
+    mref[r] = -INFINITY;
     l[r] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[r][i] = 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      acc[r][i] = 0.0f;
+      cacc[r][i] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) zl[r][k] = 0;
   }
+  int ev = 0;             // weight scale exponent
+  float sref = 0.0f;      // value scales below sref fit the current ev
+  bool empty = true;      // cacc / zl hold nothing
+  int since_flush = 0;    // tiles accumulated since the last flush
 
-  const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
-  const int64_t ntiles = (t1 - t0 + 63) / 64;
-  for (int64_t tile = wave; tile < ntiles; tile += W) {
-    const int64_t T0 = t0 + tile * 64;
-    // ---- cache row of every token of the tile (-1: masked) ----
-    {
-      const int64_t tok = T0 + lane;
-      int32_t row = -1;
-      if (tok < t1) {
-        const int64_t page = bt[tok / p.block_size];
-        if (page >= 0 && page < p.num_blocks)
-          row = (int32_t)((page * p.block_size + tok % p.block_size) * p.hk + kvh);
+  // fold cacc/zl into acc (scale 2^-ev), then rescale by alpha per head
+  auto flush = [&](const float (&alpha)[NH]) {
+    const float pinv = exp2i(-ev);
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      if (!empty) {
+        float zs[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zs[k] = (float)row16_isum(zl[r][k]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          // digit plane minus its zero-point sum: exact small integers
+          const float e0 = (float)cacc[r][i].x - zs[0];
+          const float e1 = (float)cacc[r][i].y - zs[1];
+          const float e2 = (float)cacc[r][i].z - zs[2];
+          const float e3 = (float)cacc[r][i].w - zs[3];
+          const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+          acc[r][i] = __builtin_fmaf(val, pinv, acc[r][i]);
+          cacc[r][i] = v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) zl[r][k] = 0;
       }
-      rows_lds[wave][lane] = row;
-    }
-    wave_sync();
-    int32_t rk[4];
-    int4 rv[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      rk[s] = rows_lds[wave][16 * s + ln];
-      rv[s] = *reinterpret_cast<const int4*>(&rows_lds[wave][16 * s + 4 * lg]);
+      for (int i = 0; i < 8; ++i) acc[r][i] *= alpha[r];
+      l[r] *= alpha[r];
     }
-    // ---- loads ----
-    uint4 kraw[4];
-    uint32_t ksw[4], vsw[4];
-    uint32_t vraw[4][4];  // [s][k]: dword ln of token 16s + 4lg + k
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t r0 = rk[s] < 0 ? 0 : rk[s];
-      kraw[s] = *reinterpret_cast<const uint4*>(p.kc + r0 * (D / 2) + 16 * lg);
-      ksw[s] = f2u(p.ks[r0]);
-      vsw[s] = f2u(p.vs[r0]);
-      const int rr[4] = {rv[s].x, rv[s].y, rv[s].z, rv[s].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int64_t rvk = rr[k] < 0 ? 0 : rr[k];
-        vraw[s][k] = *reinterpret_cast<const uint32_t*>(p.vc + rvk * (D / 2) + 4 * ln);
-      }
-    }
+    empty = true;
+  };
 
+  for (int64_t tile = rsl; tile < ntiles; tile += R) {
     // ---- scores on the matrix cores ----
     float sc[NH][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t w4[4] = {kraw[s].x, kraw[s].y, kraw[s].z, kraw[s].w};
-      int ev[4], od[4];
+      const v4u w4 = kraw[s];
+      int evn[4], odd[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        ev[k] = (int)(w4[k] & 0x0F0F0F0Fu);
-        od[k] = (int)((w4[k] >> 4) & 0x0F0F0F0Fu);
+        evn[k] = (int)(w4[k] & 0x0F0F0F0Fu);
+        odd[k] = (int)((w4[k] >> 4) & 0x0F0F0F0Fu);
       }
-      const v4i kb0 = v4i{ev[0], od[0], ev[1], od[1]};
-      const v4i kb1 = v4i{ev[2], od[2], ev[3], od[3]};
-      const int zpki = (int)(ksw[s] & 0xFu);
+      const v4i kb0 = v4i{evn[0], odd[0], evn[1], odd[1]};
+      const v4i kb1 = v4i{evn[2], odd[2], evn[3], odd[3]};
+      const float zpk = (float)(ksw[s] & 0xFu);
       const float ksc = u2f(ksw[s] & 0xFFFFFFF0u);
+      // masked tokens: min(score, -inf) keeps the arithmetic unconditional
+      const float mask = ((live >> s) & 1u) ? INFINITY : -INFINITY;
 #pragma unroll
       for (int r = 0; r < NH; ++r) {
         v4i c = v4i{0, 0, 0, 0};
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][0], kb0, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][1], kb1, c, 0, 0, 0);
-        // lane (n, g): rows 4g..4g+3 = digits 0..3 of head 4r+g, token 16s+n
-        const float d0 = (float)(c.x - zpki * qsum[r][0]);
-        const float d1 = (float)(c.y - zpki * qsum[r][1]);
-        const float d2 = (float)(c.z - zpki * qsum[r][2]);
-        const float d3 = (float)(c.w - zpki * qsum[r][3]);
+        // lane (n, g): rows 4g..4g+3 = digits 0..3 of head 4r+g, token 16s+n;
+        // each plane minus zp * (digit sum) is an exact small integer
+        const float d0 = __builtin_fmaf(-zpk, qsum[r][0], (float)c.x);
+        const float d1 = __builtin_fmaf(-zpk, qsum[r][1], (float)c.y);
+        const float d2 = __builtin_fmaf(-zpk, qsum[r][2], (float)c.z);
+        const float d3 = __builtin_fmaf(-zpk, qsum[r][3], (float)c.w);
         const float dot = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(d3, 128.0f, d2), 128.0f, d1), 128.0f, d0);
-        sc[r][s] = rk[s] < 0 ? -INFINITY : dot * (qf[r] * ksc);
+        sc[r][s] = fminf(dot * (qf[r] * ksc), mask);
       }
     }
-
-    // ---- online softmax (per head = per 16-lane group) ----
-    float alpha[NH], pr[NH][4];
-#pragma unroll
-    for (int r = 0; r < NH; ++r) {
-      float tm = fmaxf(fmaxf(sc[r][0], sc[r][1]), fmaxf(sc[r][2], sc[r][3]));
-      tm = row16_max(tm);
-      const float mn = fmaxf(m[r], tm);
-      const bool none = (mn == -INFINITY);
-      alpha[r] = none ? 1.0f : __builtin_amdgcn_exp2f(m[r] - mn);
-      float ps = 0.0f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        pr[r][s] = none ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mn);
-        ps += pr[r][s];
-      }
-      l[r] = l[r] * alpha[r] + ps;
-      m[r] = mn;
-    }
-
-    // ---- value weights P' = p * scale_v as 7-bit digit planes ----
     float vsc[4];
-    int zpv[4];
+    uint32_t zp4 = 0;
     float smax = 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       vsc[s] = u2f(vsw[s] & 0xFFFFFFF0u);
-      zpv[s] = (int)(vsw[s] & 0xFu);
-      if (rk[s] >= 0) smax = fmaxf(smax, vsc[s]);
+      zp4 |= (vsw[s] & 0xFu) << (8 * s);
+      smax = fmaxf(smax, vsc[s]);  // masked tokens load scale 0
+    }
+    // the next tile's rows and key-side loads (this tile's are consumed)
+    stage_rows(tile + R);
+    issue_k();
+
+    // ---- reference maximum / weight scale; flush when they move ----
+    float tm[NH];
+    bool move = false;
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      tm[r] = row16_max(fmaxf(fmaxf(sc[r][0], sc[r][1]), fmaxf(sc[r][2], sc[r][3])));
+      move |= tm[r] > mref[r] + (float)kTau;
     }
     smax = row16_max(smax);
-    const int ev_ = smax > 0.0f ? 26 - ((int)((f2u(smax) >> 23) & 0xFF) - 127) : 0;
-    const float pscale = exp2i(ev_);
-    const float pinv = exp2i(-ev_);
-    int zsum[NH][4];
+    // a flush also bounds the int32 digit sums (< 2^31 after 8192 tiles)
+    const bool smove = smax >= sref || ++since_flush >= 8192;
+    if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
+      float alpha[NH];
+#pragma unroll
+      for (int r = 0; r < NH; ++r) {
+        const float mn = fmaxf(mref[r], tm[r]);
+        alpha[r] = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref[r] - mn);
+        mref[r] = mn;
+      }
+      flush(alpha);
+      since_flush = 0;
+      // ev from the largest value scale (the same in every lane): weights
+      // 2^(s - m_ref) * scale <= 2^kTau * sref stay below 2^27 after 2^ev
+      if (smax > 0.0f) {
+        const int e = (int)((f2u(smax) >> 23) & 0xFF) - 127;
+        ev = 26 - kTau - e;
+        sref = exp2i(e + 1);
+      }
+    }
+
+    // ---- weights relative to m_ref as 7-bit digit planes ----
+    const float pscale = exp2i(ev);
+    float vq[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) vq[s] = vsc[s] * pscale;
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       uint32_t dw[4] = {0, 0, 0, 0};
-      int z[4] = {0, 0, 0, 0};
+      float ps = 0.0f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t pi = (uint32_t)__builtin_rintf((pr[r][s] * vsc[s]) * pscale);
+        const float pr = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+        ps += pr;
+        const uint32_t pi = (uint32_t)__builtin_fmaf(pr, vq[s], 0.5f);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t dk = (pi >> (7 * k)) & 127u;
-          dw[k] |= dk << (8 * s);
-          z[k] += (int)dk * zpv[s];
-        }
+        for (int k = 0; k < 4; ++k) dw[k] |= ((pi >> (7 * k)) & 127u) << (8 * s);
       }
+      l[r] += ps;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        p8_lds[wave][r][lg][k][ln] = dw[k];
-        zsum[r][k] = row16_isum(z[k]);
+        p8[r][lg][k][ln] = dw[k];
+        zl[r][k] += (int)__builtin_amdgcn_udot4(dw[k], zp4, 0u, false);
       }
     }
+    empty = false;
     wave_sync();
 
     // ---- value MFMAs: B operands by nibble transpose ----
@@ -339,87 +445,108 @@ __global__ __launch_bounds__(64 * W) void decode_int4_mfma_kernel(DecodeParams p
         vb[2 * bb + 1][k] = (t[bb] >> 4) & 0x0F0F0F0Fu;
       }
     }
+    issue_v();  // next tile's value rows (staged above)
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       // A operand: lane (m = 4h' + piece, g) reads the digit plane of head
       // 4r+h' for tokens 16s + 4g + k at byte (k, s)
-      const uint4 a4 = *reinterpret_cast<const uint4*>(&p8_lds[wave][r][ln >> 2][ln & 3][4 * lg]);
+      const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[r][ln >> 2][ln & 3][4 * lg]);
       const v4i pa = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, v4i{0, 0, 0, 0}, 0, 0, 0);
-        // lane (n, g): digits 0..3 of head 4r+g, dim 8n+i
-        const float e0 = (float)(c.x - zsum[r][0]);
-        const float e1 = (float)(c.y - zsum[r][1]);
-        const float e2 = (float)(c.z - zsum[r][2]);
-        const float e3 = (float)(c.w - zsum[r][3]);
-        const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-        acc[r][i] = __builtin_fmaf(val, pinv, acc[r][i] * alpha[r]);
+        cacc[r][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, cacc[r][i], 0, 0, 0);
       }
     }
-    wave_sync();  // p8_lds / rows_lds are rewritten by the next tile
+    wave_sync();  // the digit planes are rewritten by the next tile
+  }
+  {
+    float one[NH];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) one[r] = 1.0f;
+    flush(one);
   }
 
-  // ---------------- merge the waves, write the split partial ----------------
-  __syncthreads();  // qrot (aliased by `big`) is dead from here on
-  float* red = big;  // [W][NHEAD][D + 2]
+  // ---------------- write the split partial ----------------
+  // acc / l are relative to m_ref per head (l: per-lane partial sums)
+  float lt[NH];
+#pragma unroll
+  for (int r = 0; r < NH; ++r) lt[r] = row16_sum(l[r]);
+  if (R == 1) {
+    // this wave alone covered the split for its heads
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const int hh = 4 * r + lg;
+      if (hh < g) {
+        float* out = p.ws + (((int64_t)b * p.hq + h0 + hh) * p.splits + s_idx) * (D + 1);
+        const float inv = lt[r] > 0.0f ? 1.0f / lt[r] : 0.0f;
+        float4 o0, o1;
+        o0.x = acc[r][0] * inv; o0.y = acc[r][1] * inv; o0.z = acc[r][2] * inv; o0.w = acc[r][3] * inv;
+        o1.x = acc[r][4] * inv; o1.y = acc[r][5] * inv; o1.z = acc[r][6] * inv; o1.w = acc[r][7] * inv;
+        float* dst = out + 8 * ln;
+        dst[0] = o0.x; dst[1] = o0.y; dst[2] = o0.z; dst[3] = o0.w;
+        dst[4] = o1.x; dst[5] = o1.y; dst[6] = o1.z; dst[7] = o1.w;
+        if (ln == 0) out[D] = lt[r] > 0.0f ? (mref[r] + __log2f(lt[r])) * kLn2 : -INFINITY;
+      }
+    }
+    return;
+  }
+  // R waves shared each head: log-sum-exp merge through LDS
 #pragma unroll
   for (int r = 0; r < NH; ++r) {
-    const float lt = row16_sum(l[r]);
-    float* dst = red + ((wave * NHEAD) + 4 * r + lg) * (D + 2);
+    float* dst = &red[wave][4 * r + lg][0];
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[8 * ln + i] = acc[r][i];
     if (ln == 0) {
-      dst[D] = m[r];
-      dst[D + 1] = lt;
+      dst[D] = mref[r];
+      dst[D + 1] = lt[r];
     }
   }
   __syncthreads();
-  for (int i = tid; i < g * (D + 1); i += 64 * W) {
-    const int hh = i / (D + 1), d = i % (D + 1);
+  for (int i = tid; i < HG * g * (D + 1); i += 64 * W) {
+    const int hw = i / (g * (D + 1));          // wave (= head) within the group
+    const int hh = (i / (D + 1)) % g, d = i % (D + 1);
     float mm = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) mm = fmaxf(mm, red[(w * NHEAD + hh) * (D + 2) + D]);
+    for (int rr = 0; rr < R; ++rr) mm = fmaxf(mm, red[hw + rr * HG][hh][D]);
     float lsum = 0.0f, o = 0.0f;
     if (mm != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float* src = red + (w * NHEAD + hh) * (D + 2);
+      for (int rr = 0; rr < R; ++rr) {
+        const float* src = &red[hw + rr * HG][hh][0];
         const float a = __builtin_amdgcn_exp2f(src[D] - mm);
         lsum += src[D + 1] * a;
         if (d < D) o += src[d] * a;
       }
     }
-    float* out = p.ws + (((int64_t)b * p.hq + h0 + hh) * p.splits + s_idx) * (D + 1);
+    const int head = (grp * HG + hw) * g + hh;
+    float* out = p.ws + (((int64_t)b * p.hq + head) * p.splits + s_idx) * (D + 1);
     if (d < D) out[d] = lsum > 0.0f ? o / lsum : 0.0f;
     else out[D] = lsum > 0.0f ? (mm + __log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
 template <int NH, int W>
-hipError_t launch(const DecodeParams& p, hipStream_t st) {
-  const uint32_t blocks = (uint32_t)p.B * p.hk * p.splits;
-  hipLaunchKernelGGL((decode_int4_mfma_kernel<NH, W>), dim3(blocks), dim3(64 * W), 0, st, p);
+hipError_t launch(const DecodeParams& p, int hg, hipStream_t st) {
+  const uint32_t blocks = (uint32_t)p.B * (p.hk / hg) * p.splits;
+  hipLaunchKernelGGL((decode_int4_mfma_kernel<NH, W>), dim3(blocks), dim3(64 * W), 0, st, p, hg);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_int4_mfma(const DecodeParams& p, hipStream_t st) {
-  if (p.d != D || p.key_fmt != KF_INT4 || p.g > 16) return hipErrorNotSupported;
-  // cache rows are addressed with 32-bit indices
-  if (p.num_blocks * (int64_t)p.block_size * p.hk >= ((int64_t)1 << 31)) return hipErrorNotSupported;
-  // eight waves per workgroup when there are few (batch, split, kv head)
-  // units, so that the grid still holds enough waves to cover HBM latency
-  const int64_t units = (int64_t)p.B * p.hk * p.splits;
-  const bool wide = units < 1024;
+  if (p.d != D || p.key_fmt != KF_INT4 || p.g > 8) return hipErrorNotSupported;
+  // cache bytes are addressed with 32-bit buffer offsets
+  if (p.num_blocks * (int64_t)p.block_size * p.hk * (D / 2) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  // Heads per workgroup: as many kv heads as fit in 8 waves (whole token
+  // rows for Hk <= 8), then split them into smaller groups with several
+  // waves per head while there are too few workgroups to fill the chip.
+  int hg = 1;
+  while (hg * 2 <= 8 && p.hk % (hg * 2) == 0) hg *= 2;
+  const int64_t units_per_group = (int64_t)p.B * p.splits;
+  while (hg > 1 && units_per_group * (p.hk / hg) < 256) hg /= 2;
   const int nh = (p.g + 3) / 4;
-  switch (nh) {
-    case 1: return wide ? launch<1, 8>(p, st) : launch<1, 4>(p, st);
-    case 2: return wide ? launch<2, 8>(p, st) : launch<2, 4>(p, st);
-    default: return launch<4, 4>(p, st);
-  }
+  if (nh == 1) return launch<1, 8>(p, hg, st);
+  return launch<2, 8>(p, hg, st);
 }
 
 }  // namespace tqk

@@ -18,6 +18,7 @@ namespace {
 
 template <int D, bool ROTATE>
 __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
+  constexpr int CH = 16;  // splits whose loads are in flight together
   __shared__ float sh[D];
   const int bh = blockIdx.x;
   const int b = bh / p.hq;
@@ -26,19 +27,38 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
   seq = seq < 0 ? 0 : (seq > cap ? cap : seq);
   const int64_t split_len = (seq + p.splits - 1) / p.splits;
+  // non-empty splits are a prefix: s * split_len < seq
+  const int nsplit = seq == 0 ? 0 : (int)((seq + split_len - 1) / split_len);
   const float* part = p.ws + (int64_t)bh * p.splits * (D + 1);
 
-  float mx = -INFINITY;
-  for (int s = 0; s < p.splits && split_len * s < seq; ++s) mx = fmaxf(mx, part[s * (D + 1) + D]);
-  float wsum = 0.0f, o = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < p.splits && split_len * s < seq; ++s) {
-      const float w = __expf(part[s * (D + 1) + D] - mx);
-      wsum += w;
-      o += w * part[s * (D + 1) + d];
+  // running log-sum-exp over chunks of splits (natural-log partials)
+  float mx = -INFINITY, wsum = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < nsplit; s0 += CH) {
+    float ls[CH], pv[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int s = s0 + j;
+      const bool ok = s < nsplit;
+      ls[j] = ok ? part[s * (D + 1) + D] : -INFINITY;
+      pv[j] = ok ? part[s * (D + 1) + d] : 0.0f;
     }
-    o /= wsum;
+    float cm = ls[0];
+#pragma unroll
+    for (int j = 1; j < CH; ++j) cm = fmaxf(cm, ls[j]);
+    const float nm = fmaxf(mx, cm);
+    if (nm == -INFINITY) continue;
+    const float sc = __expf(mx - nm);
+    wsum *= sc;
+    o *= sc;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float w = __expf(ls[j] - nm);
+      wsum += w;
+      o += w * pv[j];
+    }
+    mx = nm;
   }
+  if (mx != -INFINITY) o /= wsum;
   if constexpr (ROTATE) {
     sh[d] = o;
     __syncthreads();
