@@ -1,4 +1,4 @@
-// Internal launch interface between the C ABI layer (api.cpp) and the
+// Internal launch interface between the C ABI layer (api.hip) and the
 // kernel translation units. Arguments arrive here already validated.
 #pragma once
 #include <hip/hip_runtime.h>
