@@ -140,7 +140,7 @@ def run_int4(args, torch, tq, W, name):
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.seq_lens).to(dev)
     S = w.num_splits
-    ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.d, S) // 4, dtype=torch.float32,
+    ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.hk, w.d, S) // 4, dtype=torch.float32,
                      device=dev)
     out = torch.empty(w.B, w.hq, w.d, dtype=torch.float32, device=dev)
     lse = torch.empty(w.B, w.hq, dtype=torch.float32, device=dev)
@@ -309,7 +309,7 @@ def run_other(args, torch, tq, W):
         bt = torch.from_numpy(w.block_table).to(dev)
         sl = torch.from_numpy(w.seq_lens).to(dev)
         cen = torch.linspace(-0.2, 0.2, 8, device=dev)
-        ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.d, w.num_splits) // 4,
+        ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.hk, w.d, w.num_splits) // 4,
                          dtype=torch.float32, device=dev)
         calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
                                    key_fmt=fmt[0], val_fmt=fmt[1],

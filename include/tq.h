@@ -157,13 +157,23 @@ typedef struct tq_decode_args {
   const float* centroids;      /* device [2^b] fp32 (centroid keys)        */
   const float* rot_signs;      /* device [D] +-1 or NULL (centroid keys)   */
   /* outputs */
-  float* workspace; /* device, tq_decode_workspace_bytes(B, Hq, D, S) bytes */
+  float* workspace; /* device scratch of the stage-1 partials, at least
+                       tq_decode_workspace_bytes(B, Hq, Hk, D, S) bytes;
+                       its contents on entry do not matter              */
+  int64_t workspace_bytes; /* size of `workspace` in bytes (validated)   */
   float* out;       /* device [B, Hq, D] fp32                               */
   float* lse;       /* device [B, Hq] fp32, or NULL                         */
 } tq_decode_args;
 
-/* Bytes of the stage-1 partials ([B, Hq, S, D+1] fp32). */
-size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+/*
+ * Bytes of the stage-1 workspace: the per-split partials [B, Hq, S, D+1]
+ * fp32 (triton_turboquant_decode.py: the stage-1 output buffer), followed by
+ * the piece slots of the balanced INT4 decode, which spreads the tiles of all
+ * splits evenly over the workgroups and writes a split cut between two
+ * workgroups as pieces that stage 2 merges like splits (2 * nw * Hq * (D+1)
+ * fp32, nw = max(1, 2048 / Hk)). Returns 0 for invalid sizes.
+ */
+size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hk, int32_t D,
                                  int32_t num_kv_splits);
 
 /* Padded combined-slot size for a TurboQuant format, or -1 if invalid. */

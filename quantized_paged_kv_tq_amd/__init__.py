@@ -47,7 +47,8 @@ class DecodeArgs(C.Structure):
         ("k_scale_cache", C.c_void_p), ("v_scale_cache", C.c_void_p), ("rht_signs", C.c_void_p),
         ("kv_cache", C.c_void_p), ("slot_bytes", C.c_int32),
         ("centroids", C.c_void_p), ("rot_signs", C.c_void_p),
-        ("workspace", C.c_void_p), ("out", C.c_void_p), ("lse", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_int64),
+        ("out", C.c_void_p), ("lse", C.c_void_p),
     ]
 
 
@@ -62,7 +63,7 @@ SYMBOLS = {
         C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
         C.c_void_p]),
-    "tq_decode_workspace_bytes": (C.c_size_t, [C.c_int32] * 4),
+    "tq_decode_workspace_bytes": (C.c_size_t, [C.c_int32] * 5),
     "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
@@ -159,8 +160,8 @@ def tq_reshape_and_cache_int4(key, value, key_cache, value_cache, slot_mapping, 
                     v_scale_cache=v_scale_cache, rht_signs=rht_signs).run(stream, key.device)
 
 
-def tq_decode_workspace_bytes(B, Hq, D, num_kv_splits):
-    return lib().tq_decode_workspace_bytes(B, Hq, D, num_kv_splits)
+def tq_decode_workspace_bytes(B, Hq, Hk, D, num_kv_splits):
+    return lib().tq_decode_workspace_bytes(B, Hq, Hk, D, num_kv_splits)
 
 
 def tq_slot_bytes(D, key_fmt, val_fmt):
@@ -215,7 +216,7 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
         raise ValueError("block_table must be [B, max_blocks], seq_lens [B]")
     dev = query.device
     if workspace is None:
-        nbytes = tq_decode_workspace_bytes(B, hq, d, num_kv_splits)
+        nbytes = tq_decode_workspace_bytes(B, hq, hk, d, num_kv_splits)
         workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty(B, hq, d, dtype=torch.float32, device=dev)
@@ -224,7 +225,7 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
     _need(workspace, torch.float32, "workspace")
     _need(out, torch.float32, "out")
     _need(lse, torch.float32, "lse")
-    if workspace.numel() * 4 < tq_decode_workspace_bytes(B, hq, d, num_kv_splits):
+    if workspace.numel() * 4 < tq_decode_workspace_bytes(B, hq, hk, d, num_kv_splits):
         raise ValueError("workspace too small")
     a = DecodeArgs()
     a.struct_size = C.sizeof(DecodeArgs)
@@ -241,6 +242,7 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
     a.kv_cache, a.slot_bytes = _ptr(kv_cache), slot_bytes
     a.centroids, a.rot_signs = _ptr(centroids), _ptr(rot_signs)
     a.workspace, a.out, a.lse = _ptr(workspace), _ptr(out), _ptr(lse)
+    a.workspace_bytes = workspace.numel() * 4
     keep = [query, block_table, seq_lens, key_cache, value_cache, k_scale_cache, v_scale_cache,
             rht_signs, kv_cache, centroids, rot_signs, workspace, out, lse]
     return Prepared(lib().tq_decode_attention, (C.byref(a),), keep + [a]), out, lse

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "tq.h"
+#include "balance.h"
 #include "tq_internal.h"
 
 namespace {
@@ -47,7 +48,7 @@ extern "C" {
 
 const char* tq_last_error(void) { return g_err; }
 
-int tq_version(void) { return 1; }
+int tq_version(void) { return 2; }
 
 int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt) {
   if (D <= 0 || D > 1024 || (D & (D - 1)) != 0) return -1;
@@ -57,9 +58,15 @@ int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt) {
   return (raw + 15) / 16 * 16;
 }
 
-size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t S) {
-  if (B < 0 || Hq < 0 || D < 0 || S < 0) return 0;
-  return (size_t)B * Hq * S * (D + 1) * sizeof(float);
+size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hk, int32_t D, int32_t S) {
+  if (B < 0 || Hq < 0 || Hk <= 0 || D < 0 || S < 0) return 0;
+  // per-split partials, then the piece slots of the balanced INT4 decode:
+  // [Hk / wgh][nw][2][wgh * g][D + 1] = 2 * nw * Hq * (D + 1) floats
+  const size_t parts = (size_t)B * Hq * S * (D + 1);
+  const int g = Hk > 0 && Hq % Hk == 0 ? Hq / Hk : 1;
+  const size_t pieces = (size_t)2 * tqk::balance_max_wgs(Hk, g) * Hq * (D + 1);
+  const size_t prefix = ((size_t)B + 1 + 3) / 4 * 4;  // tile-list prefix sums (int32)
+  return (parts + pieces + prefix) * sizeof(float);
 }
 
 int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dtype,
@@ -158,6 +165,11 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   }
   if (!aligned(a->query, 16) || !aligned(a->workspace, 16) || !aligned(a->out, 16))
     return fail(TQ_EINVAL, "query / workspace / out must be 16-byte aligned");
+  {
+    const size_t need = tq_decode_workspace_bytes(a->B, a->Hq, a->Hk, a->D, a->num_kv_splits);
+    if (a->workspace_bytes < 0 || (size_t)a->workspace_bytes < need)
+      return fail(TQ_EINVAL, "workspace_bytes %lld < %zu", (long long)a->workspace_bytes, need);
+  }
   p.B = a->B; p.hq = a->Hq; p.hk = a->Hk; p.d = a->D; p.g = a->Hq / a->Hk;
   p.block_size = a->block_size; p.max_blocks = a->max_blocks; p.splits = a->num_kv_splits;
   p.key_fmt = a->key_fmt; p.val_fmt = a->val_fmt; p.norm_correction = a->norm_correction;
@@ -167,6 +179,13 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   p.rht_signs = a->rht_signs; p.kv = a->kv_cache; p.slot_bytes = a->slot_bytes;
   p.centroids = a->centroids; p.rot_signs = a->rot_signs;
   p.ws = a->workspace; p.out = a->out; p.lse = a->lse;
+  p.nw = 0; p.wgh = 1;
+  p.wsp = a->workspace + (int64_t)a->B * a->Hq * a->num_kv_splits * (a->D + 1);
+  {
+    const int g = a->Hq / a->Hk;
+    p.wsx = reinterpret_cast<int*>(
+        p.wsp + (int64_t)2 * tqk::balance_max_wgs(a->Hk, g) * a->Hq * (a->D + 1));
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipErrorNotSupported;

@@ -54,13 +54,19 @@ struct DecodeParams {
   float* ws;     // [B, Hq, S, D+1]
   float* out;    // [B, Hq, D]
   float* lse;    // [B, Hq] or null
+  // Balanced partition of the INT4 decode (balance.h), set by its launcher:
+  // nw workgroups per group of wgh kv heads; 0 = one partial per split only.
+  int nw, wgh;
+  float* wsp;    // piece slots [Hk / wgh][nw][2][wgh * g][D+1], after ws
+  int* wsx;      // [B + 1] tile-list prefix sums (stage 1 writes, stage 2 reads)
 };
 
 // Format-generic vector stage 1 (every key/value format).
 hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t st);
 // INT4 stage 1 on the matrix cores; returns hipErrorNotSupported when the
 // shape is outside what it handles (the caller then uses the generic one).
-hipError_t launch_decode_int4_mfma(const DecodeParams& p, hipStream_t st);
+// Sets p.nw / p.wgh for stage 2.
+hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st);
 // Stage 2: log-sum-exp merge of the split partials (+ inverse RHT for INT4).
 hipError_t launch_merge(const DecodeParams& p, hipStream_t st);
 

@@ -40,12 +40,19 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_sizes(L):
-    assert L.tq_version() == 1
+    assert L.tq_version() == 2
     assert tq.tq_slot_bytes(128, tq.KEY_FP8, tq.VAL_U4) == 208
     assert tq.tq_slot_bytes(128, tq.KEY_MSE3, tq.VAL_U3) == 112
     assert tq.tq_slot_bytes(128, tq.KEY_INT4, tq.VAL_U4) == -1
     assert tq.tq_slot_bytes(96, tq.KEY_FP8, tq.VAL_U4) == -1
-    assert tq.tq_decode_workspace_bytes(32, 32, 128, 8) == 32 * 32 * 8 * 129 * 4
+    # per-split partials + the balanced decode's piece slots (2 * nw * Hq rows,
+    # (nw = 2048 / (Hk * ceil(g / 4)) workgroups), then B + 1 prefix sums
+    # padded to 4 words
+    assert tq.tq_decode_workspace_bytes(32, 32, 8, 128, 8) == \
+        ((32 * 32 * 8 + 2 * 256 * 32) * 129 + 36) * 4
+    assert tq.tq_decode_workspace_bytes(2, 4, 1, 64, 4) == ((2 * 4 * 4 + 2 * 2048 * 4) * 65 + 4) * 4
+    assert tq.tq_decode_workspace_bytes(1, 64, 8, 128, 64) == ((64 * 64 + 2 * 128 * 64) * 129 + 4) * 4
+    assert tq.tq_decode_workspace_bytes(2, 4, 0, 64, 4) == 0
 
 
 def test_decode_args_layout_matches_header(tmp_path):
@@ -92,6 +99,15 @@ def test_decode_rejects_invalid(L, kw, code):
     a = _args(**kw)
     assert L.tq_decode_attention(C.byref(a), None) == code
     assert tq.last_error() != ""
+
+
+def test_decode_rejects_small_workspace(L):
+    need = tq.tq_decode_workspace_bytes(2, 4, 1, 64, 4)
+    kw = dict(query=16, block_table=16, seq_lens=16, workspace=16, out=16, key_cache=16,
+              value_cache=16, k_scale_cache=16, v_scale_cache=16, rht_signs=16)
+    a = _args(workspace_bytes=need - 4, **kw)
+    assert L.tq_decode_attention(C.byref(a), None) == tq.TQ_EINVAL
+    assert "workspace_bytes" in tq.last_error()
 
 
 def test_decode_null_args_and_empty_batch(L):

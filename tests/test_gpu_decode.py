@@ -92,6 +92,49 @@ def test_int4_random_cache_bytes():
         assert_close(got, ref, lse, ref_lse, "random bytes")
 
 
+def test_int4_balanced_many_sequences():
+    """More sequences than threads per workgroup (two per thread in the
+    prefix sums), empty ones interleaved, ranges that cross many sequence
+    and split boundaries, and workgroups with empty ranges."""
+    rng = np.random.default_rng(143)
+    seq = rng.choice([0, 1, 5, 63, 64, 65, 130, 200, 777], size=600).astype(np.int32)
+    w = W.custom_decode_workload(143, 600, 8, 2, 128, 16, 3, seq, 7, "bf16")
+    kc, vc, ks, vs = W.random_int4_cache(w)
+    c = dict(kc=kc, vc=vc, ks=ks, vs=vs, signs=W.rht_signs(128))
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    got, lse = gpu_int4_decode(w, q, c)
+    assert_close(got, ref, lse, ref_lse, "600 sequences")
+
+
+@pytest.mark.parametrize("seq,S", [([1, 3], 2), ([64, 65, 1], 7), ([2000], 1), ([2000], 256)])
+def test_int4_balanced_few_tiles(seq, S):
+    """Fewer tiles than workgroups (most ranges empty), single-tile splits and
+    one split spread over many workgroups."""
+    w = W.custom_decode_workload(144 + len(seq) + S, len(seq), 32, 8, 128, 16, S, seq, 3, "bf16")
+    c = int4_caches(w)
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    got, lse = gpu_int4_decode(w, q, c)
+    assert_close(got, ref, lse, ref_lse, "seq %s S=%d" % (seq, S))
+
+
+def test_int4_balanced_chunked_range():
+    """Ranges longer than the 64 tiles a workgroup resolves at a time: one
+    sequence of 1,056,896 tokens over 8 kv heads (16,514 tiles on 256
+    workgroups), random cache bytes, sampled rows."""
+    seq = [64 * 64 * 256 + 64 * 130]
+    w = W.custom_decode_workload(145, 1, 32, 8, 128, 64, 4, seq, 0, "bf16")
+    kc, vc, ks, vs = W.random_int4_cache(w)
+    c = dict(kc=kc, vc=vc, ks=ks, vs=vs, signs=W.rht_signs(128))
+    q = W.query(w)
+    got, lse = gpu_int4_decode(w, q, c)
+    rows = np.array([0, 13, 31], np.int32)
+    ref, ref_lse = _oracle_int4(w, q, c, rows=rows)
+    assert_close(got[rows], ref, lse[rows], ref_lse, "chunked range")
+    assert np.all(np.isfinite(got))
+
+
 def _sampled_rows(w, n, seed):
     rng = np.random.default_rng(seed)
     return np.sort(rng.choice(w.B * w.hq, size=min(n, w.B * w.hq), replace=False)).astype(np.int32)
