@@ -88,6 +88,8 @@ int tq_version(void);
  *   key_cache, value_cache   device, [num_blocks, block_size, Hk, D/2] u8
  *   k_scale_cache, v_scale_cache device, [num_blocks, block_size, Hk] fp32
  *   D in {64, 128}. num_tokens == 0 returns TQ_OK without launching.
+ *   Alignment: key, value, rht_signs 16 B; key_cache, value_cache and
+ *   slot_mapping 8 B; the scale caches 4 B (TQ_EINVAL otherwise).
  *   Slots must be unique (duplicates race: an unspecified writer wins).
  */
 int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dtype,
@@ -190,6 +192,7 @@ int tq_decode_attention(const tq_decode_args* args, void* stream);
  * Bit-exact function of the input.
  *   x_bf16 device [rows, 128] bf16; y_e4m3 device [rows, 128] u8;
  *   scale device [rows] fp32. rows == 0 returns TQ_OK without launching.
+ *   Alignment: x_bf16 and y_e4m3 16 B, scale 4 B (TQ_EINVAL otherwise).
  */
 int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
                       float* scale, void* stream);

@@ -92,9 +92,10 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
       !k_scale_cache || !v_scale_cache)
     return fail(TQ_EINVAL, "null pointer argument");
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(rht_signs, 16) ||
-      !aligned(slot_mapping, 8) || !aligned(key_cache, 4) || !aligned(value_cache, 4) ||
+      !aligned(slot_mapping, 8) || !aligned(key_cache, 8) || !aligned(value_cache, 8) ||
       !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4))
-    return fail(TQ_EINVAL, "misaligned pointer (key/value/signs 16 B, caches 4 B)");
+    return fail(TQ_EINVAL,
+                "misaligned pointer (key/value/signs 16 B, key/value caches 8 B, scale caches 4 B)");
   tqk::ReshapeParams p{key, value, slot_mapping, rht_signs, key_cache, value_cache,
                        k_scale_cache, v_scale_cache, num_tokens, num_blocks, num_kv_heads,
                        head_dim, kv_dtype, block_size};
@@ -110,8 +111,8 @@ int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3, float* 
     return TQ_OK;
   }
   if (!x_bf16 || !y_e4m3 || !scale) return fail(TQ_EINVAL, "null pointer argument");
-  if (!aligned(x_bf16, 16) || !aligned(y_e4m3, 8) || !aligned(scale, 4))
-    return fail(TQ_EINVAL, "misaligned pointer (x 16 B, y 8 B, scale 4 B)");
+  if (!aligned(x_bf16, 16) || !aligned(y_e4m3, 16) || !aligned(scale, 4))
+    return fail(TQ_EINVAL, "misaligned pointer (x 16 B, y 16 B, scale 4 B)");
   if (rows > ((int64_t)1 << 36)) return fail(TQ_EINVAL, "rows too large");
   return launched(tqk::launch_fwht128_fp8(x_bf16, rows, y_e4m3, scale,
                                           static_cast<hipStream_t>(stream)),

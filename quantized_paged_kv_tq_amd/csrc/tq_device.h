@@ -125,6 +125,62 @@ __device__ __forceinline__ float butterfly_lanes(float x, bool upper) {
   return upper ? (p - x) : (x + p);
 }
 
+// Value of lane (lane ^ M), M in {1, 2, 4, 8}, with DPP moves only (no LDS
+// crossbar). Row rotations move data to higher lanes: with row_ror:N lane i
+// reads lane (i - N) mod 16. Partner i ^ 4 is i + 4 in banks 0 and 2 (lanes
+// 0-3, 8-11) and i - 4 in banks 1 and 3; partner i ^ 8 is i - 8 mod 16.
+template <int M>
+__device__ __forceinline__ float dpp_xor(float v) {
+  const int x = __float_as_int(v);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    r = __builtin_amdgcn_update_dpp(x, x, 0x12C, 0xF, 0x5, false);  // row_ror:12, banks 0, 2
+    r = __builtin_amdgcn_update_dpp(r, x, 0x124, 0xF, 0xA, false);  // row_ror:4, banks 1, 3
+  } else {
+    static_assert(M == 8, "xor distance within a 16-lane row");
+    r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  }
+  return __int_as_float(r);
+}
+
+// Butterfly between lanes i and i ^ M (M <= 8): the lane with bit M clear
+// keeps x + partner, its partner keeps partner - x. sgn is +1 / -1 for
+// those lanes; sgn * x is exact, so the single rounding of the fma equals
+// that of the plain sum or difference.
+template <int M>
+__device__ __forceinline__ float butterfly16(float x, float sgn) {
+  return __builtin_fmaf(sgn, x, dpp_xor<M>(x));
+}
+
+// Min / max over aligned groups of N lanes (N in {2, 4, 8, 16}) by DPP.
+template <int N>
+__device__ __forceinline__ float group16_max(float v) {
+  if constexpr (N >= 16) v = fmaxf(v, dpp_xor<8>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_xor<4>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_xor<2>(v));
+  if constexpr (N >= 2) v = fmaxf(v, dpp_xor<1>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group16_min(float v) {
+  if constexpr (N >= 16) v = fminf(v, dpp_xor<8>(v));
+  if constexpr (N >= 8) v = fminf(v, dpp_xor<4>(v));
+  if constexpr (N >= 4) v = fminf(v, dpp_xor<2>(v));
+  if constexpr (N >= 2) v = fminf(v, dpp_xor<1>(v));
+  return v;
+}
+
+// Round to bfloat16 (nearest, ties to even) and back with the hardware
+// convert; finite inputs.
+__device__ __forceinline__ float round_to_bf16_hw(float x) {
+  const __bf16 h = (__bf16)x;
+  return u2f((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
 // Workgroup index remap for 8 XCDs: hardware dispatches workgroup i to XCD
 // i % 8. Renumbering so that each XCD receives a contiguous range of
 // logical indices keeps neighbouring logical workgroups (which share cache
