@@ -88,8 +88,9 @@ int tq_version(void);
  *   key_cache, value_cache   device, [num_blocks, block_size, Hk, D/2] u8
  *   k_scale_cache, v_scale_cache device, [num_blocks, block_size, Hk] fp32
  *   D in {64, 128}. num_tokens == 0 returns TQ_OK without launching.
- *   Alignment: key, value, rht_signs 16 B; key_cache, value_cache and
- *   slot_mapping 8 B; the scale caches 4 B (TQ_EINVAL otherwise).
+ *   Alignment: key, value, rht_signs 16 B; slot_mapping, key_cache and
+ *   value_cache 8 B; the scale caches 4 B (TQ_EINVAL otherwise).
+ *   num_tokens * Hk < 2^31.
  *   Slots must be unique (duplicates race: an unspecified writer wins).
  */
 int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dtype,

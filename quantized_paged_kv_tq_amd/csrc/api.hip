@@ -95,7 +95,9 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
       !aligned(slot_mapping, 8) || !aligned(key_cache, 8) || !aligned(value_cache, 8) ||
       !aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4))
     return fail(TQ_EINVAL,
-                "misaligned pointer (key/value/signs 16 B, key/value caches 8 B, scale caches 4 B)");
+                "misaligned pointer (key/value/signs 16 B, slots and caches 8 B, scale caches 4 B)");
+  if (num_tokens * num_kv_heads >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "num_tokens * num_kv_heads must be below 2^31");
   tqk::ReshapeParams p{key, value, slot_mapping, rht_signs, key_cache, value_cache,
                        k_scale_cache, v_scale_cache, num_tokens, num_blocks, num_kv_heads,
                        head_dim, kv_dtype, block_size};

@@ -4,8 +4,9 @@
 // Per 128-wide bf16 row: fp32 butterflies (strides 1 -> 64), multiply by the
 // fp32 value of 1/sqrt(128), round to bf16, absmax with a 1e-4 floor, scale =
 // the power of two at or above absmax * fl(1/448), then E4M3 of
-// clamp(x / scale, +-448). Eight lanes per row, sixteen elements per lane;
-// a 256-lane workgroup handles two passes of 32 rows.
+// clamp(x / scale, +-448). Eight lanes per row; lane l holds elements 8l..8l+7
+// and 64+8l..64+8l+7 (two fully coalesced 16-byte loads per row); a 256-lane
+// workgroup handles two passes of 32 rows.
 //
 // The ceiling of log2 is taken exactly from the exponent bits (the value is
 // a power of two iff its mantissa bits are zero); division by the power-of-
@@ -31,8 +32,10 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
   for (int r = 0; r < R; ++r) {
     row[r] = ((int64_t)blockIdx.x * R + r) * 32 + (threadIdx.x >> 3);
     if (row[r] < rows) {
-      const uint4* src = reinterpret_cast<const uint4*>(x_bf16 + row[r] * 128 + li * 16);
-      const uint4 a = src[0], b = src[1];
+      // elements 8l .. 8l+7 and 64 + 8l .. 64 + 8l + 7
+      const uint16_t* src = x_bf16 + row[r] * 128 + li * 8;
+      const uint4 a = *reinterpret_cast<const uint4*>(src);
+      const uint4 b = *reinterpret_cast<const uint4*>(src + 64);
       const uint32_t ws[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -46,9 +49,10 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    // strides 1 .. 8 inside the lane, 16 .. 64 across lanes
+    // strides 1, 2, 4 inside each half, 8 .. 32 across lanes, 64 between
+    // the halves
 #pragma unroll
-    for (int h = 1; h < 16; h <<= 1) {
+    for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         if ((j & h) == 0) {
@@ -63,6 +67,12 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
       x[r][j] = butterfly16<1>(x[r][j], sg[0]);
       x[r][j] = butterfly16<2>(x[r][j], sg[1]);
       x[r][j] = butterfly16<4>(x[r][j], sg[2]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = x[r][j], b = x[r][j + 8];
+      x[r][j] = a + b;
+      x[r][j + 8] = a - b;
     }
     float amax = 0.0f;
 #pragma unroll
@@ -87,7 +97,8 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
       w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], v, true);
     }
     if (row[r] < rows) {
-      *reinterpret_cast<uint4*>(y + row[r] * 128 + li * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint2*>(y + row[r] * 128 + li * 8) = make_uint2(w[0], w[1]);
+      *reinterpret_cast<uint2*>(y + row[r] * 128 + 64 + li * 8) = make_uint2(w[2], w[3]);
       if (li == 0) scale_out[row[r]] = u2f(sb);
     }
   }

@@ -6,11 +6,15 @@
 // rotated tensors in memory; here each source row is read once, rotated in
 // registers and written straight into the paged cache.
 //
-// Lane layout: a row of D elements is spread over D/16 consecutive lanes,
-// 16 elements per lane (element i = 16 * lane_in_row + j). Butterfly strides
-// 1, 2, 4, 8 run inside a lane; strides 16 .. D/2 pair lanes whose index
-// differs by stride/16 (DPP moves). Strides run 1 -> D/2, the order that
-// fixes the fp32 rounding. A lane packs its 16 codes into 8 bytes.
+// Lane layout: a row of D elements is spread over D/16 consecutive lanes;
+// lane l holds elements 8l .. 8l+7 and D/2 + 8l .. D/2 + 8l + 7, so that each
+// of its two 16-byte loads (bf16) is part of one contiguous 128-byte span per
+// row. Butterfly strides 1, 2, 4 run inside each half of the lane, strides
+// 8 .. D/4 pair lanes whose index differs by stride/8 (DPP moves), and
+// stride D/2 pairs the two halves inside the lane: strides run 1 -> D/2, the
+// order that fixes the fp32 rounding. A lane packs its codes into two
+// 4-byte words (bytes 4l and D/4 + 4l of the packed row); neighbouring
+// lanes swap one word so that each stores 8 contiguous bytes.
 //
 // Bit exactness: compiled without fp contraction; the one fused multiply-add
 // of the quantizer is explicit, division and reciprocal are IEEE.
@@ -19,15 +23,14 @@
 
 namespace tqk {
 
-// 16 consecutive source elements -> fp32
+// 8 consecutive source elements -> fp32
 template <int DT>
-__device__ __forceinline__ void load16(const void* __restrict__ base, int64_t elem, float x[16]) {
+__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t elem, float x[8]) {
   if constexpr (DT == TQ_DT_BF16 || DT == TQ_DT_F16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-    const uint4 a = p[0], b = p[1];
-    const uint32_t ws[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       if constexpr (DT == TQ_DT_BF16) {
         x[2 * k] = bf16_lo(ws[k]);
         x[2 * k + 1] = bf16_hi(ws[k]);
@@ -38,21 +41,18 @@ __device__ __forceinline__ void load16(const void* __restrict__ base, int64_t el
     }
   } else {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 a = p[k];
-      x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
-    }
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
 }
 
-// FWHT of a row held as 16 elements per lane over LPR lanes: strides 1 .. 8
-// inside the lane, then 16 .. D/2 across lanes (sg[k] = +1 / -1 for the
-// lower / upper lane of lane distance 2^k).
+// FWHT of a row held as two 8-element halves per lane over LPR lanes (sg[k]
+// = +1 / -1 for the lower / upper lane of lane distance 2^k).
 template <int LPR>
 __device__ __forceinline__ void fwht_row(float x[16], const float sg[3]) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if ((j & h) == 0) {
@@ -68,11 +68,17 @@ __device__ __forceinline__ void fwht_row(float x[16], const float sg[3]) {
     if constexpr (LPR >= 4) x[j] = butterfly16<2>(x[j], sg[1]);
     if constexpr (LPR >= 8) x[j] = butterfly16<4>(x[j], sg[2]);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float a = x[j], b = x[j + 8];
+    x[j] = a + b;
+    x[j + 8] = a - b;
+  }
 }
 
-// Quantize one rotated row (16 elements per lane) and store the lane's 8
-// packed bytes and the scale word.
-template <int LPR>
+// Quantize one rotated row (two 8-element halves per lane) and store the
+// lane's two packed words and the scale word.
+template <int D, int LPR>
 __device__ __forceinline__ void quantize_store(const float x[16], int li, bool valid,
                                                uint8_t* __restrict__ cache_row,
                                                float* __restrict__ word_out) {
@@ -99,8 +105,16 @@ __device__ __forceinline__ void quantize_store(const float x[16], int li, bool v
     const uint32_t q = (uint32_t)__builtin_amdgcn_fmed3f(t + 0.5f, 0.0f, 15.0f);
     packed[j >> 3] |= q << (4 * (j & 7));
   }
+  // Lanes 2m and 2m+1 hold bytes 8m..8m+7 of the first half as packed[0]
+  // and of the second half as packed[1]; swapping one word gives lane 2m
+  // the first-half 8 bytes and lane 2m+1 the second-half 8 bytes, stored
+  // with one 8-byte store each.
+  const bool odd = li & 1;
+  const uint32_t give = odd ? packed[0] : packed[1];
+  const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
+  const uint2 out = odd ? make_uint2(got, packed[1]) : make_uint2(packed[0], got);
   if (valid) {
-    *reinterpret_cast<uint2*>(cache_row + 8 * li) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2*>(cache_row + (odd ? D / 4 : 0) + 8 * (li >> 1)) = out;
     if (li == 0) *word_out = u2f((f2u(scale) & 0xFFFFFFF0u) | (uint32_t)zp);
   }
 }
@@ -121,8 +135,12 @@ __global__ __launch_bounds__(256) void reshape_int4_kernel(
 #pragma unroll
   for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
 
+  // The source rows are loaded without waiting for their slots (a skipped
+  // row's values are read and discarded), so both loads are in flight
+  // together.
   float x[R][16];
-  int64_t dst[R];
+  int64_t slot[R], dst[R];
+  int head[R];
   bool valid[R], is_v[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -130,26 +148,27 @@ __global__ __launch_bounds__(256) void reshape_int4_kernel(
     const bool in_range = row < total_rows;
     const int64_t item = in_range ? (row >> 1) : 0;
     is_v[r] = row & 1;
-    const int64_t t = item / hk;
-    const int h = (int)(item - t * hk);
-    const int64_t slot = in_range ? slots[t] : -1;
-    valid[r] = in_range && slot >= 0 && slot < cache_slots;
-    dst[r] = (valid[r] ? slot : 0) * hk + h;
-    if (valid[r]) {
-      load16<DT>(is_v[r] ? value : key, item * D + li * 16, x[r]);
-    } else {
+    // token and head of the item (32-bit division: items < 2^31)
+    const uint32_t it32 = (uint32_t)item;
+    const int64_t t = (int64_t)(it32 / (uint32_t)hk);
+    head[r] = (int)(it32 - (uint32_t)t * (uint32_t)hk);
+    slot[r] = in_range ? slots[t] : -1;
+    const void* src = is_v[r] ? value : key;
+    load8<DT>(src, item * D + li * 8, x[r]);
+    load8<DT>(src, item * D + D / 2 + li * 8, x[r] + 8);
+  }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) x[r][j] = 0.0f;
-    }
+  for (int r = 0; r < R; ++r) {
+    valid[r] = slot[r] >= 0 && slot[r] < cache_slots;
+    dst[r] = (valid[r] ? slot[r] : 0) * hk + head[r];
   }
   float s[16];
-  {
-    const float4* sp = reinterpret_cast<const float4*>(signs + li * 16);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 a = sp[k];
-      s[4 * k] = a.x; s[4 * k + 1] = a.y; s[4 * k + 2] = a.z; s[4 * k + 3] = a.w;
-    }
+  for (int hf = 0; hf < 2; ++hf) {
+    const float4* sp = reinterpret_cast<const float4*>(signs + hf * (D / 2) + li * 8);
+    const float4 a = sp[0], b = sp[1];
+    s[8 * hf + 0] = a.x; s[8 * hf + 1] = a.y; s[8 * hf + 2] = a.z; s[8 * hf + 3] = a.w;
+    s[8 * hf + 4] = b.x; s[8 * hf + 5] = b.y; s[8 * hf + 6] = b.z; s[8 * hf + 7] = b.w;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -163,7 +182,7 @@ __global__ __launch_bounds__(256) void reshape_int4_kernel(
     }
     uint8_t* cache = is_v[r] ? vc : kc;
     float* words = is_v[r] ? vs : ks;
-    quantize_store<LPR>(x[r], li, valid[r], cache + dst[r] * (D / 2), words + dst[r]);
+    quantize_store<D, LPR>(x[r], li, valid[r], cache + dst[r] * (D / 2), words + dst[r]);
   }
 }
 
