@@ -17,17 +17,20 @@ namespace tqk {
 
 namespace {
 
-template <int D, bool ROTATE>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  constexpr int CH = 16;  // partials whose loads are in flight together
+template <int D, bool ROTATE, int PG>
+__global__ __launch_bounds__(D * PG) void merge_kernel(DecodeParams p) {
+  constexpr int NT = D * PG;  // PG groups of D threads share the partials
+  constexpr int CH = 16;      // partial rows whose loads are in flight together
   constexpr int kMaxParts = kWaveBudget + 256;  // nw + S bounds the list
-  __shared__ float sh[D];
   __shared__ uint32_t rows[kMaxParts];  // partial rows of ws, in merge order
-  __shared__ int cnt_scan[D];
+  __shared__ int wave_tot[NT / 64];
+  __shared__ float acc_l[PG][D];
+  __shared__ float st_l[PG][2];  // running (max, weight sum) per group
   const int bh = blockIdx.x;
   const int b = bh / p.hq;
   const int h = bh - b * p.hq;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const SeqSplits q = seq_splits(p, b);
   const int nsplit = q.n;  // non-empty splits are a prefix: s * split_len < seq
 
@@ -35,25 +38,26 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   int nparts;
   if (p.nw == 0) {
     // one partial per non-empty split: rows (b, h, s)
-    for (int s = d; s < nsplit; s += D) rows[s] = (uint32_t)((int64_t)bh * p.splits + s);
+    for (int s = tid; s < nsplit; s += NT) rows[s] = (uint32_t)((int64_t)bh * p.splits + s);
     nparts = nsplit;
   } else {
-    // balanced layout: the tile list position of this sequence and the
+    // balanced layout: the tile-list position of this sequence and the
     // total, as stage 1 computed them
     const int Pb = p.wsx[b], N = p.wsx[p.B];
     const int kvh = h / p.g;
     const int grp = kvh / p.wgh;
     const int hw = h - grp * p.wgh * p.g;  // head index within its workgroup
     const int64_t whole_rows = (int64_t)p.B * p.hq * p.splits;
-    // entries of the splits d, d + D, ... (S <= 256)
-    constexpr int SPT = (256 + D - 1) / D;
+    // entries of the splits tid, tid + NT, ... (S <= 256)
+    constexpr int SPT = (256 + NT - 1) / NT;
     int cnt[SPT], wa[SPT], ea[SPT], A_[SPT];
+    int mine = 0;
     for (int i = 0; i < SPT; ++i) {
       cnt[i] = 0;
       wa[i] = 0;
       ea[i] = 0;
       A_[i] = 0;
-      const int s = d + i * D;
+      const int s = tid + i * NT;
       if (s < nsplit) {
         const int A = Pb + s * q.TL;
         const int nt = (s == nsplit - 1) ? q.TLast : q.TL;
@@ -68,24 +72,29 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
         wa[i] = a;
         ea[i] = e;
         A_[i] = A;
+        mine += c;
       }
     }
-    // exclusive scan of per-thread counts
-    int mine = 0;
-    for (int i = 0; i < SPT; ++i) mine += cnt[i];
-    cnt_scan[d] = mine;
-    __syncthreads();
-    for (int off = 1; off < D; off <<= 1) {
-      const int v = d >= off ? cnt_scan[d - off] : 0;
-      __syncthreads();
-      cnt_scan[d] += v;
-      __syncthreads();
+    // exclusive scan of the per-thread counts: across the wave, then waves
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off);
+      if (lane >= off) incl += u;
     }
-    nparts = cnt_scan[D - 1] < kMaxParts ? cnt_scan[D - 1] : kMaxParts;
-    int pos = d ? cnt_scan[d - 1] : 0;
-    // thread d lists the partials of splits d, d + D, ... (any merge order)
+    if (lane == 63) wave_tot[tid >> 6] = incl;
+    __syncthreads();
+    int total = 0, before = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      total += wave_tot[w2];
+      before += w2 < (tid >> 6) ? wave_tot[w2] : 0;
+    }
+    nparts = total < kMaxParts ? total : kMaxParts;
+    int pos = before + incl - mine;
+    // thread tid lists the partials of splits tid, tid + NT, ... (any order)
     for (int i = 0; i < SPT; ++i) {
-      const int s = d + i * D;
+      const int s = tid + i * NT;
       if (s >= nsplit) continue;
       if (cnt[i] == 1) {
         if (pos < kMaxParts) rows[pos] = (uint32_t)((int64_t)bh * p.splits + s);
@@ -104,13 +113,15 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // running log-sum-exp over chunks of partials (natural-log lse)
-  float mx = -INFINITY, wsum = 0.0f, o = 0.0f;
-  for (int s0 = 0; s0 < nparts; s0 += CH) {
+  // ---- running log-sum-exp per group: group pg takes partials pg, pg+PG,
+  // ..., CH of them in flight at a time (lse and value together) ----
+  const int d = tid % D, pg = tid / D;
+  float mx = -INFINITY, ws = 0.0f, acc = 0.0f;
+  for (int s0 = pg; s0 < nparts; s0 += CH * PG) {
     float ls[CH], pv[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int s = s0 + j;
+      const int s = s0 + j * PG;
       const bool ok = s < nparts;
       const float* part = p.ws + (int64_t)rows[ok ? s : 0] * (D + 1);
       ls[j] = ok ? part[D] : -INFINITY;
@@ -122,31 +133,60 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
     const float nm = fmaxf(mx, cm);
     if (nm == -INFINITY) continue;
     const float sc = __expf(mx - nm);
-    wsum *= sc;
-    o *= sc;
+    ws *= sc;
+    acc *= sc;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const float w = __expf(ls[j] - nm);
-      wsum += w;
-      o += w * pv[j];
+      ws += w;
+      acc += w * pv[j];
     }
     mx = nm;
   }
-  if (mx != -INFINITY) o /= wsum;
-  if constexpr (ROTATE) {
-    sh[d] = o;
-    __syncthreads();
-#pragma unroll
-    for (int h = 1; h < D; h <<= 1) {
-      const float a = sh[d], c = sh[d ^ h];
-      __syncthreads();
-      sh[d] = (d & h) ? (c - a) : (a + c);
-      __syncthreads();
-    }
-    o = sh[d] * p.rht_signs[d] * (1.0f / (float)D);
+  acc_l[pg][d] = acc;
+  if (d == 0) {
+    st_l[pg][0] = mx;
+    st_l[pg][1] = ws;
   }
-  p.out[(int64_t)bh * D + d] = o;
-  if (p.lse && d == 0) p.lse[bh] = (mx == -INFINITY) ? -INFINITY : mx + __logf(wsum);
+  __syncthreads();
+  // combine the groups' states
+  float M = -INFINITY;
+#pragma unroll
+  for (int g2 = 0; g2 < PG; ++g2) M = fmaxf(M, st_l[g2][0]);
+  float wsum = 0.0f, o = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int g2 = 0; g2 < PG; ++g2) {
+      const float a = __expf(st_l[g2][0] - M);  // 0 for an empty group
+      wsum += st_l[g2][1] * a;
+      o += acc_l[g2][d] * a;
+    }
+  }
+  // the first group (threads < D) stores the row; the others only take
+  // part in the barriers below
+  if (wsum > 0.0f) o /= wsum;
+  if constexpr (ROTATE) {
+    // inverse RHT: FWHT over D (strides 1 .. 32 inside the wave, 64 through
+    // LDS), then signs and 1/D
+    o = butterfly_lanes<1>(o, d & 1);
+    o = butterfly_lanes<2>(o, d & 2);
+    o = butterfly_lanes<4>(o, d & 4);
+    o = butterfly_lanes<8>(o, d & 8);
+    o = butterfly_lanes<16>(o, d & 16);
+    o = butterfly_lanes<32>(o, d & 32);
+    if constexpr (D == 128) {
+      __syncthreads();  // every group has read acc_l
+      if (tid < D) acc_l[0][d] = o;
+      __syncthreads();
+      const float pr = acc_l[0][d ^ 64];
+      o = (d & 64) ? (pr - o) : (o + pr);
+    }
+    o = o * p.rht_signs[d] * (1.0f / (float)D);
+  }
+  if (tid < D) {
+    p.out[(int64_t)bh * D + d] = o;
+    if (p.lse && d == 0) p.lse[bh] = (wsum > 0.0f) ? M + __logf(wsum) : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -154,13 +194,24 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
 hipError_t launch_merge(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)p.B * p.hq;
   const bool rot = p.key_fmt == KF_INT4;
+  // more thread groups per row when there are few rows to fill the chip
+  const int pg = blocks >= 2048 ? 1 : (blocks >= 512 ? 2 : 4);
+#define TQ_MERGE(DD, RR, PP) \
+  hipLaunchKernelGGL((merge_kernel<DD, RR, PP>), dim3(blocks), dim3(DD * PP), 0, st, p)
   if (p.d == 128) {
-    if (rot) hipLaunchKernelGGL((merge_kernel<128, true>), dim3(blocks), dim3(128), 0, st, p);
-    else hipLaunchKernelGGL((merge_kernel<128, false>), dim3(blocks), dim3(128), 0, st, p);
+    if (rot) {
+      if (pg == 1) TQ_MERGE(128, true, 1); else if (pg == 2) TQ_MERGE(128, true, 2); else TQ_MERGE(128, true, 4);
+    } else {
+      if (pg == 1) TQ_MERGE(128, false, 1); else if (pg == 2) TQ_MERGE(128, false, 2); else TQ_MERGE(128, false, 4);
+    }
   } else {
-    if (rot) hipLaunchKernelGGL((merge_kernel<64, true>), dim3(blocks), dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((merge_kernel<64, false>), dim3(blocks), dim3(64), 0, st, p);
+    if (rot) {
+      if (pg == 1) TQ_MERGE(64, true, 1); else if (pg == 2) TQ_MERGE(64, true, 2); else TQ_MERGE(64, true, 4);
+    } else {
+      if (pg == 1) TQ_MERGE(64, false, 1); else if (pg == 2) TQ_MERGE(64, false, 2); else TQ_MERGE(64, false, 4);
+    }
   }
+#undef TQ_MERGE
   return hipGetLastError();
 }
 
