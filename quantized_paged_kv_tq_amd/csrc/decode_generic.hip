@@ -12,6 +12,10 @@
 // softmax state (running max m, sum l, accumulator) per head, and the groups
 // are merged by log-sum-exp at the end. Scores are kept in base-2 units
 // (log2(e) folded into the query), so p = exp2(s - m).
+//
+// Latency: the split's block-table slice is staged in LDS, and each lane
+// group issues the raw loads of U tokens (aligned dwords; sub-dword fields
+// are cut out with byte-align shifts) before decoding any of them.
 #include <type_traits>
 
 #include "tq_device.h"
@@ -24,26 +28,16 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int N>
-__device__ __forceinline__ uint32_t load_bytes_le(const uint8_t* p) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < N; ++k) w |= (uint32_t)p[k] << (8 * k);
-  return w;
-}
+constexpr int kMaxSplitPages = 2048;  // block-table entries of a split staged in LDS
 
-__device__ __forceinline__ float load_half_le(const uint8_t* p) {
-  const uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
-  return half_lo(w);
-}
-
-template <int D, int KF, int VF, int G>
+template <int D, int KF, int VF, int G, int U>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
   constexpr int LPT = D / 8;          // lanes per token
   constexpr int TPW = 64 / LPT;       // tokens per wave step
   constexpr int NG = 4 * TPW;         // token groups per workgroup
   __shared__ float qs[G][D];
   __shared__ float cen[16];
+  __shared__ int pages[kMaxSplitPages];
   __shared__ float red[4][G][D + 2];
 
   const int nchunk = (p.g + G - 1) / G;
@@ -82,6 +76,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
   }
   if constexpr (KF == KF_MSE3 || KF == KF_MSE4) {
     if (tid < 16) cen[tid] = tid < (KF == KF_MSE3 ? 8 : 16) ? p.centroids[tid] : 0.0f;
+  }
+  {
+    // this split's block-table slice (pages of tokens t0 .. t1 - 1)
+    const int64_t first = t0 / p.block_size;
+    const int64_t count = (t1 - 1) / p.block_size - first + 1;
+    if (count <= kMaxSplitPages) {
+      const int32_t* row = p.block_table + (int64_t)b * p.max_blocks + first;
+      for (int i = tid; i < count; i += 256) pages[i] = row[i];
+    }
   }
   __syncthreads();
   if constexpr (KF != KF_FP8) {
@@ -123,44 +126,80 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
   constexpr int KB = (KF == KF_MSE3) ? 3 : 4;  // centroid index bits
   constexpr int VB = (VF == VF_U3) ? 3 : 4;
   const int mse_bytes = (D * KB + 7) / 8;
+  const int bs = p.block_size;
+  const int64_t pg0 = t0 / bs;
+  const int npg = (int)((t1 - 1) / bs - pg0 + 1);
+  const bool staged = npg <= kMaxSplitPages;
 
-  for (int64_t t = t0 + grp; t < t1; t += NG) {
-    const int64_t page = bt[t / p.block_size];
-    if (page < 0 || page >= p.num_blocks) continue;
-    const int64_t row = (page * p.block_size + t % p.block_size) * p.hk + kvh;
+  // raw words of one token for this lane (masked tokens: ok = false)
+  struct Raw {
+    uint32_t w[7];
+    bool ok;
+  };
+  auto load_raw = [&](int64_t t) {
+    Raw r;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) r.w[i] = 0;
+    r.ok = false;
+    if (t >= t1) return r;
+    const int64_t page = staged ? (int64_t)pages[t / bs - pg0] : (int64_t)bt[t / bs];
+    if (page < 0 || page >= p.num_blocks) return r;
+    r.ok = true;
+    const int64_t row = (page * bs + t % bs) * p.hk + kvh;
+    if constexpr (KF == KF_INT4) {
+      r.w[0] = *reinterpret_cast<const uint32_t*>(p.kc + row * (D / 2) + li * 4);
+      r.w[1] = f2u(p.ks[row]);
+      r.w[2] = *reinterpret_cast<const uint32_t*>(p.vc + row * (D / 2) + li * 4);
+      r.w[3] = f2u(p.vs[row]);
+    } else {
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(p.kv + row * p.slot_bytes);
+      if constexpr (KF == KF_FP8) {
+        r.w[0] = s32[2 * li];
+        r.w[1] = s32[2 * li + 1];
+      } else {
+        const int kb = li * KB;  // first key byte of this lane
+        r.w[0] = s32[kb >> 2];
+        r.w[1] = s32[(kb >> 2) + 1];
+        r.w[2] = s32[mse_bytes >> 2];  // fp16 norm in the low half (mse_bytes % 4 == 0)
+      }
+      const int vbyte = p.kps + li * VB;
+      r.w[3] = s32[vbyte >> 2];
+      r.w[4] = s32[(vbyte >> 2) + 1];
+      const int sbyte = p.kps + p.vdb;
+      r.w[5] = s32[sbyte >> 2];
+      r.w[6] = s32[(sbyte >> 2) + 1];
+    }
+    return r;
+  };
 
-    // ---- key: decode 8 dims and score against every head ----
+  // decode one token's raw words and fold it into the online softmax
+  auto consume = [&](const Raw& r) {
+    if (!r.ok) return;
     float kd[8];
     float kscale;
-    const uint8_t* slot = nullptr;
     if constexpr (KF == KF_INT4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.kc + row * (D / 2) + li * 4);
-      const uint32_t sw = f2u(p.ks[row]);
+      const uint32_t w = r.w[0], sw = r.w[1];
       const float zp = (float)(sw & 0xFu);
       kscale = u2f(sw & 0xFFFFFFF0u);
 #pragma unroll
       for (int j = 0; j < 8; ++j) kd[j] = (float)((w >> (4 * j)) & 0xFu) - zp;
-    } else {
-      slot = p.kv + row * p.slot_bytes;
-      if constexpr (KF == KF_FP8) {
-        const uint2 w = *reinterpret_cast<const uint2*>(slot + li * 8);
+    } else if constexpr (KF == KF_FP8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kd[j] = e4m3_to_f32((w.x >> (8 * j)) & 0xFFu);
-          kd[j + 4] = e4m3_to_f32((w.y >> (8 * j)) & 0xFFu);
-        }
-        kscale = 1.0f;
-      } else {
-        const uint32_t w = load_bytes_le<KB>(slot + li * KB);
-        float cs = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kd[j] = cen[(w >> (KB * j)) & ((1u << KB) - 1u)];
-          cs += kd[j] * kd[j];
-        }
-        kscale = load_half_le(slot + mse_bytes);
-        if (p.norm_correction) kscale *= 1.0f / sqrtf(group_sum<LPT>(cs) + 1e-16f);
+      for (int j = 0; j < 4; ++j) {
+        kd[j] = e4m3_to_f32((r.w[0] >> (8 * j)) & 0xFFu);
+        kd[j + 4] = e4m3_to_f32((r.w[1] >> (8 * j)) & 0xFFu);
       }
+      kscale = 1.0f;
+    } else {
+      const uint32_t w = __builtin_amdgcn_alignbyte(r.w[1], r.w[0], (li * KB) & 3);
+      float cs = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kd[j] = cen[(w >> (KB * j)) & ((1u << KB) - 1u)];
+        cs += kd[j] * kd[j];
+      }
+      kscale = half_lo(r.w[2]);
+      if (p.norm_correction) kscale *= 1.0f / sqrtf(group_sum<LPT>(cs) + 1e-16f);
     }
     float sc[G];
 #pragma unroll
@@ -171,26 +210,23 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
       sc[hh] = group_sum<LPT>(part) * kscale;
     }
 
-    // ---- value: decode 8 dims ----
     float vd[8];
     if constexpr (VF == VF_INT4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.vc + row * (D / 2) + li * 4);
-      const uint32_t sw = f2u(p.vs[row]);
+      const uint32_t w = r.w[2], sw = r.w[3];
       const float zp = (float)(sw & 0xFu);
       const float vsc = u2f(sw & 0xFFFFFFF0u);
 #pragma unroll
       for (int j = 0; j < 8; ++j) vd[j] = ((float)((w >> (4 * j)) & 0xFu) - zp) * vsc;
     } else {
-      const uint8_t* vbase = slot + p.kps;
-      const uint32_t w = load_bytes_le<VB>(vbase + li * VB);
-      const float vsc = load_half_le(vbase + p.vdb);
-      const float vz = load_half_le(vbase + p.vdb + 2);
+      const uint32_t w = __builtin_amdgcn_alignbyte(r.w[4], r.w[3], (p.kps + li * VB) & 3);
+      const uint32_t sz = __builtin_amdgcn_alignbyte(r.w[6], r.w[5], (p.kps + p.vdb) & 3);
+      const float vsc = half_lo(sz);
+      const float vz = half_hi(sz);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         vd[j] = (float)((w >> (VB * j)) & ((1u << VB) - 1u)) * vsc + vz;
     }
 
-    // ---- online softmax + accumulate ----
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const float mn = fmaxf(m[hh], sc[hh]);
@@ -201,6 +237,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
       for (int j = 0; j < 8; ++j) acc[hh][j] = acc[hh][j] * alpha + pr * vd[j];
       m[hh] = mn;
     }
+  };
+
+  // U tokens per lane group: every raw load is issued before any decode
+  for (int64_t tb = t0 + grp; tb < t1; tb += (int64_t)U * NG) {
+    Raw r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = load_raw(tb + (int64_t)u * NG);
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume(r[u]);
   }
 
   // ---- merge the lane groups of this wave (log-sum-exp) ----
@@ -262,10 +307,10 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t st) {
   const int chunks = (p.g + G - 1) / G;
   const uint32_t blocks = (uint32_t)p.B * p.hk * chunks * p.splits;
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 1>), dim3(blocks), dim3(256), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 2>), dim3(blocks), dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 4>), dim3(blocks), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 8>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 1: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 1, 4>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 2, 4>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 4, 4>), dim3(blocks), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_generic_kernel<D, KF, VF, 8, 4>), dim3(blocks), dim3(256), 0, st, p); break;
   }
   return hipGetLastError();
 }
