@@ -192,7 +192,10 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipErrorNotSupported;
-  if (int4 && !(a->flags & TQ_FLAG_GENERIC)) e = tqk::launch_decode_int4_mfma(p, st);
+  if (!(a->flags & TQ_FLAG_GENERIC)) {
+    if (int4) e = tqk::launch_decode_int4_mfma(p, st);
+    else e = tqk::launch_decode_tq_mfma(p, st);
+  }
   if (e == hipErrorNotSupported) e = tqk::launch_decode_generic(p, st);
   if (e != hipSuccess) return launched(e, "tq_decode_attention stage 1");
   return launched(tqk::launch_merge(p, st), "tq_decode_attention stage 2");

@@ -1,0 +1,518 @@
+// TurboQuant split-KV decode, stage 1, on the CDNA4 matrix cores, for FP8
+// E4M3 keys with 4-bit uniform values (triton_turboquant_decode.py,
+// _tq_decode_stage1: score = sm_scale * q . e4m3(k); v = idx * scale16 +
+// zero16; online softmax; partials acc / l and m + ln l).
+//
+// Scores. The keys are converted to bf16 exactly (every E4M3 value is a
+// bf16 value) with v_cvt_scalef32_pk_bf16_fp8. The fp32 query is split into
+// three bf16 parts q = hi + mid + lo (exact to 2^-24 relative), and one
+// v_mfma_f32_16x16x32_bf16 per 32 dimensions takes A rows 4h + p = part p of
+// head h: the lane (n, g) of the 16x16 result then holds the three partial
+// products of head g and token n, which it adds in fp32.
+//
+// Values. As in the INT4 path: P' = p * scale16 (p <= 2^kTau relative to a
+// reference maximum) is scaled per tile by a power of two below 2^27 and
+// split into four 7-bit digit planes (the A operand of
+// v_mfma_i32_16x16x64_i8), the 4-bit indices are the B operand as stored,
+// and the int32 sums are exact. The zero term sum_t p_t * zero16_t is a
+// per-head fp32 sum added to every dimension at the end.
+//
+// Work decomposition, tile table, pieces and ping-pong register sets follow
+// the INT4 path (balance.h): equal ranges of the global 64-token tile list,
+// one wave per four query heads of a kv head.
+#include "balance.h"
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqk {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kChunk = 64;  // tiles resolved into LDS at a time
+constexpr int kTau = 4;     // headroom of the value-weight fixed point
+constexpr uint32_t kMasked = 0xFFFFFFFFu;
+constexpr uint32_t kMaskedByte = 0xFFFFFF00u;  // byte offset past any buffer
+constexpr int kFirstOfSplit = 1;
+constexpr int kLastOfSplit = 2;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += xor_lane<2>(v);
+  v += xor_lane<1>(v);
+  return v;
+}
+__device__ __forceinline__ float exp2i(int e) { return u2f((uint32_t)(e + 127) << 23); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// fp32 -> bf16 bits (round to nearest even; finite values)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_tq_fp8_kernel(DecodeParams p) {
+  constexpr int NT = 64 * W;
+  __shared__ __attribute__((aligned(16))) uint32_t p8[W][4][4][16];  // weight digit planes
+  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
+  __shared__ int4 tinfo[kChunk];
+  __shared__ int scan[W];
+  __shared__ float accl[W][8][64];  // fp32 value accumulators, lane-major
+  extern __shared__ int prefix[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int grp = blockIdx.x / p.nw;
+  const int wg = blockIdx.x - grp * p.nw;
+  const int qs_n = (p.g + 3) >> 2;
+  const int kvl = wave / qs_n;
+  const int qsub = wave - kvl * qs_n;
+  const int kvh = grp * p.wgh + kvl;
+  const int g = p.g;
+  const int hq0 = 4 * qsub;
+  const int gw = g - hq0 < 4 ? g - hq0 : 4;
+  const int h0 = kvh * g + hq0;
+
+  // ---- tile counts of all sequences and their prefix sums ----
+  const int per = (p.B + NT - 1) / NT;
+  int run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      run += seq_tiles(seq_splits(p, b));
+      prefix[b + 1] = run;
+    }
+  }
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int N = 0, before = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < W; ++w2) {
+    const int t = scan[w2];
+    N += t;
+    before += w2 < wave ? t : 0;
+  }
+  {
+    const int excl = before + incl - run;
+    for (int i = 0; i < per; ++i) {
+      const int b = tid * per + i;
+      if (b < p.B) {
+        prefix[b + 1] += excl;
+        if (blockIdx.x == 0) p.wsx[b + 1] = prefix[b + 1];
+      }
+    }
+    if (tid == 0) {
+      prefix[0] = 0;
+      if (blockIdx.x == 0) p.wsx[0] = 0;
+    }
+  }
+  __syncthreads();
+  if (N == 0) return;
+  const int lo = range_lo(wg, N, p.nw), hi = range_lo(wg + 1, N, p.nw);
+  if (lo >= hi) return;
+
+  const uint32_t bs = (uint32_t)p.block_size;
+  const bool bs_pow2 = (bs & (bs - 1u)) == 0u;
+  const int bs_shift = __builtin_ctz(bs);
+  const uint32_t sb = (uint32_t)p.slot_bytes;
+  const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, nrows * sb);
+  const uint32_t voff = (uint32_t)p.kps;            // value indices
+  const uint32_t soff = (uint32_t)(p.kps + p.vdb);  // fp16 scale, fp16 zero
+
+  // ---- registers of one tile ----
+  // key bytes [32g, 32g + 32) of tokens 16s + n; value dword n of tokens
+  // 16s + 4g + k; the scale/zero word of token `lane`
+  struct Buf {
+    v4u kraw[4][2];
+    uint32_t sz, live;
+    uint32_t vraw[4][4];
+  };
+  auto slot_of = [&](int k, int j) -> uint32_t {
+    const uint32_t r = tok_rows[k][j];
+    return r == kMasked ? kMaskedByte : (r + (uint32_t)kvh) * sb;
+  };
+  auto issue = [&](Buf& B, int k) {
+    B.live = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t o = slot_of(k, 16 * s + ln);
+      B.live |= (o != kMaskedByte ? 1u : 0u) << s;
+      B.kraw[s][0] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg), 0, 0);
+      B.kraw[s][1] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg + 16u), 0, 0);
+    }
+    B.sz = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(slot_of(k, lane) + soff), 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
+        B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 4u * ln), 0, 0);
+      }
+    }
+  };
+
+  // ---- online softmax state of the current segment ----
+  float mref, l, zacc;  // per lane: head lg of this wave
+  float(*acc)[64] = accl[wave];
+  v4i cacc[8];
+  int ev = 0;
+  float sref = 0.0f;
+  bool empty = true;
+  int since_flush = 0;
+  auto reset = [&]() {
+    mref = -INFINITY;
+    l = 0.0f;
+    zacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i][lane] = 0.0f;
+      cacc[i] = v4i{0, 0, 0, 0};
+    }
+    ev = 0;
+    sref = 0.0f;
+    empty = true;
+    since_flush = 0;
+  };
+  // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
+  // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
+  auto flush = [&](float alpha) {
+    const float pinv = exp2i(-ev);
+    if (!empty) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e0 = (float)cacc[i].x, e1 = (float)cacc[i].y;
+        const float e2 = (float)cacc[i].z, e3 = (float)cacc[i].w;
+        const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+        acc[i][lane] = __builtin_fmaf(val, pinv, acc[i][lane]) * alpha;
+        cacc[i] = v4i{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][lane] *= alpha;
+    }
+    l *= alpha;
+    zacc *= alpha;
+    empty = true;
+  };
+
+  // ---------------- query of sequence b: three bf16 parts ----------------
+  // A operand of MFMA kb for lane (m = 4h + part, g): 8 bf16 of dims
+  // 32g + 8kb .. 32g + 8kb + 7 (part 3: zero)
+  v8bf16 qa[4];
+  float qf;
+  auto load_query = [&](int b) {
+    const int hq = ln >> 2, part = ln & 3;
+    const bool ok = hq < gw && part < 3;
+    const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
+      const float4 c = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        uint32_t pr[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float v = x[j + e];
+          const uint32_t bh = bf16_bits(v);
+          const float r1 = v - u2f(bh << 16);
+          const uint32_t bm = bf16_bits(r1);
+          const float r2 = r1 - u2f(bm << 16);
+          const uint32_t bl = bf16_bits(r2);
+          const uint32_t sel = part == 0 ? bh : (part == 1 ? bm : bl);
+          pr[e] = ok ? sel : 0u;
+        }
+        w[j >> 1] = pr[0] | (pr[1] << 16);
+      }
+      qa[kb] = __builtin_bit_cast(v8bf16, v4u{w[0], w[1], w[2], w[3]});
+    }
+    qf = p.sm_scale * kLog2e;
+  };
+
+  // ---------------- segment bookkeeping ----------------
+  int seg_b = -1, seg_s = 0;
+  bool seg_from_start = false, seg_to_end = false, seg_first = false;
+  auto emit = [&]() {
+    flush(1.0f);
+    const bool whole = seg_from_start && seg_to_end;
+    const float lt = row16_sum(l);
+    const float zt = row16_sum(zacc);
+    const int hh = lg;
+    if (hh < gw) {
+      float* out;
+      if (whole)
+        out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
+      else
+        out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
+                       kvl * g + hq0 + hh) * (D + 1);
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      float* dst = out + 8 * ln;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = (acc[i][lane] + zt) * inv;
+      if (ln == 0) out[D] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  };
+
+  // ---------------- one tile ----------------
+  auto process = [&](Buf& X, Buf& Y, int k, int c0) {
+    const int gk = c0 + k;
+    const int4 info = tinfo[k];
+    if (gk == lo || (info.z & kFirstOfSplit)) {
+      if (gk != lo) emit();
+      if (gk == lo || info.x != seg_b) load_query(info.x);
+      reset();
+      seg_b = info.x;
+      seg_s = info.y;
+      seg_from_start = (info.z & kFirstOfSplit) != 0;
+      seg_first = gk == lo;
+    }
+    seg_to_end = (info.z & kLastOfSplit) != 0;
+    issue(Y, k + 1);
+    // keep every use of X's registers after the next tile's loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    // scale/zero words of tokens 16s + n
+    uint32_t sz[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sz[s] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz);
+
+    // ---- scores: lane (n, g) gets head g, token 16s + n ----
+    float sc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        // key bytes 8kb .. 8kb + 7 of this lane's 32 -> 8 bf16
+        const v4u kw = X.kraw[s][kb >> 1];
+        const uint32_t w0 = kw[2 * (kb & 1)], w1 = kw[2 * (kb & 1) + 1];
+        const v2bf16 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const v2bf16 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const v2bf16 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const v2bf16 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        const v8bf16 kb8 = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], kb8, c, 0, 0, 0);
+      }
+      const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
+      sc[s] = fminf((c.x + c.y + c.z) * qf, mask);
+    }
+    float vsc[4], vz[4];
+    float smax = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      vsc[s] = half_lo(sz[s]);
+      vz[s] = half_hi(sz[s]);
+      smax = fmaxf(smax, fabsf(vsc[s]));
+    }
+
+    // ---- reference maximum / weight scale; flush when they move ----
+    const float tm = row16_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const bool move = tm > mref + (float)kTau;
+    smax = row16_max(smax);
+    const bool smove = smax >= sref || ++since_flush >= 8192;
+    if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
+      const float mn = fmaxf(mref, tm);
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
+      mref = mn;
+      flush(alpha);
+      since_flush = 0;
+      if (smax > 0.0f) {
+        const int e = (int)((f2u(smax) >> 23) & 0xFF) - 127;
+        ev = 26 - kTau - e;
+        sref = exp2i(e + 1);
+      }
+    }
+
+    // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
+    // The encoder's scale16 = (max - min) / levels is positive. A negative
+    // one (any bytes are accepted) takes signed digits: the digits of
+    // p * |scale16|, negated as int8, which the i8 MFMA sums exactly too.
+    const float pscale = exp2i(ev);
+    uint32_t dw[4] = {0, 0, 0, 0};
+    float ps = 0.0f, zs = 0.0f;
+    float pr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      pr[s] = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[s] - mref);
+      ps += pr[s];
+      zs = __builtin_fmaf(pr[s], vz[s], zs);
+    }
+    const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
+                                                     vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
+    if (!any_neg) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
+        const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
+          dw[kk] |= (d & 255u) << (8 * s);
+        }
+      }
+    }
+    l += ps;
+    zacc += zs;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) p8[wave][lg][kk][ln] = dw[kk];
+    empty = false;
+    wave_sync();
+
+    // ---- value MFMAs: B operands by nibble transpose, in two halves ----
+    const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][ln >> 2][ln & 3][4 * lg]);
+    const v4i pa = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t vb[4][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t w0 = X.vraw[0][kk], w1 = X.vraw[1][kk], w2 = X.vraw[2][kk], w3 = X.vraw[3][kk];
+        const uint32_t sel = h ? 0x07030602u : 0x05010400u;
+        const uint32_t x01 = __builtin_amdgcn_perm(w1, w0, sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(w3, w2, sel);
+        const uint32_t ta = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+        const uint32_t tb = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+        vb[0][kk] = ta & 0x0F0F0F0Fu;
+        vb[1][kk] = (ta >> 4) & 0x0F0F0F0Fu;
+        vb[2][kk] = tb & 0x0F0F0F0Fu;
+        vb[3][kk] = (tb >> 4) & 0x0F0F0F0Fu;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
+        cacc[4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, cacc[4 * h + i], 0, 0, 0);
+      }
+    }
+    wave_sync();
+  };
+
+  Buf A, Bb;
+  for (int c0 = lo; c0 < hi; c0 += kChunk) {
+    const int K = hi - c0 < kChunk ? hi - c0 : kChunk;
+    __syncthreads();
+    for (int e = tid; e < (K + 1) * 64; e += NT) {
+      const int k = e >> 6, j = e & 63;
+      if (k == K) {
+        tok_rows[k][j] = kMasked;
+        continue;
+      }
+      const int x = c0 + k;
+      int bl = 0, bh = p.B - 1;
+      while (bl < bh) {
+        const int m = (bl + bh + 1) >> 1;
+        if (prefix[m] <= x) bl = m;
+        else bh = m - 1;
+      }
+      const int b = bl;
+      const SeqSplits q = seq_splits(p, b);
+      const int r = x - prefix[b];
+      int s = r / q.TL;
+      if (s > q.n - 1) s = q.n - 1;
+      const int t = r - s * q.TL;
+      const int tok0 = s * q.L + t * kTileTokens;
+      int end = s * q.L + q.L;
+      if (end > q.seq) end = q.seq;
+      if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
+      const int tok = tok0 + j;
+      uint32_t row = kMasked;
+      if (tok < end) {
+        const uint32_t t32 = (uint32_t)tok;
+        const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
+        const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
+        if (page >= 0 && page < p.num_blocks)
+          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
+      }
+      tok_rows[k][j] = row;
+      if (j == 0) {
+        const int nt = (s == q.n - 1) ? q.TLast : q.TL;
+        tinfo[k] = make_int4(b, s, (t == 0 ? kFirstOfSplit : 0) | (t == nt - 1 ? kLastOfSplit : 0), 0);
+      }
+    }
+    __syncthreads();
+    issue(A, 0);
+    for (int k = 0; k < K; k += 2) {
+      process(A, Bb, k, c0);
+      if (k + 1 >= K) break;
+      process(Bb, A, k + 1, c0);
+    }
+  }
+  emit();
+}
+
+template <int W>
+hipError_t launch(const DecodeParams& p, hipStream_t st) {
+  const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
+  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_tq_fp8_kernel<W>), dim3(blocks), dim3(64 * W), lds, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
+  if (p.d != D || p.key_fmt != KF_FP8 || p.val_fmt != VF_U4 || p.g > 8) return hipErrorNotSupported;
+  // slot bytes are addressed with 32-bit buffer offsets (masked: 0xFFFFFF00)
+  if (p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  if ((p.kps + p.vdb) % 4 != 0 || p.kps % 4 != 0 || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
+  const int64_t cap = (int64_t)p.max_blocks * p.block_size;
+  if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
+  const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
+  if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
+  const int qs = (p.g + 3) / 4;
+  p.wgh = balance_heads_per_wg(p.hk, p.g);
+  const int64_t nw = balance_max_wgs(p.hk, p.g);
+  p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+  switch (p.wgh * qs) {
+    case 1: return launch<1>(p, st);
+    case 2: return launch<2>(p, st);
+    case 4: return launch<4>(p, st);
+    default: return launch<8>(p, st);
+  }
+}
+
+}  // namespace tqk

@@ -67,6 +67,9 @@ hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t st);
 // shape is outside what it handles (the caller then uses the generic one).
 // Sets p.nw / p.wgh for stage 2.
 hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st);
+// FP8-key / 4-bit-value TurboQuant stage 1 on the matrix cores (D = 128,
+// g <= 8); hipErrorNotSupported otherwise. Sets p.nw / p.wgh for stage 2.
+hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st);
 // Stage 2: log-sum-exp merge of the split partials (+ inverse RHT for INT4).
 hipError_t launch_merge(const DecodeParams& p, hipStream_t st);
 

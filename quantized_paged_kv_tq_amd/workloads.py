@@ -208,6 +208,28 @@ def fwht_rows(rows=1048576, wid=6):
     return to_bits(x, "bf16")
 
 
+def random_tq_fp8_u4_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=8):
+    """Random FP8-key / 4-bit-value TurboQuant slots: key bytes uniform over
+    the finite E4M3 codes (0x7F / 0xFF, the NaN codes, are replaced by
+    0x7E / 0xFE), uniform value nibbles, fp16 scales of either sign with
+    magnitude in [2^-6, 2^0) and fp16 zeros in [-2, 2). For decode inputs
+    that do not depend on any writer."""
+    g = rng(w.wid, wid_tensor)
+    d = w.d
+    cache = np.zeros((w.num_blocks, w.block_size, w.hk, slot_bytes), np.uint8)
+    keys = g.integers(0, 256, size=cache.shape[:3] + (d,), dtype=np.uint8)
+    keys[(keys & 0x7F) == 0x7F] -= 1
+    cache[..., :d] = keys
+    cache[..., d:d + d // 2] = g.integers(0, 256, size=cache.shape[:3] + (d // 2,), dtype=np.uint8)
+    mag = np.exp2(g.uniform(-6, 0, size=cache.shape[:3]))
+    sign = np.where(g.random(size=cache.shape[:3]) < 0.25, -1.0, 1.0)
+    sc = (sign * mag).astype(np.float16)
+    zr = g.uniform(-2, 2, size=cache.shape[:3]).astype(np.float16)
+    cache[..., d + d // 2:d + d // 2 + 2] = sc[..., None].view(np.uint8).reshape(cache.shape[:3] + (2,))
+    cache[..., d + d // 2 + 2:d + d // 2 + 4] = zr[..., None].view(np.uint8).reshape(cache.shape[:3] + (2,))
+    return cache
+
+
 def random_int4_cache(w: DecodeWorkload, wid_tensor=7):
     """Uniformly random INT4 cache bytes plus valid scale words (positive
     normal scales in [2^-4, 2^2) with a random 4-bit zero-point in the low

@@ -86,10 +86,11 @@ def tq_case(w: W.DecodeWorkload, key_fmt, val_fmt, rot_signs=None):
 
 
 def gpu_tq_decode(w, q, cache, cen, key_fmt, val_fmt, rot_signs=None, norm_correction=False,
-                  num_splits=None):
+                  num_splits=None, flags=0, seq_lens=None):
     import quantized_paged_kv_tq_amd as tq
     out, lse = tq.tq_decode_attention(
-        to_dev(q), to_dev(w.block_table), to_dev(w.seq_lens),
+        to_dev(q), to_dev(w.block_table), to_dev(w.seq_lens if seq_lens is None else seq_lens),
+        flags=flags,
         num_kv_splits=w.num_splits if num_splits is None else num_splits,
         kv_cache=to_dev(cache), key_fmt=key_fmt, val_fmt=val_fmt,
         centroids=None if cen is None else to_dev(cen),

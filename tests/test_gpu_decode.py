@@ -196,3 +196,74 @@ def test_tq_full_size_sampled(fmt):
     ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, key_fmt,
                                     val_fmt, 0, w.num_splits, w.sm_scale, rows)
     assert_close(got[rows], ref, lse[rows], ref_lse, "tq_mixed %s" % (fmt,))
+
+
+def _oracle_tq(w, q, cache, cen, key_fmt, val_fmt, splits=None, rows=None, seq_lens=None):
+    return oracle.tq_decode(q, cache, w.block_table, w.seq_lens if seq_lens is None else seq_lens,
+                            cen, None, key_fmt, val_fmt, 0,
+                            w.num_splits if splits is None else splits, w.sm_scale, rows)
+
+
+A_FMT = (oracle.KEY_FP8, oracle.VAL_U4)
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_tq_fp8_u4_shapes(shape, flags):
+    """FP8 keys / 4-bit values on the matrix-core kernel (D = 128, up to
+    8 query heads per kv head) and on the generic one, same shapes as the
+    INT4 cases (the others fall back to the generic kernel)."""
+    B, hq, hk, d, bs, seq, S = shape
+    w = W.custom_decode_workload(200 + len(seq) * 7 + hq + d, B, hq, hk, d, bs, S, seq, 5, "bf16")
+    cache, cen = tq_case(w, *A_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *A_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *A_FMT, flags=flags)
+    assert_close(got, ref, lse, ref_lse, str(shape))
+
+
+def test_tq_fp8_u4_split_invariance_and_degenerate_lengths():
+    w = W.custom_decode_workload(240, 3, 8, 2, 128, 16, 4, [37, 1, 100], 2, "bf16")
+    cache, cen = tq_case(w, *A_FMT)
+    q = W.query(w, bf16_valued=True)
+    seq = np.array([37, 0, 100], np.int32)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *A_FMT, splits=0, seq_lens=seq)
+    for S in (1, 2, 8, 37, 64, 100, 105, 256):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *A_FMT, num_splits=S, seq_lens=seq)
+        assert_close(got, ref, lse, ref_lse, "S=%d" % S)
+        assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
+
+
+def test_tq_fp8_u4_random_slot_bytes():
+    """Random slots (no writer): every finite E4M3 key code, value scales of
+    both signs (negative ones take the signed-digit path), random zeros."""
+    w = W.custom_decode_workload(241, 2, 16, 4, 128, 16, 4, [300, 77], 4, "bf16")
+    cache = W.random_tq_fp8_u4_cache(w, oracle.tq_slot_bytes(128, *A_FMT))
+    q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
+    ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
+    for flags in (0, tq.FLAG_GENERIC):
+        got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "random slots flags=%d" % flags)
+
+
+def test_tq_fp8_u4_balanced_many_sequences():
+    """600 sequences (two per thread in the prefix sums), empty ones
+    interleaved, ranges over many sequence and split boundaries."""
+    rng = np.random.default_rng(242)
+    seq = rng.choice([0, 1, 5, 63, 64, 65, 130, 200, 777], size=600).astype(np.int32)
+    w = W.custom_decode_workload(242, 600, 8, 2, 128, 16, 3, seq, 7, "bf16")
+    cache = W.random_tq_fp8_u4_cache(w, oracle.tq_slot_bytes(128, *A_FMT))
+    q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
+    ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT)
+    assert_close(got, ref, lse, ref_lse, "600 sequences")
+
+
+@pytest.mark.parametrize("seq,S", [([1, 3], 2), ([64, 65, 1], 7), ([2000], 1), ([2000], 256)])
+def test_tq_fp8_u4_balanced_few_tiles(seq, S):
+    w = W.custom_decode_workload(243 + len(seq) + S, len(seq), 32, 8, 128, 16, S, seq, 3, "bf16")
+    cache, cen = tq_case(w, *A_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *A_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *A_FMT)
+    assert_close(got, ref, lse, ref_lse, "seq %s S=%d" % (seq, S))
