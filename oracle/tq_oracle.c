@@ -486,11 +486,25 @@ static void rotate_f64(const float* x, const float* rot_signs, int d, double* y)
 }
 
 /* Harness-side TurboQuant encoder (the pages show only the reader).
- * Keys: FP8 -> e4m3(clamp(k, +-448)); centroid -> norm = ||k||_2 (fp64,
- * stored fp16), u = Pi k / norm, index = nearest centroid (ties to the lower
- * index; norm 0 gives the centroid nearest 0). Values (b bits): scale =
+ * Keys: FP8 -> e4m3(clamp(k, +-448)); centroid -> norm = ||k||_2 stored
+ * fp16, u = Pi k / norm, index = nearest centroid (ties to the lower index;
+ * norm 0 gives the centroid nearest 0). Values (b bits): scale =
  * max((max-min)/(2^b-1), 1e-6) and zero = min, both stored fp16; index =
- * clamp(rint((v - zero16) / scale16), 0, 2^b-1) in fp32. */
+ * clamp(rint((v - zero16) / scale16), 0, 2^b-1).
+ * Everything is fp32, each operation rounded once, in this order:
+ *   ss   = sum of k_i^2, added pairwise with strides 1, 2, ..., d/2 (the
+ *          order of the butterflies; see tree_sum_f32);
+ *   norm = sqrt(ss) (correctly rounded);
+ *   y    = FWHT(k * rot_signs) (strides 1 -> d/2), u_i = (y_i * r) / norm
+ *          with r = the fp32 rounding of 1/sqrt(d);
+ *   index_i = argmin_j |u_i - c_j|.
+ * The pages fix none of these roundings; this order is the reading taken,
+ * so that an fp32 encoder can reproduce the bytes exactly. */
+static float tree_sum_f32(float* s, int d) {
+  for (int h = 1; h < d; h <<= 1)
+    for (int i = 0; i < d; i += 2 * h) s[i] = s[i] + s[i + h];
+  return s[0];
+}
 int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
                   int hk, int d, int key_fmt, int val_fmt,
                   const float* centroids, const float* rot_signs,
@@ -503,7 +517,6 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
   int kb = key_bits(key_fmt), vb = val_bits(val_fmt);
   int kps = key_region(d, key_fmt), vdb = val_data_bytes(d, val_fmt);
   int nc = 1 << kb;
-  double u[1024];
   for (int64_t t = 0; t < num_tokens; ++t) {
     int64_t slot = slot_mapping[t];
     if (slot < 0 || slot >= num_blocks * (int64_t)block_size) continue;
@@ -518,21 +531,23 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
           s[i] = orc_f32_to_e4m3(x);
         }
       } else {
-        double ss = 0.0;
-        for (int i = 0; i < d; ++i) ss += (double)k[i] * (double)k[i];
-        double nrm = sqrt(ss);
-        rotate_f64(k, rot_signs, d, u);
+        float sq[1024], y[1024];
+        for (int i = 0; i < d; ++i) sq[i] = k[i] * k[i];
+        const float nrm = sqrtf(tree_sum_f32(sq, d));
+        const float r = (float)(1.0 / sqrt((double)d));
+        for (int i = 0; i < d; ++i) y[i] = rot_signs ? k[i] * rot_signs[i] : k[i];
+        orc_fwht_f32(y, d);
         for (int i = 0; i < d; ++i) {
-          double ui = nrm > 0.0 ? u[i] / nrm : 0.0;
+          const float ui = nrm > 0.0f ? (y[i] * r) / nrm : 0.0f;
           int best = 0;
-          double bd = fabs(ui - (double)centroids[0]);
+          float bd = fabsf(ui - centroids[0]);
           for (int j = 1; j < nc; ++j) {
-            double dj = fabs(ui - (double)centroids[j]);
+            const float dj = fabsf(ui - centroids[j]);
             if (dj < bd) { bd = dj; best = j; }
           }
           put_bits(s, i, kb, (unsigned)best);
         }
-        uint16_t n16 = orc_f32_to_f16((float)nrm);
+        uint16_t n16 = orc_f32_to_f16(nrm);
         s[kps - 2] = (uint8_t)(n16 & 0xFF);
         s[kps - 1] = (uint8_t)(n16 >> 8);
       }

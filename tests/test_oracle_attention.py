@@ -241,3 +241,53 @@ def test_tq_encoder_round_trip_quality():
                     cos = rec @ k[t, h] / (np.linalg.norm(rec) * np.linalg.norm(k[t, h]))
                     assert cos > 0.95
                     assert abs(norm[p, o, h] - np.linalg.norm(k[t, h])) <= 1e-3 * np.linalg.norm(k[t, h])
+
+
+@pytest.mark.parametrize("key_fmt,bits", [(oracle.KEY_MSE3, 3), (oracle.KEY_MSE4, 4)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tq_centroid_encoder_fp32_agrees_with_fp64(key_fmt, bits, d):
+    """The fp32 centroid encoder picks the fp64 nearest centroid of
+    u = H diag(s) k / (sqrt(d) ||k||) wherever u is not within 1e-5 of a
+    decision boundary, and stores ||k|| rounded to fp16 (within one fp16 ulp
+    of the fp64 norm's rounding). Special rows: a zero key (norm 0, every
+    index the centroid nearest 0) and a one-hot key (u = +-1/sqrt(d))."""
+    rng = np.random.default_rng(50 + d + bits)
+    hk, T = 2, 300
+    k = rng.standard_normal((T, hk, d)).astype(np.float32)
+    k[:, :, :4] *= 10.0
+    k[5, 0] = 0.0
+    k[6, 1] = 0.0
+    k[6, 1, 3] = -2.5
+    v = rng.standard_normal((T, hk, d)).astype(np.float32)
+    cen = (oracle.lloyd_max_gaussian(1 << bits) / np.sqrt(d)).astype(np.float32)
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    mids = (cen[1:].astype(np.float64) + cen[:-1]) / 2
+    for rs in (None, W.rht_signs(d, round_idx=2)):
+        sb = oracle.tq_slot_bytes(d, key_fmt, oracle.VAL_U4)
+        cache = np.zeros((T, 1, hk, sb), np.uint8)
+        oracle.tq_encode(k, v, key_fmt, oracle.VAL_U4, cen, rs, np.arange(T, dtype=np.int64), cache)
+        mb = (d * bits + 7) // 8
+        got = np.unpackbits(cache[:, 0, :, :mb], axis=-1, bitorder="little")
+        got = (got.reshape(T, hk, d, bits) * (1 << np.arange(bits))).sum(-1)
+        n16 = cache[:, 0, :, mb:mb + 2].copy().view(np.float16)[..., 0]
+        k64 = k.astype(np.float64) * (1.0 if rs is None else rs.astype(np.float64))
+        nrm = np.linalg.norm(k.astype(np.float64), axis=-1)
+        u = (k64 @ H.T) / np.sqrt(d) / np.where(nrm > 0, nrm, 1.0)[..., None]
+        u[nrm == 0] = 0.0
+        ref = np.abs(u[..., None] - cen.astype(np.float64)).argmin(-1)
+        far = np.abs(u[..., None] - mids).min(-1) > 1e-5
+        far[5, 0] = far[6, 1] = False  # the special rows are checked below
+        assert far.mean() > 0.99
+        assert np.array_equal(got[far], ref[far])
+        assert np.array_equal(got[5, 0], np.full(d, np.abs(cen).argmin()))
+        assert n16[5, 0] == 0
+        # one-hot row: |u| = 1/sqrt(d) everywhere, sign = sign(k) * s_3 * H[:, 3]
+        s3 = 1.0 if rs is None else float(rs[3])
+        sign = -s3 * H[:, 3]
+        one = np.where(sign > 0, np.abs(cen - 1 / np.sqrt(d)).argmin(), np.abs(cen + 1 / np.sqrt(d)).argmin())
+        assert np.array_equal(got[6, 1], one)
+        assert float(n16[6, 1]) == 2.5
+        want16 = nrm.astype(np.float16)
+        ulp = np.spacing(np.abs(want16).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(n16.astype(np.float64) - want16.astype(np.float64)) <= ulp)
+        assert (n16 == want16).mean() > 0.99
