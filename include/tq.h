@@ -1,8 +1,10 @@
 /*
  * tq.h -- C ABI of the MI355X (gfx950) quantized paged-KV decode library.
  *
- * Three operations, each enqueued on the caller's HIP stream:
+ * Four operations, each enqueued on the caller's HIP stream:
  *   tq_reshape_and_cache_int4  randomized Hadamard rotation + INT4 cache write
+ *   tq_encode_and_cache        TurboQuant combined-slot cache write (FP8 or
+ *                              centroid keys, uniform 3/4-bit values)
  *   tq_decode_attention        split-KV decode attention over a paged,
  *                              sub-byte-quantized cache (stage 1 + stage 2)
  *   fwht128_quant_fp8          Hadamard-128 + power-of-two-scale FP8 quantizer
@@ -100,6 +102,47 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
                               uint8_t* value_cache, float* k_scale_cache,
                               float* v_scale_cache, int64_t num_blocks,
                               int32_t block_size, void* stream);
+
+/*
+ * TurboQuant combined-slot cache write: the encoder of the slot formats
+ * tq_decode_attention reads (triton_turboquant_decode.py, _tq_decode_stage1
+ * reads them; the pages show no writer, so the encoder below is a reading).
+ * For every token t with slot_mapping[t] in [0, num_blocks * block_size)
+ * and every kv head h, the slot kv_cache[slot / bs, slot % bs, h, :] is
+ * rewritten from k = fp32(key[t, h, :]) and v = fp32(value[t, h, :]):
+ *   TQ_KEY_FP8   bytes 0..D-1 = e4m3(clamp(k, +-448)) (RNE);
+ *   TQ_KEY_MSE3 / MSE4 (b = 3 / 4):
+ *     ss   = sum k_i^2 in fp32, added pairwise with strides 1, 2, ..., D/2
+ *     norm = sqrt(ss) (correctly rounded)
+ *     y    = FWHT(k * rot_signs) in fp32, strides 1 -> D/2 (rot_signs NULL:
+ *            all +1); u_i = fl(fl(y_i * r) / norm), r = fl(1 / sqrt(D)),
+ *            u = 0 when norm == 0
+ *     idx_i = argmin_j |u_i - centroids[j]| (fp32; ties to the lower j),
+ *            packed LSB first in ceil(D*b/8) bytes, then fp16(norm);
+ *   values (b = 3 / 4 for TQ_VAL_U3 / U4):
+ *     scale = max(fl((max v - min v) / (2^b - 1)), 1e-6), zero = min v (+0
+ *     for a zero minimum), both stored fp16 (RNE); idx = clamp(rint(fl(v - zero16) / scale16), 0,
+ *     2^b - 1) (IEEE division), packed LSB first after the key region, then
+ *     fp16 scale and fp16 zero; the remaining bytes of the slot are zeroed.
+ * The slot bytes are a bit-exact function of the inputs.
+ *
+ *   key, value      device, [num_tokens, Hk, D] of kv_dtype (TQ_DTYPE_*)
+ *   slot_mapping    device, [num_tokens] int64 (< 0 or out of range: skip)
+ *   centroids       device, [2^b] fp32 (centroid keys; NULL for FP8 keys)
+ *   rot_signs       device, [D] fp32 +-1, or NULL (centroid keys)
+ *   kv_cache        device, [num_blocks, block_size, Hk, slot_bytes] u8,
+ *                   slot_bytes >= tq_slot_bytes(D, key_fmt, val_fmt), a
+ *                   multiple of 16
+ *   D in {64, 128}. num_tokens == 0 returns TQ_OK without launching.
+ *   Alignment: key, value, rot_signs, kv_cache 16 B; slot_mapping 8 B;
+ *   centroids 4 B. num_tokens * Hk < 2^31. Slots must be unique.
+ */
+int tq_encode_and_cache(const void* key, const void* value, int32_t kv_dtype,
+                        int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t key_fmt, int32_t val_fmt, const int64_t* slot_mapping,
+                        const float* centroids, const float* rot_signs, uint8_t* kv_cache,
+                        int32_t slot_bytes, int64_t num_blocks, int32_t block_size,
+                        void* stream);
 
 /*
  * Decode attention, one query token per sequence.

@@ -490,7 +490,7 @@ static void rotate_f64(const float* x, const float* rot_signs, int d, double* y)
  * fp16, u = Pi k / norm, index = nearest centroid (ties to the lower index;
  * norm 0 gives the centroid nearest 0). Values (b bits): scale =
  * max((max-min)/(2^b-1), 1e-6) and zero = min, both stored fp16; index =
- * clamp(rint((v - zero16) / scale16), 0, 2^b-1).
+ * clamp(rint((v - zero16) / scale16), 0, 2^b-1); a zero minimum is +0.
  * Everything is fp32, each operation rounded once, in this order:
  *   ss   = sum of k_i^2, added pairwise with strides 1, 2, ..., d/2 (the
  *          order of the butterflies; see tree_sum_f32);
@@ -556,6 +556,9 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
         if (v[i] < mn) mn = v[i];
         if (v[i] > mx) mx = v[i];
       }
+      /* a zero minimum is stored as +0 whatever the signs of the zeros in
+       * the row, so the bytes do not depend on the order of the reduction */
+      mn = mn + 0.0f;
       float levels = (float)((1 << vb) - 1);
       float sc = (mx - mn) / levels;
       if (!(sc > 1e-6f)) sc = 1e-6f;

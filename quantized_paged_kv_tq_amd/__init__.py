@@ -5,6 +5,7 @@ Thin Python binding over the C ABI of ``libtq_amd.so`` (declared in
 in the library's HIP kernels. torch supplies device memory and streams.
 
     tq_reshape_and_cache_int4   RHT + INT4 paged-cache write
+    tq_encode_and_cache         TurboQuant combined-slot cache write
     tq_decode_attention         split-KV decode (stage 1 + stage 2)
     fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
 
@@ -63,6 +64,10 @@ SYMBOLS = {
         C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int32,
         C.c_void_p]),
+    "tq_encode_and_cache": (C.c_int, [
+        C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32,
+        C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int64,
+        C.c_int32, C.c_void_p]),
     "tq_decode_workspace_bytes": (C.c_size_t, [C.c_int32] * 5),
     "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
@@ -158,6 +163,42 @@ def tq_reshape_and_cache_int4(key, value, key_cache, value_cache, slot_mapping, 
     ([NB, bs, Hk, D/2] u8 and [NB, bs, Hk] f32 scale words), in place."""
     prepare_reshape(key, value, key_cache, value_cache, slot_mapping, k_scale_cache=k_scale_cache,
                     v_scale_cache=v_scale_cache, rht_signs=rht_signs).run(stream, key.device)
+
+
+def prepare_encode(key, value, kv_cache, slot_mapping, *, key_fmt, val_fmt, centroids=None,
+                   rot_signs=None):
+    """Validate and marshal a tq_encode_and_cache call (see Prepared)."""
+    T, hk, d = key.shape
+    if value.shape != key.shape or value.dtype != key.dtype:
+        raise ValueError("key and value must share shape and dtype")
+    if key.dtype not in _DT:
+        raise TypeError("unsupported dtype %s" % key.dtype)
+    for t, n in ((key, "key"), (value, "value")):
+        _need(t, key.dtype, n)
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    _need(kv_cache, torch.uint8, "kv_cache")
+    if kv_cache.dim() != 4 or kv_cache.shape[2] != hk:
+        raise ValueError("kv_cache must be [NB, bs, Hk, slot_bytes]")
+    nb, bs, _, sb = kv_cache.shape
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    keep = [key, value, kv_cache, slot_mapping]
+    for t, n in ((centroids, "centroids"), (rot_signs, "rot_signs")):
+        if t is not None:
+            _need(t, torch.float32, n)
+            keep.append(t)
+    args = (_ptr(key), _ptr(value), _DT[key.dtype], T, hk, d, key_fmt, val_fmt, _ptr(slot_mapping),
+            _ptr(centroids) if centroids is not None else None,
+            _ptr(rot_signs) if rot_signs is not None else None, _ptr(kv_cache), sb, nb, bs)
+    return Prepared(lib().tq_encode_and_cache, args, keep)
+
+
+def tq_encode_and_cache(key, value, kv_cache, slot_mapping, *, key_fmt, val_fmt, centroids=None,
+                        rot_signs=None, stream=None):
+    """TurboQuant encode of key/value [T, Hk, D] into the combined-slot cache
+    [NB, bs, Hk, slot_bytes] u8, in place."""
+    prepare_encode(key, value, kv_cache, slot_mapping, key_fmt=key_fmt, val_fmt=val_fmt,
+                   centroids=centroids, rot_signs=rot_signs).run(stream, key.device)
 
 
 def tq_decode_workspace_bytes(B, Hq, Hk, D, num_kv_splits):

@@ -105,6 +105,58 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
                   "tq_reshape_and_cache_int4");
 }
 
+int tq_encode_and_cache(const void* key, const void* value, int32_t kv_dtype,
+                        int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t key_fmt, int32_t val_fmt, const int64_t* slot_mapping,
+                        const float* centroids, const float* rot_signs, uint8_t* kv_cache,
+                        int32_t slot_bytes, int64_t num_blocks, int32_t block_size,
+                        void* stream) {
+  if (num_tokens < 0) return fail(TQ_EINVAL, "num_tokens < 0");
+  if (num_kv_heads <= 0) return fail(TQ_EINVAL, "num_kv_heads must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TQ_ENOTSUP, "head_dim %d not supported (64, 128)", head_dim);
+  if (kv_dtype != TQ_DTYPE_F32 && kv_dtype != TQ_DTYPE_F16 && kv_dtype != TQ_DTYPE_BF16)
+    return fail(TQ_ENOTSUP, "kv_dtype %d not supported", kv_dtype);
+  const int sb = tq_slot_bytes(head_dim, key_fmt, val_fmt);
+  if (sb < 0) return fail(TQ_EINVAL, "invalid key_fmt %d / val_fmt %d", key_fmt, val_fmt);
+  if (slot_bytes < sb || slot_bytes % 16 != 0)
+    return fail(TQ_EINVAL, "slot_bytes %d: need a multiple of 16 >= %d", slot_bytes, sb);
+  if (block_size <= 0 || num_blocks < 0) return fail(TQ_EINVAL, "bad block_size / num_blocks");
+  if (num_tokens == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  const bool centroid = key_fmt == TQ_KEY_MSE3 || key_fmt == TQ_KEY_MSE4;
+  if (!key || !value || !slot_mapping || !kv_cache || (centroid && !centroids))
+    return fail(TQ_EINVAL, "null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(kv_cache, 16) ||
+      !aligned(slot_mapping, 8) || (rot_signs && !aligned(rot_signs, 16)) ||
+      (centroids && !aligned(centroids, 4)))
+    return fail(TQ_EINVAL,
+                "misaligned pointer (key/value/kv_cache/rot_signs 16 B, slots 8 B, centroids 4 B)");
+  if (num_tokens * num_kv_heads >= ((int64_t)1 << 31))
+    return fail(TQ_EINVAL, "num_tokens * num_kv_heads must be below 2^31");
+  tqk::TqWriteParams p;
+  p.key = key;
+  p.value = value;
+  p.slots = slot_mapping;
+  p.centroids = centroids;
+  p.rot_signs = centroid ? rot_signs : nullptr;
+  p.cache = kv_cache;
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.hk = num_kv_heads;
+  p.d = head_dim;
+  p.dtype = kv_dtype;
+  p.block_size = block_size;
+  p.slot_bytes = slot_bytes;
+  p.key_fmt = key_fmt;
+  p.val_fmt = val_fmt;
+  p.kps = key_region_bytes(head_dim, key_fmt);
+  p.vdb = value_index_bytes(head_dim, val_fmt);
+  return launched(tqk::launch_write_tq(p, static_cast<hipStream_t>(stream)), "tq_encode_and_cache");
+}
+
 int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3, float* scale,
                       void* stream) {
   if (rows < 0) return fail(TQ_EINVAL, "rows < 0");

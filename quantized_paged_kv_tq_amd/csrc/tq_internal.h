@@ -32,6 +32,19 @@ hipError_t launch_fwht128_fp8(const void* x, int64_t rows, uint8_t* y, float* sc
 enum { KF_INT4 = 0, KF_FP8 = 1, KF_MSE3 = 2, KF_MSE4 = 3 };
 enum { VF_INT4 = 0, VF_U3 = 1, VF_U4 = 2 };
 
+struct TqWriteParams {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  const float* centroids;
+  const float* rot_signs;
+  uint8_t* cache;
+  int64_t num_tokens, num_blocks;
+  int hk, d, dtype, block_size, slot_bytes;
+  int key_fmt, val_fmt, kps, vdb;
+};
+hipError_t launch_write_tq(const TqWriteParams& p, hipStream_t st);
+
 struct DecodeParams {
   int B, hq, hk, d, g, block_size, max_blocks, splits;
   int key_fmt, val_fmt, norm_correction;

@@ -1,0 +1,240 @@
+// TurboQuant combined-slot cache write: the encoder of the slot formats the
+// TurboQuant decode reads (triton_turboquant_decode.py, _tq_decode_stage1,
+// reads FP8 or Lloyd-Max centroid keys and uniform 3/4-bit values; the pages
+// show no writer). For each (token, kv head) with a valid slot:
+//   FP8 keys       e4m3(clamp(k, +-448)), D bytes;
+//   centroid keys  norm = sqrt(pairwise sum of k^2), u = (FWHT(s * k) *
+//                  fl(1/sqrt(D))) / norm, b-bit index of the nearest
+//                  centroid (ties to the lower index; norm 0: u = 0), packed
+//                  LSB first, then fp16(norm);
+//   values         scale = max((max - min) / (2^b - 1), 1e-6), zero = min,
+//                  both rounded to fp16; index = clamp(rint((v - zero16) /
+//                  scale16), 0, 2^b - 1), packed LSB first; then fp16 scale
+//                  and zero; the slot's padding bytes are zeroed.
+// All arithmetic is fp32 with one rounding per operation in that order
+// (sums with strides 1 -> D/2, correctly rounded sqrt and division), which
+// is what makes the bytes reproducible.
+//
+// Lane layout as the INT4 writer (write_rows.h): D/16 lanes per row, row r
+// of a pass is (item r / 2, K for even r, V for odd r). A lane holds 8
+// consecutive elements per half, i.e. whole bytes of a 3- or 4-bit stream
+// (3 or 4 bytes per half).
+//
+// Compiled without fp contraction.
+#include "tq_device.h"
+#include "tq_internal.h"
+#include "write_rows.h"
+
+namespace tqk {
+
+namespace {
+
+struct TqWriteArgs {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  const float* centroids;
+  const float* rot_signs;
+  uint8_t* cache;
+  int64_t total_rows, cache_slots;
+  int hk, slot_bytes;
+  int key_fmt, kb, vb;  // key format, key index bits (3/4; 8 = FP8), value bits
+  int kps, vdb;         // key region bytes, value index bytes
+};
+
+// LSB-first b-bit stream bytes of 8 consecutive indices (b in {3, 4}).
+__device__ __forceinline__ uint32_t pack8(const uint32_t q[8], int b) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= q[j] << (b * j);
+  return w;
+}
+__device__ __forceinline__ void store_bytes(uint8_t* dst, uint32_t w, int n) {
+  for (int i = 0; i < n; ++i) dst[i] = (uint8_t)(w >> (8 * i));
+}
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int D, int DT, int R>
+__global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
+  constexpr int LPR = D / 16;
+  constexpr int ROWS = 256 / LPR;
+  const int li = threadIdx.x % LPR;
+  float sg[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
+
+  float x[R][16];
+  int64_t slot[R];
+  int head[R];
+  bool is_v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = ((int64_t)blockIdx.x * R + r) * ROWS + threadIdx.x / LPR;
+    const bool in_range = row < a.total_rows;
+    const int64_t item = in_range ? (row >> 1) : 0;
+    is_v[r] = row & 1;
+    const uint32_t it32 = (uint32_t)item;
+    const int64_t t = (int64_t)(it32 / (uint32_t)a.hk);
+    head[r] = (int)(it32 - (uint32_t)t * (uint32_t)a.hk);
+    slot[r] = in_range ? a.slots[t] : -1;
+    const void* src = is_v[r] ? a.value : a.key;
+    load8<DT>(src, item * D + li * 8, x[r]);
+    load8<DT>(src, item * D + D / 2 + li * 8, x[r] + 8);
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (slot[r] < 0 || slot[r] >= a.cache_slots) continue;
+    uint8_t* s = a.cache + (slot[r] * a.hk + head[r]) * (int64_t)a.slot_bytes;
+    const float* v = x[r];
+    if (!is_v[r]) {
+      if (a.key_fmt == KF_FP8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float c0 = __builtin_amdgcn_fmed3f(v[2 * j], -448.0f, 448.0f);
+          const float c1 = __builtin_amdgcn_fmed3f(v[2 * j + 1], -448.0f, 448.0f);
+          const uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
+          if (j & 1) w[j >> 1] |= p << 16;
+          else w[j >> 1] = p;
+        }
+        *reinterpret_cast<uint2*>(s + 8 * li) = make_uint2(w[0], w[1]);
+        *reinterpret_cast<uint2*>(s + D / 2 + 8 * li) = make_uint2(w[2], w[3]);
+        continue;
+      }
+      // ---- centroid keys: norm by pairwise sums (strides 1 -> D/2) ----
+      float hs[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float q2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q2[j] = v[8 * hf + j] * v[8 * hf + j];
+        q2[0] = q2[0] + q2[1];
+        q2[2] = q2[2] + q2[3];
+        q2[4] = q2[4] + q2[5];
+        q2[6] = q2[6] + q2[7];
+        q2[0] = q2[0] + q2[2];
+        q2[4] = q2[4] + q2[6];
+        hs[hf] = q2[0] + q2[4];
+        // strides 8 .. D/4: lanes li ^ 1, li ^ 2, (li ^ 4); the sum of a
+        // pair is the same in both lanes
+        if constexpr (LPR >= 2) hs[hf] = hs[hf] + dpp_xor<1>(hs[hf]);
+        if constexpr (LPR >= 4) hs[hf] = hs[hf] + dpp_xor<2>(hs[hf]);
+        if constexpr (LPR >= 8) hs[hf] = hs[hf] + dpp_xor<4>(hs[hf]);
+      }
+      const float nrm = __builtin_sqrtf(hs[0] + hs[1]);
+      // ---- rotation ----
+      float y[16];
+      if (a.rot_signs) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float4* sp = reinterpret_cast<const float4*>(a.rot_signs + hf * (D / 2) + li * 8);
+          const float4 s0 = sp[0], s1 = sp[1];
+          const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[8 * hf + j] = v[8 * hf + j] * ss[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = v[j];
+      }
+      fwht_row<LPR>(y, sg);
+      const float rs = D == 128 ? 0.0883883461356163f : 0.125f;  // fp32 1/sqrt(D)
+      const int nc = 1 << a.kb;
+      uint32_t q[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float u = nrm > 0.0f ? (y[j] * rs) / nrm : 0.0f;
+        uint32_t best = 0;
+        float bd = fabsf(u - a.centroids[0]);
+        for (int c = 1; c < nc; ++c) {
+          const float dc = fabsf(u - a.centroids[c]);
+          if (dc < bd) {
+            bd = dc;
+            best = (uint32_t)c;
+          }
+        }
+        q[j] = best;
+      }
+      const int b = a.kb;
+      store_bytes(s + b * li, pack8(q, b), b);
+      store_bytes(s + b * (D / 16) + b * li, pack8(q + 8, b), b);
+      if (li == 0) *reinterpret_cast<uint16_t*>(s + a.kps - 2) = f16_bits(nrm);
+      continue;
+    }
+    // ---- values ----
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+      mn = fminf(mn, v[j]);
+      mx = fmaxf(mx, v[j]);
+    }
+    mn = group16_min<LPR>(mn) + 0.0f;  // a zero minimum is +0
+    mx = group16_max<LPR>(mx);
+    const float levels = (float)((1 << a.vb) - 1);
+    float sc = (mx - mn) / levels;
+    if (!(sc > 1e-6f)) sc = 1e-6f;
+    const uint16_t sc16 = f16_bits(sc), z16 = f16_bits(mn);
+    const float scr = (float)__builtin_bit_cast(_Float16, sc16);
+    const float zr = (float)__builtin_bit_cast(_Float16, z16);
+    uint32_t q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float idx = __builtin_rintf((v[j] - zr) / scr);
+      idx = idx < 0.0f ? 0.0f : (idx > levels ? levels : idx);
+      q[j] = (uint32_t)idx;
+    }
+    const int b = a.vb;
+    uint8_t* vd = s + a.kps;
+    store_bytes(vd + b * li, pack8(q, b), b);
+    store_bytes(vd + b * (D / 16) + b * li, pack8(q + 8, b), b);
+    if (li == 0) {
+      *reinterpret_cast<uint16_t*>(vd + a.vdb) = sc16;
+      *reinterpret_cast<uint16_t*>(vd + a.vdb + 2) = z16;
+    }
+    // padding bytes of the slot
+    for (int i = a.kps + a.vdb + 4 + li; i < a.slot_bytes; i += LPR) s[i] = 0;
+  }
+}
+
+template <int D, int DT>
+hipError_t launch(const TqWriteArgs& a, hipStream_t st) {
+  constexpr int R = 2;
+  constexpr int ROWS = 256 / (D / 16);
+  const int64_t blocks = (a.total_rows + ROWS * R - 1) / (ROWS * R);
+  hipLaunchKernelGGL((write_tq_kernel<D, DT, R>), dim3((uint32_t)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_write_tq(const TqWriteParams& p, hipStream_t st) {
+  TqWriteArgs a;
+  a.key = p.key;
+  a.value = p.value;
+  a.slots = p.slots;
+  a.centroids = p.centroids;
+  a.rot_signs = p.rot_signs;
+  a.cache = p.cache;
+  a.total_rows = p.num_tokens * p.hk * 2;
+  a.cache_slots = p.num_blocks * (int64_t)p.block_size;
+  a.hk = p.hk;
+  a.slot_bytes = p.slot_bytes;
+  a.key_fmt = p.key_fmt;
+  a.kb = p.key_fmt == KF_MSE3 ? 3 : (p.key_fmt == KF_MSE4 ? 4 : 8);
+  a.vb = p.val_fmt == VF_U3 ? 3 : 4;
+  a.kps = p.kps;
+  a.vdb = p.vdb;
+  if (p.d == 128) {
+    if (p.dtype == TQ_DT_BF16) return launch<128, TQ_DT_BF16>(a, st);
+    if (p.dtype == TQ_DT_F16) return launch<128, TQ_DT_F16>(a, st);
+    return launch<128, TQ_DT_F32>(a, st);
+  }
+  if (p.dtype == TQ_DT_BF16) return launch<64, TQ_DT_BF16>(a, st);
+  if (p.dtype == TQ_DT_F16) return launch<64, TQ_DT_F16>(a, st);
+  return launch<64, TQ_DT_F32>(a, st);
+}
+
+}  // namespace tqk

@@ -31,7 +31,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
-                          "tq_decode_workspace_bytes", "tq_slot_bytes",
+                          "tq_encode_and_cache", "tq_decode_workspace_bytes", "tq_slot_bytes",
                           "tq_decode_attention", "fwht128_quant_fp8"}
     raw = C.CDLL(tq.LIB_PATH)
     for n in names:
@@ -145,3 +145,29 @@ def test_binding_requires_library(monkeypatch):
     monkeypatch.setattr(tq, "LIB_PATH", "/nonexistent/libtq_amd.so")
     with pytest.raises(ImportError):
         tq.lib()
+
+
+def test_tq_writer_validation(L):
+    f = L.tq_encode_and_cache
+    # key, value, dtype, T, Hk, D, key_fmt, val_fmt, slots, centroids, rot_signs, cache,
+    # slot_bytes, num_blocks, block_size, stream
+    ok = (tq.DTYPE_BF16, 0, 8, 128, tq.KEY_FP8, tq.VAL_U4)
+    assert f(None, None, *ok, None, None, None, None, 208, 4, 16, None) == tq.TQ_OK
+    assert tq.last_error() == ""
+    assert f(None, None, tq.DTYPE_BF16, 5, 8, 128, tq.KEY_FP8, tq.VAL_U4, None, None, None, None,
+             208, 4, 16, None) == tq.TQ_EINVAL  # null pointers
+    assert f(None, None, tq.DTYPE_BF16, 0, 8, 128, tq.KEY_FP8, tq.VAL_U4, None, None, None, None,
+             192, 4, 16, None) == tq.TQ_EINVAL  # slot too small
+    assert f(None, None, tq.DTYPE_BF16, 0, 8, 128, tq.KEY_FP8, tq.VAL_U4, None, None, None, None,
+             216, 4, 16, None) == tq.TQ_EINVAL  # not a multiple of 16
+    assert f(None, None, tq.DTYPE_BF16, 0, 8, 128, tq.KEY_INT4, tq.VAL_U4, None, None, None, None,
+             208, 4, 16, None) == tq.TQ_EINVAL  # INT4 is not a combined-slot format
+    assert f(None, None, tq.DTYPE_BF16, 0, 8, 96, tq.KEY_FP8, tq.VAL_U4, None, None, None, None,
+             208, 4, 16, None) == tq.TQ_ENOTSUP
+    assert f(None, None, 7, 0, 8, 128, tq.KEY_FP8, tq.VAL_U4, None, None, None, None,
+             208, 4, 16, None) == tq.TQ_ENOTSUP
+    assert f(16, 16, tq.DTYPE_BF16, 5, 8, 128, tq.KEY_MSE3, tq.VAL_U3, 16, None, None, 16,
+             112, 4, 16, None) == tq.TQ_EINVAL  # centroid keys need the table
+    assert f(16, 16, tq.DTYPE_BF16, 5, 8, 128, tq.KEY_FP8, tq.VAL_U4, 16, None, None, 8,
+             208, 4, 16, None) == tq.TQ_EINVAL  # misaligned cache
+    assert "kv_cache" in tq.last_error()

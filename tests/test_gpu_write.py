@@ -113,3 +113,76 @@ def test_fwht_empty():
     import quantized_paged_kv_tq_amd as tq
     y, s = tq.fwht128_quant_fp8(torch.empty(0, 128, dtype=torch.bfloat16, device=DEV))
     assert y.shape == (0, 128) and s.shape == (0, 1)
+
+
+# ---------------------------------------------------------------------------
+# TurboQuant combined-slot writer (tq_encode_and_cache)
+
+TQ_FMTS = [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_FP8, oracle.VAL_U3),
+           (oracle.KEY_MSE3, oracle.VAL_U3), (oracle.KEY_MSE3, oracle.VAL_U4),
+           (oracle.KEY_MSE4, oracle.VAL_U4), (oracle.KEY_MSE4, oracle.VAL_U3)]
+
+
+def _centroids(key_fmt, d):
+    if key_fmt == oracle.KEY_FP8:
+        return None
+    bits = 3 if key_fmt == oracle.KEY_MSE3 else 4
+    return (oracle.lloyd_max_gaussian(1 << bits) / np.sqrt(d)).astype(np.float32)
+
+
+def _encode_both(kb, vb, dtype, slots, nb, bs, hk, d, key_fmt, val_fmt, rot_signs=None,
+                 extra_pad=0):
+    import quantized_paged_kv_tq_amd as tq
+    sb = oracle.tq_slot_bytes(d, key_fmt, val_fmt) + extra_pad
+    cen = _centroids(key_fmt, d)
+    want = np.full((nb, bs, hk, sb), 0xA5, np.uint8)  # canary: skipped slots keep it
+    got = to_dev(want)
+    k32 = W.bits_to_f32(kb, dtype)
+    v32 = W.bits_to_f32(vb, dtype)
+    oracle.tq_encode(k32, v32, key_fmt, val_fmt, cen, rot_signs, slots, want)
+    tq.tq_encode_and_cache(src_to_dev(kb, dtype), src_to_dev(vb, dtype), got, to_dev(slots),
+                           key_fmt=key_fmt, val_fmt=val_fmt,
+                           centroids=None if cen is None else to_dev(cen),
+                           rot_signs=None if rot_signs is None else to_dev(rot_signs))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("fmt", TQ_FMTS, ids=[str(f) for f in TQ_FMTS])
+@pytest.mark.parametrize("d,hk,T", [(128, 4, 300), (64, 3, 257)])
+def test_tq_encode_formats_bit_exact(fmt, d, hk, T):
+    wl = W.write_workload(num_tokens=T, hk=hk, d=d, block_size=16, skip_frac=0.1, dtype="bf16",
+                          wid=60 + d + hk + 7 * fmt[0] + fmt[1])
+    _encode_both(wl["key"], wl["value"], "bf16", wl["slot_mapping"], wl["num_blocks"], 16, hk, d,
+                 *fmt)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("key_fmt", [oracle.KEY_FP8, oracle.KEY_MSE4])
+def test_tq_encode_dtypes_rot_signs_and_padding(dtype, key_fmt):
+    d, hk, T = 128, 2, 129
+    wl = W.write_workload(num_tokens=T, hk=hk, d=d, block_size=16, skip_frac=0.05, dtype=dtype,
+                          wid=70 + key_fmt)
+    rs = None if key_fmt == oracle.KEY_FP8 else W.rht_signs(d, round_idx=3)
+    _encode_both(wl["key"], wl["value"], dtype, wl["slot_mapping"], wl["num_blocks"], 16, hk, d,
+                 key_fmt, oracle.VAL_U4, rot_signs=rs, extra_pad=32)
+
+
+@pytest.mark.parametrize("fmt", TQ_FMTS[:3], ids=[str(f) for f in TQ_FMTS[:3]])
+def test_tq_encode_special_rows(fmt):
+    """Zero and constant rows (norm 0, value range 0), FP8 saturation beyond
+    +-448, tiny and huge magnitudes, single spikes."""
+    rng = np.random.default_rng(11)
+    T, hk, d = 64, 2, 128
+    k = rng.standard_normal((T, hk, d)).astype(np.float32)
+    k[0] = 0.0
+    k[1] = 3.0
+    k[2] *= 1e-6
+    k[3] *= 1e3
+    k[4, :, 7] = 500.0
+    k[5, :, 9] = -1e5
+    v = np.flip(k, 0).copy()
+    slots = np.arange(T, dtype=np.int64)[::-1].copy()
+    slots[10] = -1
+    slots[11] = 10 ** 6  # beyond the cache: skipped
+    _encode_both(k, v, "f32", slots, 4, 16, hk, d, *fmt)
