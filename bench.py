@@ -17,8 +17,9 @@ stage 2 kernels), timed with HIP events on the stream it runs on.
 bounded sample of the same step on the host cores.
 
 Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
-tq_mixed_b, write (65536 tokens x 8 heads x 128 bf16), fwht (1,048,576 rows),
-copy (device copy used to calibrate the HBM byte counters).
+tq_mixed_b, write (65536 tokens x 8 heads x 128 bf16), tq_write_a /
+tq_write_b (the TurboQuant slot writer on the same rows), fwht (1,048,576
+rows), copy (device copy used to calibrate the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -259,6 +260,33 @@ def run_other(args, torch, tq, W):
         line = dict(workload="write: tq_reshape_and_cache_int4 65536 tokens x 8 heads x 128 bf16, "
                              "5% slots skipped", us=t * 1e6, algorithmic_bytes=nbytes,
                     TBps=nbytes / t / 1e12, pct_peak=100 * nbytes / t / PEAK_HBM)
+    elif name in ("tq_write_a", "tq_write_b"):
+        wl = W.write_workload()
+        T, hk, d = wl["key"].shape
+        fmt = (tq.KEY_FP8, tq.VAL_U4) if name.endswith("a") else (tq.KEY_MSE3, tq.VAL_U3)
+        sb = tq.tq_slot_bytes(d, *fmt)
+        per = T * hk * d * 2 * 2 + wl["num_blocks"] * 16 * hk * sb
+        ncopies = max(2, -(-1024 * 2 ** 20 // per))
+        key = torch.from_numpy(wl["key"].view(np.int16)).view(torch.bfloat16).to(dev)
+        val = torch.from_numpy(wl["value"].view(np.int16)).view(torch.bfloat16).to(dev)
+        slots = torch.from_numpy(wl["slot_mapping"]).to(dev)
+        cen = None
+        if fmt[0] != tq.KEY_FP8:
+            cen = torch.linspace(-0.2, 0.2, 8, device=dev)
+        calls = []
+        for c in range(ncopies):
+            cache = torch.zeros(wl["num_blocks"], 16, hk, sb, dtype=torch.uint8, device=dev)
+            calls.append(tq.prepare_encode(key.clone(), val.clone(), cache, slots, key_fmt=fmt[0],
+                                           val_fmt=fmt[1], centroids=cen))
+        t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
+        valid = int((wl["slot_mapping"] >= 0).sum())
+        nbytes = valid * hk * (2 * d * 2 + sb) + T * 8
+        line = dict(workload="%s: tq_encode_and_cache 65536 tokens x 8 heads x 128 bf16 -> %s "
+                             "slots of %d B, 5%% slots skipped" % (
+                                 name, "FP8 key / U4 value" if fmt[0] == tq.KEY_FP8
+                                 else "3-bit centroid key / U3 value", sb),
+                    us=t * 1e6, algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
+                    pct_peak=100 * nbytes / t / PEAK_HBM)
     elif name == "fwht":
         bits = W.fwht_rows()
         rows = bits.shape[0]

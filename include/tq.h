@@ -115,14 +115,15 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
  *     ss   = sum k_i^2 in fp32, added pairwise with strides 1, 2, ..., D/2
  *     norm = sqrt(ss) (correctly rounded)
  *     y    = FWHT(k * rot_signs) in fp32, strides 1 -> D/2 (rot_signs NULL:
- *            all +1); u_i = fl(fl(y_i * r) / norm), r = fl(1 / sqrt(D)),
+ *            all +1); u_i = fl(y_i * fl(r / norm)), r = fl(1 / sqrt(D)),
  *            u = 0 when norm == 0
  *     idx_i = argmin_j |u_i - centroids[j]| (fp32; ties to the lower j),
  *            packed LSB first in ceil(D*b/8) bytes, then fp16(norm);
  *   values (b = 3 / 4 for TQ_VAL_U3 / U4):
  *     scale = max(fl((max v - min v) / (2^b - 1)), 1e-6), zero = min v (+0
- *     for a zero minimum), both stored fp16 (RNE); idx = clamp(rint(fl(v - zero16) / scale16), 0,
- *     2^b - 1) (IEEE division), packed LSB first after the key region, then
+ *     for a zero minimum), both stored fp16 (RNE); idx = clamp(rint(
+ *     fl(fl(v - zero16) * fl(1 / scale16))), 0, 2^b - 1), packed LSB first
+ *     after the key region, then
  *     fp16 scale and fp16 zero; the remaining bytes of the slot are zeroed.
  * The slot bytes are a bit-exact function of the inputs.
  *

@@ -3,22 +3,24 @@
 // reads FP8 or Lloyd-Max centroid keys and uniform 3/4-bit values; the pages
 // show no writer). For each (token, kv head) with a valid slot:
 //   FP8 keys       e4m3(clamp(k, +-448)), D bytes;
-//   centroid keys  norm = sqrt(pairwise sum of k^2), u = (FWHT(s * k) *
-//                  fl(1/sqrt(D))) / norm, b-bit index of the nearest
+//   centroid keys  norm = sqrt(pairwise sum of k^2), u = FWHT(s * k) *
+//                  (fl(1/sqrt(D)) / norm), b-bit index of the nearest
 //                  centroid (ties to the lower index; norm 0: u = 0), packed
 //                  LSB first, then fp16(norm);
 //   values         scale = max((max - min) / (2^b - 1), 1e-6), zero = min,
-//                  both rounded to fp16; index = clamp(rint((v - zero16) /
-//                  scale16), 0, 2^b - 1), packed LSB first; then fp16 scale
+//                  both rounded to fp16; index = clamp(rint((v - zero16) *
+//                  (1 / scale16)), 0, 2^b - 1), packed LSB first; then fp16 scale
 //                  and zero; the slot's padding bytes are zeroed.
 // All arithmetic is fp32 with one rounding per operation in that order
 // (sums with strides 1 -> D/2, correctly rounded sqrt and division), which
 // is what makes the bytes reproducible.
 //
-// Lane layout as the INT4 writer (write_rows.h): D/16 lanes per row, row r
-// of a pass is (item r / 2, K for even r, V for odd r). A lane holds 8
-// consecutive elements per half, i.e. whole bytes of a 3- or 4-bit stream
-// (3 or 4 bytes per half).
+// Lane layout as the INT4 writer (write_rows.h): D/16 lanes per row, a lane
+// holds 8 consecutive elements per half, i.e. whole bytes of a 3- or 4-bit
+// stream (3 or 4 bytes per half). Key and value rows take different code,
+// so each wave holds rows of one kind only: in a workgroup pass, waves 0 and
+// 2 encode the keys and waves 1 and 3 the values of the same 128 / LPR
+// items.
 //
 // Compiled without fp contraction.
 #include "tq_device.h"
@@ -36,7 +38,7 @@ struct TqWriteArgs {
   const float* centroids;
   const float* rot_signs;
   uint8_t* cache;
-  int64_t total_rows, cache_slots;
+  int64_t total_items, cache_slots;  // items: (token, kv head) pairs
   int hk, slot_bytes;
   int key_fmt, kb, vb;  // key format, key index bits (3/4; 8 = FP8), value bits
   int kps, vdb;         // key region bytes, value index bytes
@@ -56,11 +58,86 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-template <int D, int DT, int R>
+// Centroid key of one row (D/16 lanes, 16 elements per lane): norm by
+// pairwise sums with strides 1 -> D/2, rotation, nearest centroid, packing.
+template <int D, int KB>
+__device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* s, int li,
+                                                    const float (&cen)[1 << KB],
+                                                    const float* rot_signs, int kps,
+                                                    const float sg[3]) {
+  constexpr int LPR = D / 16;
+  float hs[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    float q2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q2[j] = v[8 * hf + j] * v[8 * hf + j];
+    q2[0] = q2[0] + q2[1];
+    q2[2] = q2[2] + q2[3];
+    q2[4] = q2[4] + q2[5];
+    q2[6] = q2[6] + q2[7];
+    q2[0] = q2[0] + q2[2];
+    q2[4] = q2[4] + q2[6];
+    hs[hf] = q2[0] + q2[4];
+    // strides 8 .. D/4: lanes li ^ 1, li ^ 2, (li ^ 4); the sum of a pair
+    // is the same in both lanes
+    if constexpr (LPR >= 2) hs[hf] = hs[hf] + dpp_xor<1>(hs[hf]);
+    if constexpr (LPR >= 4) hs[hf] = hs[hf] + dpp_xor<2>(hs[hf]);
+    if constexpr (LPR >= 8) hs[hf] = hs[hf] + dpp_xor<4>(hs[hf]);
+  }
+  const float nrm = __builtin_sqrtf(hs[0] + hs[1]);
+  float y[16];
+  if (rot_signs) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const float4* sp = reinterpret_cast<const float4*>(rot_signs + hf * (D / 2) + li * 8);
+      const float4 s0 = sp[0], s1 = sp[1];
+      const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[8 * hf + j] = v[8 * hf + j] * ss[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y[j] = v[j];
+  }
+  fwht_row<LPR>(y, sg);
+  const float rs = D == 128 ? 0.0883883461356163f : 0.125f;  // fp32 1/sqrt(D)
+  const float wn = nrm > 0.0f ? rs / nrm : 0.0f;
+  uint32_t q[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float u = y[j] * wn;
+    uint32_t best = 0;
+    float bd = fabsf(u - cen[0]);
+#pragma unroll
+    for (int c = 1; c < (1 << KB); ++c) {
+      const float dc = fabsf(u - cen[c]);
+      if (dc < bd) {
+        bd = dc;
+        best = (uint32_t)c;
+      }
+    }
+    q[j] = best;
+  }
+  store_bytes(s + KB * li, pack8(q, KB), KB);
+  store_bytes(s + KB * (D / 16) + KB * li, pack8(q + 8, KB), KB);
+  if (li == 0) *reinterpret_cast<uint16_t*>(s + kps - 2) = f16_bits(nrm);
+}
+
+// KB: key index bits (3 or 4; 8 for FP8 keys)
+template <int D, int DT, int KB, int R>
 __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
   constexpr int LPR = D / 16;
-  constexpr int ROWS = 256 / LPR;
+  constexpr int NC = KB == 8 ? 1 : 1 << KB;
+  // the centroid table, once per workgroup (uniform: scalar registers)
+  float cen[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) cen[c] = KB == 8 ? 0.0f : a.centroids[c];
+  constexpr int ITEMS = 128 / LPR;  // items per pass
   const int li = threadIdx.x % LPR;
+  const int wave = threadIdx.x >> 6;
+  const bool values = wave & 1;  // wave-uniform
+  const int it_in = (wave >> 1) * (64 / LPR) + (threadIdx.x & 63) / LPR;
   float sg[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
@@ -71,10 +148,10 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
   bool is_v[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t row = ((int64_t)blockIdx.x * R + r) * ROWS + threadIdx.x / LPR;
-    const bool in_range = row < a.total_rows;
-    const int64_t item = in_range ? (row >> 1) : 0;
-    is_v[r] = row & 1;
+    const int64_t it = ((int64_t)blockIdx.x * R + r) * ITEMS + it_in;
+    const bool in_range = it < a.total_items;
+    const int64_t item = in_range ? it : 0;
+    is_v[r] = values;
     const uint32_t it32 = (uint32_t)item;
     const int64_t t = (int64_t)(it32 / (uint32_t)a.hk);
     head[r] = (int)(it32 - (uint32_t)t * (uint32_t)a.hk);
@@ -90,7 +167,7 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
     uint8_t* s = a.cache + (slot[r] * a.hk + head[r]) * (int64_t)a.slot_bytes;
     const float* v = x[r];
     if (!is_v[r]) {
-      if (a.key_fmt == KF_FP8) {
+      if constexpr (KB == 8) {
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -103,66 +180,10 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
         *reinterpret_cast<uint2*>(s + 8 * li) = make_uint2(w[0], w[1]);
         *reinterpret_cast<uint2*>(s + D / 2 + 8 * li) = make_uint2(w[2], w[3]);
         continue;
-      }
-      // ---- centroid keys: norm by pairwise sums (strides 1 -> D/2) ----
-      float hs[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float q2[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) q2[j] = v[8 * hf + j] * v[8 * hf + j];
-        q2[0] = q2[0] + q2[1];
-        q2[2] = q2[2] + q2[3];
-        q2[4] = q2[4] + q2[5];
-        q2[6] = q2[6] + q2[7];
-        q2[0] = q2[0] + q2[2];
-        q2[4] = q2[4] + q2[6];
-        hs[hf] = q2[0] + q2[4];
-        // strides 8 .. D/4: lanes li ^ 1, li ^ 2, (li ^ 4); the sum of a
-        // pair is the same in both lanes
-        if constexpr (LPR >= 2) hs[hf] = hs[hf] + dpp_xor<1>(hs[hf]);
-        if constexpr (LPR >= 4) hs[hf] = hs[hf] + dpp_xor<2>(hs[hf]);
-        if constexpr (LPR >= 8) hs[hf] = hs[hf] + dpp_xor<4>(hs[hf]);
-      }
-      const float nrm = __builtin_sqrtf(hs[0] + hs[1]);
-      // ---- rotation ----
-      float y[16];
-      if (a.rot_signs) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const float4* sp = reinterpret_cast<const float4*>(a.rot_signs + hf * (D / 2) + li * 8);
-          const float4 s0 = sp[0], s1 = sp[1];
-          const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y[8 * hf + j] = v[8 * hf + j] * ss[j];
-        }
       } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) y[j] = v[j];
+        encode_centroid_key<D, KB>(v, s, li, cen, a.rot_signs, a.kps, sg);
+        continue;
       }
-      fwht_row<LPR>(y, sg);
-      const float rs = D == 128 ? 0.0883883461356163f : 0.125f;  // fp32 1/sqrt(D)
-      const int nc = 1 << a.kb;
-      uint32_t q[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float u = nrm > 0.0f ? (y[j] * rs) / nrm : 0.0f;
-        uint32_t best = 0;
-        float bd = fabsf(u - a.centroids[0]);
-        for (int c = 1; c < nc; ++c) {
-          const float dc = fabsf(u - a.centroids[c]);
-          if (dc < bd) {
-            bd = dc;
-            best = (uint32_t)c;
-          }
-        }
-        q[j] = best;
-      }
-      const int b = a.kb;
-      store_bytes(s + b * li, pack8(q, b), b);
-      store_bytes(s + b * (D / 16) + b * li, pack8(q + 8, b), b);
-      if (li == 0) *reinterpret_cast<uint16_t*>(s + a.kps - 2) = f16_bits(nrm);
-      continue;
     }
     // ---- values ----
     float mn = v[0], mx = v[0];
@@ -179,10 +200,11 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
     const uint16_t sc16 = f16_bits(sc), z16 = f16_bits(mn);
     const float scr = (float)__builtin_bit_cast(_Float16, sc16);
     const float zr = (float)__builtin_bit_cast(_Float16, z16);
+    const float inv = 1.0f / scr;
     uint32_t q[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float idx = __builtin_rintf((v[j] - zr) / scr);
+      float idx = __builtin_rintf((v[j] - zr) * inv);
       idx = idx < 0.0f ? 0.0f : (idx > levels ? levels : idx);
       q[j] = (uint32_t)idx;
     }
@@ -202,9 +224,14 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
 template <int D, int DT>
 hipError_t launch(const TqWriteArgs& a, hipStream_t st) {
   constexpr int R = 2;
-  constexpr int ROWS = 256 / (D / 16);
-  const int64_t blocks = (a.total_rows + ROWS * R - 1) / (ROWS * R);
-  hipLaunchKernelGGL((write_tq_kernel<D, DT, R>), dim3((uint32_t)blocks), dim3(256), 0, st, a);
+  constexpr int ITEMS = 128 / (D / 16);
+  const int64_t blocks = (a.total_items + ITEMS * R - 1) / (ITEMS * R);
+  if (a.kb == 3)
+    hipLaunchKernelGGL((write_tq_kernel<D, DT, 3, R>), dim3((uint32_t)blocks), dim3(256), 0, st, a);
+  else if (a.kb == 4)
+    hipLaunchKernelGGL((write_tq_kernel<D, DT, 4, R>), dim3((uint32_t)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((write_tq_kernel<D, DT, 8, R>), dim3((uint32_t)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -218,7 +245,7 @@ hipError_t launch_write_tq(const TqWriteParams& p, hipStream_t st) {
   a.centroids = p.centroids;
   a.rot_signs = p.rot_signs;
   a.cache = p.cache;
-  a.total_rows = p.num_tokens * p.hk * 2;
+  a.total_items = p.num_tokens * p.hk;
   a.cache_slots = p.num_blocks * (int64_t)p.block_size;
   a.hk = p.hk;
   a.slot_bytes = p.slot_bytes;
