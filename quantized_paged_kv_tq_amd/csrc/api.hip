@@ -246,7 +246,8 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   hipError_t e = hipErrorNotSupported;
   if (!(a->flags & TQ_FLAG_GENERIC)) {
     if (int4) e = tqk::launch_decode_int4_mfma(p, st);
-    else e = tqk::launch_decode_tq_mfma(p, st);
+    else if (a->key_fmt == TQ_KEY_FP8) e = tqk::launch_decode_tq_mfma(p, st);
+    else e = tqk::launch_decode_tqb_mfma(p, st);
   }
   if (e == hipErrorNotSupported) e = tqk::launch_decode_generic(p, st);
   if (e != hipSuccess) return launched(e, "tq_decode_attention stage 1");

@@ -1,0 +1,628 @@
+// TurboQuant split-KV decode, stage 1, on the CDNA4 matrix cores, for
+// 3-bit Lloyd-Max centroid keys with 3-bit uniform values
+// (triton_turboquant_decode.py, _tq_decode_stage1: score = sm_scale *
+// norm16 * (q_rot . c[idx]); v = idx * scale16 + zero16; online softmax;
+// partials acc / l and m + ln l).
+//
+// Scores. A key's 3-bit index idx = b0 + 2 b1 + 4 b2 picks c[idx]; as a
+// function of its bits, c is the multilinear polynomial
+//   c(b) = sum over S of alpha_S * prod_{i in S} b_i   (S a subset of bits),
+// alpha the Moebius transform of the table. So
+//   q_rot . c[idx] = alpha_0 * sum(q_rot) + sum_{S != 0} alpha_S * (q_rot . P_S)
+// with P_S the 0/1 vector of the product of the bits in S. The seven dot
+// products with 0/1 vectors run as v_mfma_i32_16x16x64_i8 on exact
+// integers: the rotated query is scaled by 2^E to integers below 2^27 and
+// split into four balanced base-128 digits (the A operand, as in the INT4
+// path), the bit planes are the int8 B operand. The int32 sums are exact;
+// they are combined with alpha in fp32.
+//
+// Values. As in the INT4 path: P' = p * scale16 is split into four 7-bit
+// digit planes (A operand), the 3-bit indices unpacked to bytes are the B
+// operand; the zero term sum_t p_t * zero16_t is a per-head fp32 sum added
+// to every dimension at the end.
+//
+// Work decomposition, tile table, pieces and ping-pong register sets follow
+// the INT4 path (balance.h): equal ranges of the global 64-token tile list,
+// one wave per four query heads of a kv head.
+//
+// Slot layout (D = 128): bytes [0, 48) key indices (LSB-first 3-bit
+// stream), [48, 50) fp16 norm, [50, 98) value indices, [98, 100) fp16
+// scale, [100, 102) fp16 zero.
+#include "balance.h"
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tqk {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kChunk = 64;  // tiles resolved into LDS at a time
+constexpr int kTau = 4;     // headroom of the value-weight fixed point
+constexpr uint32_t kMasked = 0xFFFFFFFFu;
+constexpr uint32_t kMaskedByte = 0xFFFFFF00u;  // byte offset past any buffer
+constexpr int kFirstOfSplit = 1;
+constexpr int kLastOfSplit = 2;
+// slot offsets
+constexpr uint32_t kNormOff = 48, kValOff = 50, kScaleOff = 96;  // scale word pair at 96
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += xor_lane<2>(v);
+  v += xor_lane<1>(v);
+  return v;
+}
+__device__ __forceinline__ float exp2i(int e) { return u2f((uint32_t)(e + 127) << 23); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// four 3-bit fields (bits 0..11 of x) -> four bytes
+__device__ __forceinline__ uint32_t unpack3x4(uint32_t x) {
+  const uint32_t y = ((x & 0xFC0u) << 10) | (x & 0x3Fu);  // fields 2, 3 to bits 16..21
+  return (y | (y << 5)) & 0x07070707u;                      // fields 1, 3 to bytes 1, 3
+}
+// bits [bit, bit + 12) of the 96-bit little-endian value w
+__device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
+  const int word = bit >> 5, sh = bit & 31;
+  if (sh <= 20) return w[word] >> sh;
+  return __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)sh);
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_tqb_kernel(DecodeParams p) {
+  constexpr int NT = 64 * W;
+  __shared__ __attribute__((aligned(16))) uint32_t p8[W][4][4][16];  // weight digit planes
+  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][2][64][4];  // query digit image
+  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
+  __shared__ int4 tinfo[kChunk];
+  __shared__ int scan[W];
+  __shared__ float accl[W][8][64];  // fp32 value accumulators, lane-major
+  extern __shared__ int prefix[];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int ln = lane & 15;
+  const int lg = lane >> 4;
+  const int grp = blockIdx.x / p.nw;
+  const int wg = blockIdx.x - grp * p.nw;
+  const int qs_n = (p.g + 3) >> 2;
+  const int kvl = wave / qs_n;
+  const int qsub = wave - kvl * qs_n;
+  const int kvh = grp * p.wgh + kvl;
+  const int g = p.g;
+  const int hq0 = 4 * qsub;
+  const int gw = g - hq0 < 4 ? g - hq0 : 4;
+  const int h0 = kvh * g + hq0;
+
+  // multilinear coefficients of the centroid table (uniform); subset S of
+  // bits {b0, b1, b2} is the index mask S in 1..7
+  float al[8];
+  {
+    float c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = p.centroids[j];
+#pragma unroll
+    for (int S = 0; S < 8; ++S) {
+      float a = 0.0f;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        if ((T & S) != T) continue;
+        const int sign = __builtin_popcount(S ^ T) & 1;
+        a = sign ? a - c[T] : a + c[T];
+      }
+      al[S] = a;
+    }
+  }
+
+  // ---- tile counts of all sequences and their prefix sums ----
+  const int per = (p.B + NT - 1) / NT;
+  int run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      run += seq_tiles(seq_splits(p, b));
+      prefix[b + 1] = run;
+    }
+  }
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int N = 0, before = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < W; ++w2) {
+    const int t = scan[w2];
+    N += t;
+    before += w2 < wave ? t : 0;
+  }
+  {
+    const int excl = before + incl - run;
+    for (int i = 0; i < per; ++i) {
+      const int b = tid * per + i;
+      if (b < p.B) {
+        prefix[b + 1] += excl;
+        if (blockIdx.x == 0) p.wsx[b + 1] = prefix[b + 1];
+      }
+    }
+    if (tid == 0) {
+      prefix[0] = 0;
+      if (blockIdx.x == 0) p.wsx[0] = 0;
+    }
+  }
+  __syncthreads();
+  if (N == 0) return;
+  const int lo = range_lo(wg, N, p.nw), hi = range_lo(wg + 1, N, p.nw);
+  if (lo >= hi) return;
+
+  const uint32_t bs = (uint32_t)p.block_size;
+  const bool bs_pow2 = (bs & (bs - 1u)) == 0u;
+  const int bs_shift = __builtin_ctz(bs);
+  const uint32_t sb = (uint32_t)p.slot_bytes;
+  const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, nrows * sb);
+  // this lane's 3 value bytes (dims 8n .. 8n+7) start at byte kValOff + 3n;
+  // one dword load from that byte offset (buffer loads take byte offsets,
+  // dword loads need not be 4-byte aligned)
+  const uint32_t vbyte = kValOff + 3u * (uint32_t)ln;
+
+  // ---- registers of one tile ----
+  // key bytes [12g, 12g + 12) of tokens 16s + n (dims 32g .. 32g+31); the
+  // norm word and scale/zero words of token `lane`; the dword starting at
+  // value byte 3n of tokens 16s + 4g + k
+  struct Buf {
+    uint32_t kraw[4][3];
+    uint32_t nw, sz0, sz1, live;
+    uint32_t vraw[4][4];
+  };
+  auto slot_of = [&](int k, int j) -> uint32_t {
+    const uint32_t r = tok_rows[k][j];
+    return r == kMasked ? kMaskedByte : (r + (uint32_t)kvh) * sb;
+  };
+  // keys and per-token words first; the value windows after the current
+  // tile's scores (issue_v), which keeps both tiles' values from being live
+  // through the score computation
+  auto issue_v = [&](Buf& B, int k) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
+        B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + vbyte), 0, 0);
+      }
+    }
+  };
+  auto issue = [&](Buf& B, int k) {
+    B.live = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t o = slot_of(k, 16 * s + ln);
+      B.live |= (o != kMaskedByte ? 1u : 0u) << s;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        B.kraw[s][i] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + 12u * lg + 4u * i), 0, 0);
+    }
+    {
+      const uint32_t o = slot_of(k, lane);
+      B.nw = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + kNormOff), 0, 0);
+      const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rkv, (int)(o + kScaleOff), 0, 0);
+      B.sz0 = w.x;
+      B.sz1 = w.y;
+    }
+  };
+
+  // ---- online softmax state of the current segment ----
+  float mref, l, zacc;  // per lane: head lg of this wave
+  float(*acc)[64] = accl[wave];
+  v4i cacc[8];
+  int ev = 0;
+  float sref = 0.0f;
+  bool empty = true;
+  int since_flush = 0;
+  auto reset = [&]() {
+    mref = -INFINITY;
+    l = 0.0f;
+    zacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[i][lane] = 0.0f;
+      cacc[i] = v4i{0, 0, 0, 0};
+    }
+    ev = 0;
+    sref = 0.0f;
+    empty = true;
+    since_flush = 0;
+  };
+  // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
+  // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
+  auto flush = [&](float alpha) {
+    const float pinv = exp2i(-ev);
+    if (!empty) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e0 = (float)cacc[i].x, e1 = (float)cacc[i].y;
+        const float e2 = (float)cacc[i].z, e3 = (float)cacc[i].w;
+        const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+        acc[i][lane] = __builtin_fmaf(val, pinv, acc[i][lane]) * alpha;
+        cacc[i] = v4i{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][lane] *= alpha;
+    }
+    l *= alpha;
+    zacc *= alpha;
+    empty = true;
+  };
+
+  // ---------------- query of sequence b ----------------
+  // q' = FWHT(rot_signs * q) (two dims per lane), scaled by 2^E to integers
+  // below 2^27 and split into four balanced base-128 digits; the image for
+  // MFMA chunk kc: lane (m = 4h' + piece, g), dword j, byte bb holds the
+  // digit of dim 32g + 16kc + 4j + bb -- the byte order of the bit planes.
+  v4i qa[2];
+  float qsum, qf;  // this lane's head (lg): sum of the scaled query, score scale
+  auto load_query = [&](int b) {
+    float qx[4][2];
+    const float s0 = p.rot_signs ? p.rot_signs[lane] : 1.0f;
+    const float s1 = p.rot_signs ? p.rot_signs[lane + 64] : 1.0f;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const bool ok = hh < gw;
+      const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (ok ? hh : 0)) * D;
+      qx[hh][0] = ok ? qrow[lane] * s0 : 0.0f;
+      qx[hh][1] = ok ? qrow[lane + 64] * s1 : 0.0f;
+    }
+    uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0]);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      float x0 = qx[hh][0], x1 = qx[hh][1];
+      {
+        const float a = x0 + x1, c = x0 - x1;
+        x0 = a;
+        x1 = c;
+      }
+      x0 = butterfly_lanes<1>(x0, lane & 1);   x1 = butterfly_lanes<1>(x1, lane & 1);
+      x0 = butterfly_lanes<2>(x0, lane & 2);   x1 = butterfly_lanes<2>(x1, lane & 2);
+      x0 = butterfly_lanes<4>(x0, lane & 4);   x1 = butterfly_lanes<4>(x1, lane & 4);
+      x0 = butterfly_lanes<8>(x0, lane & 8);   x1 = butterfly_lanes<8>(x1, lane & 8);
+      x0 = butterfly_lanes<16>(x0, lane & 16); x1 = butterfly_lanes<16>(x1, lane & 16);
+      x0 = butterfly_lanes<32>(x0, lane & 32); x1 = butterfly_lanes<32>(x1, lane & 32);
+      // x0 = q'[lane], x1 = q'[lane + 64]
+      const float amax = group_max<64>(fmaxf(fabsf(x0), fabsf(x1)));
+      const int E = amax > 0.0f ? 26 - ((int)((f2u(amax) >> 23) & 0xFF) - 127) : 0;
+      const float sc = exp2i(E);
+      float dsum[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int dim = lane + 64 * e;
+        int v = (int)__builtin_rintf((e ? x1 : x0) * sc);
+        const int gg = dim >> 5, o = dim & 31;
+        const int kc = o >> 4, j = (o & 15) >> 2, bb = o & 3;
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) {
+          const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
+          v = (v - dk) >> 7;
+          const int L = 16 * gg + 4 * hh + pc;
+          img[((kc * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
+          dsum[pc] = (e ? dsum[pc] : 0.0f) + (float)dk;
+        }
+      }
+      float t[4];
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) t[pc] = group_sum<64>(dsum[pc]);
+      if (hh == lg) {
+        qsum = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(t[3], 128.0f, t[2]), 128.0f, t[1]), 128.0f, t[0]);
+        // score in base-2 units = sm_scale / sqrt(D) * log2(e) * 2^-E * norm * (integer dot)
+        qf = p.sm_scale * 0.08838834764831845f * kLog2e * exp2i(-E);
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][kc][lane][0]);
+      qa[kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
+    }
+  };
+
+  // ---------------- segment bookkeeping ----------------
+  int seg_b = -1, seg_s = 0;
+  bool seg_from_start = false, seg_to_end = false, seg_first = false;
+  auto emit = [&]() {
+    flush(1.0f);
+    const bool whole = seg_from_start && seg_to_end;
+    const float lt = row16_sum(l);
+    const float zt = row16_sum(zacc);
+    const int hh = lg;
+    if (hh < gw) {
+      float* out;
+      if (whole)
+        out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
+      else
+        out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
+                       kvl * g + hq0 + hh) * (D + 1);
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      float* dst = out + 8 * ln;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = (acc[i][lane] + zt) * inv;
+      if (ln == 0) out[D] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  };
+
+  // ---------------- one tile ----------------
+  auto process = [&](Buf& X, Buf& Y, int k, int c0) {
+    const int gk = c0 + k;
+    const int4 info = tinfo[k];
+    if (gk == lo || (info.z & kFirstOfSplit)) {
+      if (gk != lo) emit();
+      if (gk == lo || info.x != seg_b) load_query(info.x);
+      reset();
+      seg_b = info.x;
+      seg_s = info.y;
+      seg_from_start = (info.z & kFirstOfSplit) != 0;
+      seg_first = gk == lo;
+    }
+    seg_to_end = (info.z & kLastOfSplit) != 0;
+    issue(Y, k + 1);
+    // keep every use of X's registers after the next tile's loads
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- scores: lane (n, g) gets head g, token 16s + n ----
+    float sc[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
+      // index bytes of dims 32g + 4i .. +3
+      uint32_t ix[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
+      // one bit-plane product at a time: two MFMAs (dims 32g + 16kc + ...),
+      // then its share of the dot product; lane (n, g) holds rows 4g..4g+3
+      // = the digit planes of head g, token 16s+n
+      float dot = al[0] * qsum;
+#pragma unroll
+      for (int S = 1; S < 8; ++S) {
+        v4i c = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          uint32_t pl[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = ix[4 * kc + j];
+            uint32_t m = 0x01010101u;
+            if (S & 1) m &= x;
+            if (S & 2) m &= x >> 1;
+            if (S & 4) m &= x >> 2;
+            pl[j] = m;
+          }
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[kc], v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]},
+                                                    c, 0, 0, 0);
+        }
+        const float v = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c.w, 128.0f, (float)c.z), 128.0f,
+                                                      (float)c.y), 128.0f, (float)c.x);
+        dot = __builtin_fmaf(al[S], v, dot);
+      }
+      const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
+      sc[s] = fminf(dot * (qf * nrm), mask);
+      // one token block at a time (bounds the live bit planes)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    issue_v(Y, k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    float vsc[4], vz[4];
+    float smax = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      vsc[s] = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz0));
+      vz[s] = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz1));
+      smax = fmaxf(smax, fabsf(vsc[s]));
+    }
+
+    // ---- reference maximum / weight scale; flush when they move ----
+    const float tm = row16_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const bool move = tm > mref + (float)kTau;
+    smax = row16_max(smax);
+    // a flush also bounds the int32 digit sums (< 2^31 after 8192 tiles)
+    const bool smove = smax >= sref || ++since_flush >= 8192;
+    if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
+      const float mn = fmaxf(mref, tm);
+      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
+      mref = mn;
+      flush(alpha);
+      since_flush = 0;
+      if (smax > 0.0f) {
+        const int e = (int)((f2u(smax) >> 23) & 0xFF) - 127;
+        ev = 26 - kTau - e;
+        sref = exp2i(e + 1);
+      }
+    }
+
+    // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
+    // A negative scale16 (bytes not written by the encoder) takes signed
+    // digits: the digits of p * |scale16| negated as int8.
+    const float pscale = exp2i(ev);
+    uint32_t dw[4] = {0, 0, 0, 0};
+    float ps = 0.0f, zs = 0.0f;
+    float pr[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      pr[s] = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[s] - mref);
+      ps += pr[s];
+      zs = __builtin_fmaf(pr[s], vz[s], zs);
+    }
+    const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
+                                                     vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
+    if (!any_neg) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
+        const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
+          dw[kk] |= (d & 255u) << (8 * s);
+        }
+      }
+    }
+    l += ps;
+    zacc += zs;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) p8[wave][lg][kk][ln] = dw[kk];
+    empty = false;
+    wave_sync();
+
+    // ---- value MFMAs: B operands by 4x4 byte transposes ----
+    // u[s][h]: index bytes of dims 8n + 4h .. +3 of token 16s + 4g + kk;
+    // vb[4h + i][kk] byte s = dim 8n + 4h + i of token 16s + 4g + kk
+    const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][ln >> 2][ln & 3][4 * lg]);
+    const v4i pa = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t vb[4][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t u[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t x = X.vraw[s][kk];
+          u[s] = unpack3x4(h ? x >> 12 : x);
+        }
+        const uint32_t t01l = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
+        const uint32_t t01h = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
+        const uint32_t t23l = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+        const uint32_t t23h = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+        vb[0][kk] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+        vb[1][kk] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+        vb[2][kk] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+        vb[3][kk] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
+        cacc[4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, cacc[4 * h + i], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wave_sync();
+  };
+
+  Buf A, Bb;
+  for (int c0 = lo; c0 < hi; c0 += kChunk) {
+    const int K = hi - c0 < kChunk ? hi - c0 : kChunk;
+    __syncthreads();
+    for (int e = tid; e < (K + 1) * 64; e += NT) {
+      const int k = e >> 6, j = e & 63;
+      if (k == K) {
+        tok_rows[k][j] = kMasked;
+        continue;
+      }
+      const int x = c0 + k;
+      int bl = 0, bh = p.B - 1;
+      while (bl < bh) {
+        const int m = (bl + bh + 1) >> 1;
+        if (prefix[m] <= x) bl = m;
+        else bh = m - 1;
+      }
+      const int b = bl;
+      const SeqSplits q = seq_splits(p, b);
+      const int r = x - prefix[b];
+      int s = r / q.TL;
+      if (s > q.n - 1) s = q.n - 1;
+      const int t = r - s * q.TL;
+      const int tok0 = s * q.L + t * kTileTokens;
+      int end = s * q.L + q.L;
+      if (end > q.seq) end = q.seq;
+      if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
+      const int tok = tok0 + j;
+      uint32_t row = kMasked;
+      if (tok < end) {
+        const uint32_t t32 = (uint32_t)tok;
+        const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
+        const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
+        if (page >= 0 && page < p.num_blocks)
+          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
+      }
+      tok_rows[k][j] = row;
+      if (j == 0) {
+        const int nt = (s == q.n - 1) ? q.TLast : q.TL;
+        tinfo[k] = make_int4(b, s, (t == 0 ? kFirstOfSplit : 0) | (t == nt - 1 ? kLastOfSplit : 0), 0);
+      }
+    }
+    __syncthreads();
+    issue(A, 0);
+    issue_v(A, 0);
+    for (int k = 0; k < K; k += 2) {
+      process(A, Bb, k, c0);
+      if (k + 1 >= K) break;
+      process(Bb, A, k + 1, c0);
+    }
+  }
+  emit();
+}
+
+template <int W>
+hipError_t launch(const DecodeParams& p, hipStream_t st) {
+  const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
+  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_tqb_kernel<W>), dim3(blocks), dim3(64 * W), lds, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
+  if (p.d != D || p.key_fmt != KF_MSE3 || p.val_fmt != VF_U3 || p.g > 8 || p.norm_correction)
+    return hipErrorNotSupported;
+  if (p.kps != (int)kValOff || p.vdb != 48 || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
+  // slot bytes are addressed with 32-bit buffer offsets (masked: 0xFFFFFF00)
+  if (p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  const int64_t cap = (int64_t)p.max_blocks * p.block_size;
+  if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
+  const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
+  if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
+  const int qs = (p.g + 3) / 4;
+  p.wgh = balance_heads_per_wg(p.hk, p.g);
+  const int64_t nw = balance_max_wgs(p.hk, p.g);
+  p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+  switch (p.wgh * qs) {
+    case 1: return launch<1>(p, st);
+    case 2: return launch<2>(p, st);
+    case 4: return launch<4>(p, st);
+    default: return launch<8>(p, st);
+  }
+}
+
+}  // namespace tqk

@@ -83,6 +83,10 @@ hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st);
 // FP8-key / 4-bit-value TurboQuant stage 1 on the matrix cores (D = 128,
 // g <= 8); hipErrorNotSupported otherwise. Sets p.nw / p.wgh for stage 2.
 hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st);
+// 3-bit centroid-key / 3-bit-value TurboQuant stage 1 on the matrix cores
+// (D = 128, g <= 8, no norm correction); hipErrorNotSupported otherwise.
+// Sets p.nw / p.wgh for stage 2.
+hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st);
 // Stage 2: log-sum-exp merge of the split partials (+ inverse RHT for INT4).
 hipError_t launch_merge(const DecodeParams& p, hipStream_t st);
 

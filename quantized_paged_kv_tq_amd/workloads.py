@@ -230,6 +230,31 @@ def random_tq_fp8_u4_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=8):
     return cache
 
 
+def random_tq_mse3_u3_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=9):
+    """Random 3-bit-centroid-key / 3-bit-value TurboQuant slots: uniform index
+    bytes, fp16 norms in [2^-2, 2^4), fp16 value scales of either sign with
+    magnitude in [2^-6, 2^0) and fp16 zeros in [-2, 2). For decode inputs
+    that do not depend on any writer."""
+    g = rng(w.wid, wid_tensor)
+    d = w.d
+    shp = (w.num_blocks, w.block_size, w.hk)
+    cache = np.zeros(shp + (slot_bytes,), np.uint8)
+    kb = 3 * d // 8
+    cache[..., :kb] = g.integers(0, 256, size=shp + (kb,), dtype=np.uint8)
+    nrm = np.exp2(g.uniform(-2, 4, size=shp)).astype(np.float16)
+    cache[..., kb:kb + 2] = nrm[..., None].view(np.uint8).reshape(shp + (2,))
+    vo = kb + 2
+    cache[..., vo:vo + kb] = g.integers(0, 256, size=shp + (kb,), dtype=np.uint8)
+    mag = np.exp2(g.uniform(-6, 0, size=shp))
+    sign = np.where(g.random(size=shp) < 0.25, -1.0, 1.0)
+    sc = (sign * mag).astype(np.float16)
+    zr = g.uniform(-2, 2, size=shp).astype(np.float16)
+    so = vo + kb
+    cache[..., so:so + 2] = sc[..., None].view(np.uint8).reshape(shp + (2,))
+    cache[..., so + 2:so + 4] = zr[..., None].view(np.uint8).reshape(shp + (2,))
+    return cache
+
+
 def random_int4_cache(w: DecodeWorkload, wid_tensor=7):
     """Uniformly random INT4 cache bytes plus valid scale words (positive
     normal scales in [2^-4, 2^2) with a random 4-bit zero-point in the low

@@ -267,3 +267,74 @@ def test_tq_fp8_u4_balanced_few_tiles(seq, S):
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *A_FMT)
     got, lse = gpu_tq_decode(w, q, cache, cen, *A_FMT)
     assert_close(got, ref, lse, ref_lse, "seq %s S=%d" % (seq, S))
+
+
+# ---------------------------------------------------------------------------
+# 3-bit centroid keys + 3-bit values (matrix-core path for D = 128, g <= 8)
+
+B_FMT = (oracle.KEY_MSE3, oracle.VAL_U3)
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_tq_mse3_u3_shapes(shape, flags):
+    B, hq, hk, d, bs, seq, S = shape
+    w = W.custom_decode_workload(300 + len(seq) * 7 + hq + d, B, hq, hk, d, bs, S, seq, 5, "bf16")
+    cache, cen = tq_case(w, *B_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT, flags=flags)
+    assert_close(got, ref, lse, ref_lse, str(shape))
+
+
+def test_tq_mse3_u3_rot_signs_split_invariance_and_degenerate_lengths():
+    w = W.custom_decode_workload(340, 3, 8, 2, 128, 16, 4, [37, 1, 100], 2, "bf16")
+    rs = W.rht_signs(128, round_idx=4)
+    cache, cen = tq_case(w, *B_FMT, rot_signs=rs)
+    q = W.query(w)
+    seq = np.array([37, 0, 100], np.int32)
+    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, seq, cen, rs, *B_FMT, 0, 0, w.sm_scale)
+    for S in (1, 2, 8, 37, 64, 100, 105, 256):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT, rot_signs=rs, num_splits=S, seq_lens=seq)
+        assert_close(got, ref, lse, ref_lse, "S=%d" % S)
+        assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
+
+
+def _random_centroids(seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.uniform(-0.3, 0.3, 8)).astype(np.float32)
+
+
+def test_tq_mse3_u3_random_slot_bytes_and_table():
+    """Random slots (no writer) and an arbitrary centroid table: every index
+    pattern, value scales of both signs, random norms and zeros."""
+    w = W.custom_decode_workload(341, 2, 16, 4, 128, 16, 4, [300, 77], 4, "bf16")
+    cache = W.random_tq_mse3_u3_cache(w, oracle.tq_slot_bytes(128, *B_FMT))
+    cen = _random_centroids(341)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
+    for flags in (0, tq.FLAG_GENERIC):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "random slots flags=%d" % flags)
+
+
+def test_tq_mse3_u3_balanced_many_sequences():
+    rng = np.random.default_rng(342)
+    seq = rng.choice([0, 1, 5, 63, 64, 65, 130, 200, 777], size=600).astype(np.int32)
+    w = W.custom_decode_workload(342, 600, 8, 2, 128, 16, 3, seq, 7, "bf16")
+    cache = W.random_tq_mse3_u3_cache(w, oracle.tq_slot_bytes(128, *B_FMT))
+    cen = _random_centroids(342)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
+    assert_close(got, ref, lse, ref_lse, "600 sequences")
+
+
+@pytest.mark.parametrize("seq,S", [([1, 3], 2), ([64, 65, 1], 7), ([2000], 1), ([2000], 256)])
+def test_tq_mse3_u3_balanced_few_tiles(seq, S):
+    w = W.custom_decode_workload(343 + len(seq) + S, len(seq), 32, 8, 128, 16, S, seq, 3, "bf16")
+    cache, cen = tq_case(w, *B_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
+    assert_close(got, ref, lse, ref_lse, "seq %s S=%d" % (seq, S))
