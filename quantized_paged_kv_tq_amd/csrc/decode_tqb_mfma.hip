@@ -28,6 +28,8 @@
 // Slot layout (D = 128): bytes [0, 48) key indices (LSB-first 3-bit
 // stream), [48, 50) fp16 norm, [50, 98) value indices, [98, 100) fp16
 // scale, [100, 102) fp16 zero.
+#include <type_traits>
+
 #include "balance.h"
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -116,23 +118,33 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int gw = g - hq0 < 4 ? g - hq0 : 4;
   const int h0 = kvh * g + hq0;
 
-  // multilinear coefficients of the centroid table (uniform); subset S of
-  // bits {b0, b1, b2} is the index mask S in 1..7
-  float al[8];
+  // Coefficients of the centroid table (uniform), for the index bits
+  // b = (b0, b1, b2) as the subset mask S in 0..7:
+  //   al: multilinear (Moebius) form c(b) = sum_S al_S prod_{i in S} b_i;
+  //   ga: Walsh form c(b) = sum_S ga_S (-1)^{popcount(b & S)}.
+  // A table with c[7 - j] = -c[j] (Lloyd-Max tables are) has ga_S = 0 for
+  // every even |S|; then only the planes b0, b1, b2 and b0^b1^b2 are needed:
+  //   q . c[idx] = sum_S ga_S (sum q - 2 q . [popcount(b & S) odd]).
+  float al[8], ga[8];
+  bool anti = true;
   {
     float c[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) c[j] = p.centroids[j];
 #pragma unroll
+    for (int j = 0; j < 8; ++j) anti = anti && (c[7 - j] == -c[j]);
+#pragma unroll
     for (int S = 0; S < 8; ++S) {
-      float a = 0.0f;
+      float a = 0.0f, w = 0.0f;
 #pragma unroll
       for (int T = 0; T < 8; ++T) {
+        w = (__builtin_popcount(T & S) & 1) ? w - c[T] : w + c[T];
         if ((T & S) != T) continue;
         const int sign = __builtin_popcount(S ^ T) & 1;
         a = sign ? a - c[T] : a + c[T];
       }
       al[S] = a;
+      ga[S] = w * 0.125f;
     }
   }
 
@@ -401,12 +413,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       uint32_t ix[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
-      // one bit-plane product at a time: two MFMAs (dims 32g + 16kc + ...),
-      // then its share of the dot product; lane (n, g) holds rows 4g..4g+3
-      // = the digit planes of head g, token 16s+n
-      float dot = al[0] * qsum;
-#pragma unroll
-      for (int S = 1; S < 8; ++S) {
+      // one bit plane at a time: two MFMAs (dims 32g + 16kc + ...), then its
+      // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
+      // digit planes of head g, token 16s+n
+      auto plane_dot = [&](auto sel) -> float {
+        constexpr int S = decltype(sel)::value;  // 1..7: product; 8 + S: parity
         v4i c = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
@@ -414,18 +425,44 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const uint32_t x = ix[4 * kc + j];
-            uint32_t m = 0x01010101u;
-            if (S & 1) m &= x;
-            if (S & 2) m &= x >> 1;
-            if (S & 4) m &= x >> 2;
+            uint32_t m;
+            if constexpr (S < 8) {
+              m = 0x01010101u;
+              if (S & 1) m &= x;
+              if (S & 2) m &= x >> 1;
+              if (S & 4) m &= x >> 2;
+            } else {
+              m = 0;
+              if (S & 1) m ^= x;
+              if (S & 2) m ^= x >> 1;
+              if (S & 4) m ^= x >> 2;
+              m &= 0x01010101u;
+            }
             pl[j] = m;
           }
           c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[kc], v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]},
                                                     c, 0, 0, 0);
         }
-        const float v = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c.w, 128.0f, (float)c.z), 128.0f,
-                                                      (float)c.y), 128.0f, (float)c.x);
-        dot = __builtin_fmaf(al[S], v, dot);
+        return __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c.w, 128.0f, (float)c.z), 128.0f, (float)c.y),
+                              128.0f, (float)c.x);
+      };
+      float dot;
+      if (anti) {
+        // odd Walsh terms: planes b0, b1, b2, b0^b1^b2
+        const float t = plane_dot(std::integral_constant<int, 9>{}) * ga[1] +
+                        plane_dot(std::integral_constant<int, 10>{}) * ga[2] +
+                        plane_dot(std::integral_constant<int, 12>{}) * ga[4] +
+                        plane_dot(std::integral_constant<int, 15>{}) * ga[7];
+        dot = __builtin_fmaf(ga[1] + ga[2] + ga[4] + ga[7], qsum, -2.0f * t);
+      } else {
+        dot = al[0] * qsum;
+        dot = __builtin_fmaf(al[1], plane_dot(std::integral_constant<int, 1>{}), dot);
+        dot = __builtin_fmaf(al[2], plane_dot(std::integral_constant<int, 2>{}), dot);
+        dot = __builtin_fmaf(al[3], plane_dot(std::integral_constant<int, 3>{}), dot);
+        dot = __builtin_fmaf(al[4], plane_dot(std::integral_constant<int, 4>{}), dot);
+        dot = __builtin_fmaf(al[5], plane_dot(std::integral_constant<int, 5>{}), dot);
+        dot = __builtin_fmaf(al[6], plane_dot(std::integral_constant<int, 6>{}), dot);
+        dot = __builtin_fmaf(al[7], plane_dot(std::integral_constant<int, 7>{}), dot);
       }
       const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
       sc[s] = fminf(dot * (qf * nrm), mask);

@@ -300,17 +300,26 @@ def test_tq_mse3_u3_rot_signs_split_invariance_and_degenerate_lengths():
         assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
 
 
-def _random_centroids(seed):
+def _random_centroids(seed, antisymmetric=False):
+    """A sorted random table; ``antisymmetric`` mirrors its upper half so that
+    c[7 - j] == -c[j] holds exactly (the shape of every Lloyd-Max table)."""
     rng = np.random.default_rng(seed)
-    return np.sort(rng.uniform(-0.3, 0.3, 8)).astype(np.float32)
+    c = np.sort(rng.uniform(-0.3, 0.3, 8)).astype(np.float32)
+    if antisymmetric:
+        c[:4] = -c[4:][::-1]
+    return c
 
 
-def test_tq_mse3_u3_random_slot_bytes_and_table():
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+def test_tq_mse3_u3_random_slot_bytes_and_table(antisymmetric):
     """Random slots (no writer) and an arbitrary centroid table: every index
-    pattern, value scales of both signs, random norms and zeros."""
+    pattern, value scales of both signs, random norms and zeros.  The matrix
+    kernel has one score form for any table and a shorter one for tables with
+    c[7 - j] == -c[j]; both are run."""
     w = W.custom_decode_workload(341, 2, 16, 4, 128, 16, 4, [300, 77], 4, "bf16")
     cache = W.random_tq_mse3_u3_cache(w, oracle.tq_slot_bytes(128, *B_FMT))
-    cen = _random_centroids(341)
+    cen = _random_centroids(341, antisymmetric)
+    assert np.array_equal(cen[::-1] == -cen, np.full(8, antisymmetric))
     q = W.query(w) / 4
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
     for flags in (0, tq.FLAG_GENERIC):
