@@ -6,38 +6,125 @@
 // rotated tensors in memory; here each source row is read once, rotated in
 // registers and written straight into the paged cache.
 //
-// Lane layout: a row of D elements is spread over D/16 consecutive lanes;
-// lane l holds elements 8l .. 8l+7 and D/2 + 8l .. D/2 + 8l + 7, so that each
-// of its two 16-byte loads (bf16) is part of one contiguous 128-byte span per
-// row. Butterfly strides 1, 2, 4 run inside each half of the lane, strides
-// 8 .. D/4 pair lanes whose index differs by stride/8 (DPP moves), and
-// stride D/2 pairs the two halves inside the lane: strides run 1 -> D/2, the
-// order that fixes the fp32 rounding. A lane packs its codes into two
-// 4-byte words (bytes 4l and D/4 + 4l of the packed row); neighbouring
-// lanes swap one word so that each stores 8 contiguous bytes.
+// Lane layout (write_rows.h, pair layout): two lanes per row; lane q holds
+// the 8-element chunks 2m + q. The RHT sign flips are XOR masks on the
+// packed 16-bit source words (from LDS), fused with unpacking and the
+// stride-1 butterflies; the stride-8 butterflies cross the lane pair as one
+// DPP fused multiply-add per element, which leaves lane 1 with the negated
+// transform. The negation is folded into the row's min / max and into the
+// quantizer's reciprocal (sign flips are exact), so the codes are those of
+// the plain transform. Each lane packs its 8 chunks into 8 words (word c of
+// the packed row is chunk c); one word exchange per pair of words gives lane
+// 0 the first and lane 1 the second half of the packed row.
 //
-// Bit exactness: compiled without fp contraction; the one fused multiply-add
-// of the quantizer is explicit, division and reciprocal are IEEE.
+// Bit exactness: the FWHT strides run 1 -> D/2 in fp32 with one rounding per
+// butterfly, as the pages' transform; the file is compiled without fp
+// contraction; the one fused multiply-add of the quantizer is explicit;
+// division and reciprocal are IEEE.
 #include "tq_device.h"
 #include "tq_internal.h"
 #include "write_rows.h"
 
 namespace tqk {
 
-// Quantize one rotated row (two 8-element halves per lane) and store the
-// lane's two packed words and the scale word.
-template <int D, int LPR>
-__device__ __forceinline__ void quantize_store(const float x[16], int li, bool valid,
-                                               uint8_t* __restrict__ cache_row,
-                                               float* __restrict__ word_out) {
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int j = 1; j < 16; ++j) {
-    mn = fminf(mn, x[j]);
-    mx = fmaxf(mx, x[j]);
+namespace {
+
+// One workgroup of 256 lanes handles 128 rows; row r is (item = r / 2, K if
+// r even else V), item = t * Hk + h.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void reshape_int4_kernel(
+    const void* __restrict__ key, const void* __restrict__ value,
+    const int64_t* __restrict__ slots, const float* __restrict__ signs,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, int64_t total_rows, int hk, int64_t cache_slots) {
+  constexpr int M = D / 16;  // chunks per lane
+  constexpr int NE = D / 2;  // elements per lane
+  constexpr bool kHalf = DT == TQ_DT_BF16 || DT == TQ_DT_F16;
+  // RHT signs: XOR masks of the packed 16-bit pairs, or the fp32 signs
+  __shared__ __attribute__((aligned(16))) uint32_t smask[kHalf ? D / 2 : D];
+  if (threadIdx.x < (kHalf ? D / 2 : D)) {
+    if constexpr (kHalf) {
+      const float2 sp = reinterpret_cast<const float2*>(signs)[threadIdx.x];
+      smask[threadIdx.x] = (sp.x < 0.0f ? 0x8000u : 0u) | (sp.y < 0.0f ? 0x80000000u : 0u);
+    } else {
+      smask[threadIdx.x] = f2u(signs[threadIdx.x]);
+    }
   }
-  mn = group16_min<LPR>(mn);
-  mx = group16_max<LPR>(mx);
+
+  const int q = threadIdx.x & 1;
+  const int64_t row = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 1);
+  const bool in_range = row < total_rows;
+  const int64_t item = in_range ? (row >> 1) : 0;
+  const bool is_v = row & 1;
+  // token and head of the item (32-bit division: items < 2^31)
+  const uint32_t it32 = (uint32_t)item;
+  const uint32_t t = it32 / (uint32_t)hk;
+  const int head = (int)(it32 - t * (uint32_t)hk);
+  // the source row is loaded without waiting for the slot (a skipped row's
+  // values are read and discarded)
+  const int64_t slot = in_range ? slots[t] : -1;
+  const char* src = static_cast<const char*>(is_v ? value : key);
+  constexpr int ES = kHalf ? 2 : 4;  // source element bytes
+  uint4 raw[M][kHalf ? 1 : 2];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint4* p = reinterpret_cast<const uint4*>(src + (item * D + 8 * (2 * m + q)) * ES);
+    raw[m][0] = p[0];
+    if constexpr (!kHalf) raw[m][1] = p[1];
+  }
+  __syncthreads();  // smask
+
+  // signs, unpacking and the stride-1 butterflies
+  float x[NE];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = 2 * m + q;
+    if constexpr (kHalf) {
+      const uint4 mk = *reinterpret_cast<const uint4*>(&smask[4 * c]);
+      const uint32_t w[4] = {raw[m][0].x ^ mk.x, raw[m][0].y ^ mk.y, raw[m][0].z ^ mk.z, raw[m][0].w ^ mk.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = DT == TQ_DT_BF16 ? bf16_lo(w[k]) : half_lo(w[k]);
+        const float b = DT == TQ_DT_BF16 ? bf16_hi(w[k]) : half_hi(w[k]);
+        x[8 * m + 2 * k] = a + b;
+        x[8 * m + 2 * k + 1] = a - b;
+      }
+    } else {
+      const uint4 s0 = *reinterpret_cast<const uint4*>(&smask[8 * c]);
+      const uint4 s1 = *reinterpret_cast<const uint4*>(&smask[8 * c + 4]);
+      const uint32_t w[8] = {raw[m][0].x, raw[m][0].y, raw[m][0].z, raw[m][0].w,
+                             raw[m][1].x, raw[m][1].y, raw[m][1].z, raw[m][1].w};
+      const uint32_t sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = u2f(w[2 * k]) * u2f(sg[2 * k]);
+        const float b = u2f(w[2 * k + 1]) * u2f(sg[2 * k + 1]);
+        x[8 * m + 2 * k] = a + b;
+        x[8 * m + 2 * k + 1] = a - b;
+      }
+    }
+  }
+  fwht_pair_from_stride2<D>(x, q);  // lane 1 now holds the negated values
+
+  // the source dtype's rounding of the rotated row (symmetric in sign)
+  if constexpr (DT == TQ_DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < NE; i += 2) round2_bf16(x[i], x[i + 1]);
+  } else if constexpr (DT == TQ_DT_F16) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) x[i] = round_to_f16(x[i]);
+  }
+
+  // row minimum and maximum of the true values
+  float hmn = x[0], hmx = x[0];
+#pragma unroll
+  for (int i = 1; i < NE; ++i) {
+    hmn = fminf(hmn, x[i]);
+    hmx = fmaxf(hmx, x[i]);
+  }
+  float mn = q ? -hmx : hmn, mx = q ? -hmn : hmx;
+  mn = fminf(mn, dpp_xor<1>(mn));
+  mx = fmaxf(mx, dpp_xor<1>(mx));
   float scale = (mx - mn) / 15.0f;
   scale = (scale > 1e-6f) ? scale : 1e-6f;
   // The page rounds half away from zero and clamps to [0, 15]; for a
@@ -46,105 +133,50 @@ __device__ __forceinline__ void quantize_store(const float x[16], int li, bool v
   const float u = -mn / scale;
   const float zp = __builtin_truncf(__builtin_amdgcn_fmed3f(u + 0.5f, 0.0f, 15.0f));
   const float inv = 1.0f / scale;
-  uint32_t packed[2] = {0, 0};
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float t = __builtin_fmaf(x[j], inv, zp);
-    const uint32_t q = (uint32_t)__builtin_amdgcn_fmed3f(t + 0.5f, 0.0f, 15.0f);
-    packed[j >> 3] |= q << (4 * (j & 7));
-  }
-  // Lanes 2m and 2m+1 hold bytes 8m..8m+7 of the first half as packed[0]
-  // and of the second half as packed[1]; swapping one word gives lane 2m
-  // the first-half 8 bytes and lane 2m+1 the second-half 8 bytes, stored
-  // with one 8-byte store each.
-  const bool odd = li & 1;
-  const uint32_t give = odd ? packed[0] : packed[1];
-  const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, 0xB1, 0xF, 0xF, false);
-  const uint2 out = odd ? make_uint2(got, packed[1]) : make_uint2(packed[0], got);
-  if (valid) {
-    *reinterpret_cast<uint2*>(cache_row + (odd ? D / 4 : 0) + 8 * (li >> 1)) = out;
-    if (li == 0) *word_out = u2f((f2u(scale) & 0xFFFFFFF0u) | (uint32_t)zp);
-  }
-}
+  const float invs = q ? -inv : inv;  // x * invs = (true value) * inv exactly
 
-// One workgroup of 256 lanes handles R passes of 256 / (D/16) rows; row r
-// is (item = r / 2, K if r even else V), item = t * Hk + h. Every pass's
-// loads are issued before the first row is transformed.
-template <int D, int DT, int R>
-__global__ __launch_bounds__(256) void reshape_int4_kernel(
-    const void* __restrict__ key, const void* __restrict__ value,
-    const int64_t* __restrict__ slots, const float* __restrict__ signs,
-    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
-    float* __restrict__ vs, int64_t total_rows, int hk, int64_t cache_slots) {
-  constexpr int LPR = D / 16;
-  constexpr int ROWS = 256 / LPR;
-  const int li = threadIdx.x % LPR;
-  float sg[3];
+  uint32_t d[M];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
-
-  // The source rows are loaded without waiting for their slots (a skipped
-  // row's values are read and discarded), so both loads are in flight
-  // together.
-  float x[R][16];
-  int64_t slot[R], dst[R];
-  int head[R];
-  bool valid[R], is_v[R];
+  for (int m = 0; m < M; ++m) {
+    d[m] = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t row = ((int64_t)blockIdx.x * R + r) * ROWS + threadIdx.x / LPR;
-    const bool in_range = row < total_rows;
-    const int64_t item = in_range ? (row >> 1) : 0;
-    is_v[r] = row & 1;
-    // token and head of the item (32-bit division: items < 2^31)
-    const uint32_t it32 = (uint32_t)item;
-    const int64_t t = (int64_t)(it32 / (uint32_t)hk);
-    head[r] = (int)(it32 - (uint32_t)t * (uint32_t)hk);
-    slot[r] = in_range ? slots[t] : -1;
-    const void* src = is_v[r] ? value : key;
-    load8<DT>(src, item * D + li * 8, x[r]);
-    load8<DT>(src, item * D + D / 2 + li * 8, x[r] + 8);
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    valid[r] = slot[r] >= 0 && slot[r] < cache_slots;
-    dst[r] = (valid[r] ? slot[r] : 0) * hk + head[r];
-  }
-  float s[16];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const float4* sp = reinterpret_cast<const float4*>(signs + hf * (D / 2) + li * 8);
-    const float4 a = sp[0], b = sp[1];
-    s[8 * hf + 0] = a.x; s[8 * hf + 1] = a.y; s[8 * hf + 2] = a.z; s[8 * hf + 3] = a.w;
-    s[8 * hf + 4] = b.x; s[8 * hf + 5] = b.y; s[8 * hf + 6] = b.z; s[8 * hf + 7] = b.w;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[r][j] *= s[j];
-    fwht_row<LPR>(x[r], sg);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if constexpr (DT == TQ_DT_BF16) x[r][j] = round_to_bf16_hw(x[r][j]);
-      else if constexpr (DT == TQ_DT_F16) x[r][j] = round_to_f16(x[r][j]);
+    for (int j = 0; j < 8; ++j) {
+      const float tq = __builtin_fmaf(x[8 * m + j], invs, zp);
+      const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(tq + 0.5f, 0.0f, 15.0f);
+      d[m] |= code << (4 * j);
     }
-    uint8_t* cache = is_v[r] ? vc : kc;
-    float* words = is_v[r] ? vs : ks;
-    quantize_store<D, LPR>(x[r], li, valid[r], cache + dst[r] * (D / 2), words + dst[r]);
+  }
+  // word c = 2m + q of the packed row is d[m]; lane 0 stores words
+  // 0 .. M-1, lane 1 words M .. 2M-1
+  constexpr int H = M / 2;
+  uint32_t out[M];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const uint32_t send = q ? d[k] : d[H + k];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    out[2 * k] = q ? recv : d[k];
+    out[2 * k + 1] = q ? d[H + k] : recv;
+  }
+  if (slot >= 0 && slot < cache_slots) {
+    const int64_t dst = slot * hk + head;
+    uint2* o = reinterpret_cast<uint2*>((is_v ? vc : kc) + dst * (D / 2) + 4 * M * q);
+#pragma unroll
+    for (int k = 0; k < H; ++k) o[k] = make_uint2(out[2 * k], out[2 * k + 1]);
+    if (q == 0) (is_v ? vs : ks)[dst] = u2f((f2u(scale) & 0xFFFFFFF0u) | (uint32_t)zp);
   }
 }
 
 template <int D, int DT>
-static hipError_t launch_reshape(const ReshapeParams& p, hipStream_t st) {
-  constexpr int R = 2;
-  constexpr int ROWS = 256 / (D / 16);
+hipError_t launch_reshape(const ReshapeParams& p, hipStream_t st) {
   const int64_t total_rows = p.num_tokens * p.hk * 2;
-  const int64_t blocks = (total_rows + ROWS * R - 1) / (ROWS * R);
-  hipLaunchKernelGGL((reshape_int4_kernel<D, DT, R>), dim3((uint32_t)blocks), dim3(256), 0, st,
+  const int64_t blocks = (total_rows + 127) / 128;
+  hipLaunchKernelGGL((reshape_int4_kernel<D, DT>), dim3((uint32_t)blocks), dim3(256), 0, st,
                      p.key, p.value, p.slots, p.signs, p.kc, p.vc, p.ks, p.vs, total_rows,
                      p.hk, p.num_blocks * (int64_t)p.block_size);
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_reshape_int4(const ReshapeParams& p, hipStream_t st) {
   if (p.d == 128) {

@@ -67,4 +67,76 @@ __device__ __forceinline__ void fwht_row(float x[16], const float sg[3]) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pair layout: a row of D elements over two adjacent lanes. Lane q = lane & 1
+// holds the 8-element chunks c = 2m + q (m = 0 .. D/16 - 1) as
+// x[8m + j] = element 8c + j, so element e = 16m + 8q + j: FWHT strides 1, 2,
+// 4 pair elements inside a chunk, stride 8 pairs the two lanes, and strides
+// 16 .. D/2 pair chunks m and m ^ (stride / 16) inside the lane. The two
+// lanes of a row read its 32-byte spans together (bf16), and a row costs one
+// lane exchange per element instead of three.
+
+// x[i] += (x[i] of lane ^ 1) * s for eight values: one v_fmac_f32 with a DPP
+// operand each. With s = +1 in lane 0 and -1 in lane 1 this is the stride-8
+// butterfly, except that lane 1 receives the negated difference x1 - x0
+// (exact: sign flips commute with rounding). Every lane of the wave must be
+// active. The s_nop covers the wait states a DPP read needs after a VALU
+// write of its operand or of EXEC.
+__device__ __forceinline__ void fmac_partner8(float* x, float s) {
+  asm("s_nop 4\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+      : "v"(s));
+}
+
+// In-place butterfly (a, b) -> (a + b, a - b).
+__device__ __forceinline__ void bfly(float& a, float& b) {
+  const float u = a + b, v = a - b;
+  a = u;
+  b = v;
+}
+
+// FWHT over the pair layout from the state after stride 1 (the writers fuse
+// that stage with unpacking). On return lane 0 holds FWHT(row) at its
+// elements and lane 1 holds -FWHT(row) at its elements (sigma = +1 / -1).
+template <int D>
+__device__ __forceinline__ void fwht_pair_from_stride2(float (&x)[D / 2], int q) {
+  constexpr int M = D / 16;
+#pragma unroll
+  for (int h = 2; h < 8; h <<= 1)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((j & h) == 0) bfly(x[8 * m + j], x[8 * m + j + h]);
+  const float s = q ? -1.0f : 1.0f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) fmac_partner8(x + 8 * m, s);
+#pragma unroll
+  for (int hm = 1; hm < M; hm <<= 1)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if ((m & hm) == 0)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bfly(x[8 * m + j], x[8 * (m + hm) + j]);
+}
+
+// Round a pair of fp32 values to bfloat16 (nearest even) and back, with one
+// packed convert.
+__device__ __forceinline__ void round2_bf16(float& a, float& b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  a = u2f(u << 16);
+  b = u2f(u & 0xFFFF0000u);
+}
+
 }  // namespace tqk
