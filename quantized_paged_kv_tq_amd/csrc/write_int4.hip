@@ -13,7 +13,8 @@
 // DPP fused multiply-add per element, which leaves lane 1 with the negated
 // transform. The negation is folded into the row's min / max and into the
 // quantizer's reciprocal (sign flips are exact), so the codes are those of
-// the plain transform. Each lane packs its 8 chunks into 8 words (word c of
+// the plain transform (the sign of an exact zero, which the negation does
+// not carry, changes no code and no scale word). Each lane packs its 8 chunks into 8 words (word c of
 // the packed row is chunk c); one word exchange per pair of words gives lane
 // 0 the first and lane 1 the second half of the packed row.
 //

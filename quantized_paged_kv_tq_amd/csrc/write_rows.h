@@ -105,7 +105,9 @@ __device__ __forceinline__ void bfly(float& a, float& b) {
 
 // FWHT over the pair layout from the state after stride 1 (the writers fuse
 // that stage with unpacking). On return lane 0 holds FWHT(row) at its
-// elements and lane 1 holds -FWHT(row) at its elements (sigma = +1 / -1).
+// elements and lane 1 holds -FWHT(row) at its elements (sigma = +1 / -1),
+// except for the sign of exact zeros: a zero difference is +0 whichever way
+// round it is taken, so a consumer must not depend on the sign of a zero.
 template <int D>
 __device__ __forceinline__ void fwht_pair_from_stride2(float (&x)[D / 2], int q) {
   constexpr int M = D / 16;
