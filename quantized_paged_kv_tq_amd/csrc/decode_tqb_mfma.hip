@@ -46,8 +46,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kChunk = 64;  // tiles resolved into LDS at a time
 constexpr int kTau = 4;     // headroom of the value-weight fixed point
-constexpr uint32_t kMasked = 0xFFFFFFFFu;
-constexpr uint32_t kMaskedByte = 0xFFFFFF00u;  // byte offset past any buffer
+// Byte offset of a masked token's slot: at or past 2^31, beyond every
+// buffer (cache sizes stay below 2^31 bytes), so its loads read zeros even
+// after a kv head's offset and a field offset are added.
+constexpr uint32_t kMaskedByte = 0x80000000u;
 constexpr int kFirstOfSplit = 1;
 constexpr int kLastOfSplit = 2;
 // slot offsets
@@ -96,6 +98,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   constexpr int NT = 64 * W;
   __shared__ __attribute__((aligned(16))) uint32_t p8[W][4][4][16];  // weight digit planes
   __shared__ __attribute__((aligned(16))) uint32_t qimg[W][2][64][4];  // query digit image
+  // byte offset of kv head 0's slot of each token of the chunk's tiles
+  // (kMaskedByte for masked tokens and the prefetch row past the end)
   __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
@@ -212,10 +216,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     uint32_t nw, sz0, sz1, live;
     uint32_t vraw[4][4];
   };
-  auto slot_of = [&](int k, int j) -> uint32_t {
-    const uint32_t r = tok_rows[k][j];
-    return r == kMasked ? kMaskedByte : (r + (uint32_t)kvh) * sb;
-  };
+  const uint32_t kvh_off = (uint32_t)kvh * sb;
+  auto slot_of = [&](int k, int j) -> uint32_t { return tok_rows[k][j] + kvh_off; };
   // keys and per-token words first; the value windows after the current
   // tile's scores (issue_v), which keeps both tiles' values from being live
   // through the score computation
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint32_t o = slot_of(k, 16 * s + ln);
-      B.live |= (o != kMaskedByte ? 1u : 0u) << s;
+      B.live |= (o < kMaskedByte ? 1u : 0u) << s;
 #pragma unroll
       for (int i = 0; i < 3; ++i)
         B.kraw[s][i] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + 12u * lg + 4u * i), 0, 0);
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int e = tid; e < (K + 1) * 64; e += NT) {
       const int k = e >> 6, j = e & 63;
       if (k == K) {
-        tok_rows[k][j] = kMasked;
+        tok_rows[k][j] = kMaskedByte;
         continue;
       }
       const int x = c0 + k;
@@ -603,13 +605,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       if (end > q.seq) end = q.seq;
       if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
       const int tok = tok0 + j;
-      uint32_t row = kMasked;
+      uint32_t row = kMaskedByte;
       if (tok < end) {
         const uint32_t t32 = (uint32_t)tok;
         const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
         const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
         if (page >= 0 && page < p.num_blocks)
-          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
+          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk * sb;
       }
       tok_rows[k][j] = row;
       if (j == 0) {
