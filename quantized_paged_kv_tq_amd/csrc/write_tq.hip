@@ -58,11 +58,56 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// Decision thresholds of the nearest-centroid search. For a table with
+// c[j] < c[j+1], |c[j]| <= 1 and gaps of at least 2^-20, and |u| <= ~1 (u is
+// a coordinate of a unit vector, up to rounding): the fp32 distances to two
+// centroids on the same side of u differ by more than their rounding, so
+// only the two centroids around u can be nearest, and between c[j] and
+// c[j+1] the choice "c[j+1] strictly nearer" is monotone in u (one
+// difference rounds up, the other down, as u grows). Hence the index is the
+// number of thresholds T[j] <= u, with T[j] the least fp32 u in
+// [c[j], c[j+1]] for which |u - c[j+1]| < |u - c[j]| in fp32, the same
+// comparison, ties to the lower index, as a full scan. T[j] is found by
+// bisection over the fp32 values of that interval (ordered as integers).
+template <int NC>
+__device__ __forceinline__ bool centroid_thresholds(const float (&cen)[NC], const float* centroids,
+                                                    float (&thr)[NC - 1]) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) ok = ok && fabsf(cen[j]) <= 1.0f;
+#pragma unroll
+  for (int j = 0; j + 1 < NC; ++j) ok = ok && cen[j] < cen[j + 1] && cen[j + 1] - cen[j] >= 0x1p-20f;
+  if (!ok) return false;  // uniform
+  // lane j < NC - 1 bisects interval j
+  const int lane = threadIdx.x & 63;
+  const int j = lane < NC - 1 ? lane : NC - 2;
+  const float a = centroids[j], b = centroids[j + 1];
+  auto key = [](float f) -> uint32_t {
+    const uint32_t u = f2u(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  auto unkey = [](uint32_t k) -> float { return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k); };
+  uint32_t lo = key(a), hi = key(b);  // "b strictly nearer": false at a, true at b
+  for (int it = 0; it < 32; ++it) {
+    if (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      const float u = unkey(mid);
+      if (fabsf(u - b) < fabsf(u - a)) hi = mid;
+      else lo = mid;
+    }
+  }
+  const float t = unkey(hi);
+#pragma unroll
+  for (int k = 0; k + 1 < NC; ++k) thr[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), k));
+  return true;
+}
+
 // Centroid key of one row (D/16 lanes, 16 elements per lane): norm by
 // pairwise sums with strides 1 -> D/2, rotation, nearest centroid, packing.
 template <int D, int KB>
 __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* s, int li,
-                                                    const float (&cen)[1 << KB],
+                                                    const float (&cen)[1 << KB], bool fast,
+                                                    const float (&thr)[(1 << KB) - 1],
                                                     const float* rot_signs, int kps,
                                                     const float sg[3]) {
   constexpr int LPR = D / 16;
@@ -104,20 +149,31 @@ __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* 
   const float rs = D == 128 ? 0.0883883461356163f : 0.125f;  // fp32 1/sqrt(D)
   const float wn = nrm > 0.0f ? rs / nrm : 0.0f;
   uint32_t q[16];
+  if (fast) {  // uniform
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float u = y[j] * wn;
-    uint32_t best = 0;
-    float bd = fabsf(u - cen[0]);
+    for (int j = 0; j < 16; ++j) {
+      const float u = y[j] * wn;
+      uint32_t n = 0;
 #pragma unroll
-    for (int c = 1; c < (1 << KB); ++c) {
-      const float dc = fabsf(u - cen[c]);
-      if (dc < bd) {
-        bd = dc;
-        best = (uint32_t)c;
-      }
+      for (int c = 0; c + 1 < (1 << KB); ++c) n += u >= thr[c] ? 1u : 0u;
+      q[j] = n;
     }
-    q[j] = best;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float u = y[j] * wn;
+      uint32_t best = 0;
+      float bd = fabsf(u - cen[0]);
+#pragma unroll
+      for (int c = 1; c < (1 << KB); ++c) {
+        const float dc = fabsf(u - cen[c]);
+        if (dc < bd) {
+          bd = dc;
+          best = (uint32_t)c;
+        }
+      }
+      q[j] = best;
+    }
   }
   store_bytes(s + KB * li, pack8(q, KB), KB);
   store_bytes(s + KB * (D / 16) + KB * li, pack8(q + 8, KB), KB);
@@ -138,6 +194,12 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
   const int wave = threadIdx.x >> 6;
   const bool values = wave & 1;  // wave-uniform
   const int it_in = (wave >> 1) * (64 / LPR) + (threadIdx.x & 63) / LPR;
+  // key waves of a centroid format: decision thresholds of the table
+  float thr[NC > 1 ? NC - 1 : 1];
+  bool fast = false;
+  if constexpr (KB != 8) {
+    if (!values) fast = centroid_thresholds<NC>(cen, a.centroids, thr);
+  }
   float sg[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
@@ -181,7 +243,7 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
         *reinterpret_cast<uint2*>(s + D / 2 + 8 * li) = make_uint2(w[2], w[3]);
         continue;
       } else {
-        encode_centroid_key<D, KB>(v, s, li, cen, a.rot_signs, a.kps, sg);
+        encode_centroid_key<D, KB>(v, s, li, cen, fast, thr, a.rot_signs, a.kps, sg);
         continue;
       }
     }

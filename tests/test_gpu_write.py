@@ -131,10 +131,11 @@ def _centroids(key_fmt, d):
 
 
 def _encode_both(kb, vb, dtype, slots, nb, bs, hk, d, key_fmt, val_fmt, rot_signs=None,
-                 extra_pad=0):
+                 extra_pad=0, cen=None):
     import quantized_paged_kv_tq_amd as tq
     sb = oracle.tq_slot_bytes(d, key_fmt, val_fmt) + extra_pad
-    cen = _centroids(key_fmt, d)
+    if cen is None:
+        cen = _centroids(key_fmt, d)
     want = np.full((nb, bs, hk, sb), 0xA5, np.uint8)  # canary: skipped slots keep it
     got = to_dev(want)
     k32 = W.bits_to_f32(kb, dtype)
@@ -186,3 +187,41 @@ def test_tq_encode_special_rows(fmt):
     slots[10] = -1
     slots[11] = 10 ** 6  # beyond the cache: skipped
     _encode_both(k, v, "f32", slots, 4, 16, hk, d, *fmt)
+
+
+def _table_cases(d):
+    """Centroid tables for the nearest-centroid search: the writer takes
+    decision thresholds for sorted tables with gaps >= 2^-20 inside [-1, 1]
+    and scans every centroid otherwise."""
+    lm = (oracle.lloyd_max_gaussian(8) / np.sqrt(d)).astype(np.float32)
+    rs = np.float32(1.0 / np.sqrt(d))
+    # c[4] and c[5] straddle rs = u of a one-hot key exactly: a tie, which
+    # goes to the lower index
+    tie = lm.copy()
+    tie[4], tie[5] = rs - np.float32(0.03125), rs + np.float32(0.03125)
+    tie[6], tie[7] = np.float32(0.25), np.float32(0.5)
+    near = lm.copy()
+    near[5] = np.nextafter(near[4], np.float32(1))  # gap of one ulp: scanned
+    big = lm.copy()
+    big[7] = np.float32(1.5)  # beyond [-1, 1]: scanned
+    perm = lm[[3, 0, 7, 1, 6, 2, 5, 4]].copy()  # unsorted: scanned
+    return {"lloyd_max": lm, "tie": tie, "near_duplicate": near, "outside_unit": big,
+            "unsorted": perm}
+
+
+@pytest.mark.parametrize("case", ["lloyd_max", "tie", "near_duplicate", "outside_unit", "unsorted"])
+def test_tq_encode_centroid_tables(case):
+    """Threshold and scan forms of the nearest-centroid search against the
+    oracle's scan: random rows, one-hot rows (every coordinate of u is
+    +-1/sqrt(D) exactly) and rows of one repeated value."""
+    d, hk, T = 128, 2, 96
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((T, hk, d)).astype(np.float32)
+    for t in range(0, 32):
+        k[t] = 0.0
+        k[t, :, t % d] = np.float32(2.0 ** (t % 3 - 1))  # u = +-1/sqrt(D) exactly
+    k[32:40] = np.float32(0.75)
+    v = rng.standard_normal((T, hk, d)).astype(np.float32)
+    slots = rng.permutation(T).astype(np.int64)
+    cen = _table_cases(d)[case]
+    _encode_both(k, v, "f32", slots, 6, 16, hk, d, oracle.KEY_MSE3, oracle.VAL_U3, cen=cen)
