@@ -101,17 +101,24 @@ constexpr int kTau = 4;
 constexpr int kFirstOfSplit = 1;
 constexpr int kLastOfSplit = 2;
 
-template <int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_int4_mfma_kernel(DecodeParams p) {
-  constexpr int NH = 1;          // MFMA row sets of four query heads per wave
+// NH: MFMA row sets of four query heads per wave (a wave serves 4 * NH query
+// heads of one kv head). DEPTH register sets form a ring: the loads of tile
+// k + DEPTH - 1 are issued at the top of tile k. The launcher uses NH = 1 and
+// DEPTH = 2 with two waves per SIMD: one wave per SIMD with NH = 2 (all of
+// a kv head's query heads) and rings of 3 or 4 measured slower, the second
+// wave on a SIMD hiding the first one's MFMA, LDS and DPP latencies.
+template <int W, int NH, int DEPTH>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DEPTH == 2 ? 2 : 1)))
+void decode_int4_mfma_kernel(DecodeParams p) {
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
   constexpr int NT = 64 * W;
   // per wave: MFMA A-operand image of its queries (query set-up), then the
   // per-tile weight digit planes
   __shared__ __attribute__((aligned(16))) uint32_t wbuf[W][NH][2][64][4];
-  // (page * bs + offset) * Hk of each token of the chunk's tiles; the row
-  // after the chunk's last tile is all masked (the prefetch past the end)
-  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
+  // (page * bs + offset) * Hk of each token of the chunk's tiles; the
+  // DEPTH - 1 rows after the chunk's last tile are all masked (the prefetch
+  // past the end)
+  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + DEPTH - 1][64];
   __shared__ int4 tinfo[kChunk];  // (b, s, flags, -) per tile of the chunk
   __shared__ int scan[W];
   // fp32 accumulators of the wave's heads, lane-major (touched only when
@@ -127,13 +134,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int grp = blockIdx.x / p.nw;
   const int wg = blockIdx.x - grp * p.nw;
   // wave -> (kv head, sub-group of four of its query heads)
-  const int qs_n = (p.g + 3) >> 2;  // sub-groups per kv head
+  const int qs_n = (p.g + NHEAD - 1) / NHEAD;  // sub-groups per kv head
   const int kvl = wave / qs_n;      // kv head within the workgroup
   const int qsub = wave - kvl * qs_n;
   const int kvh = grp * p.wgh + kvl;
   const int g = p.g;
-  const int hq0 = 4 * qsub;               // first query head of this wave within its kv head
-  const int gw = g - hq0 < 4 ? g - hq0 : 4;  // query heads of this wave
+  const int hq0 = NHEAD * qsub;                      // first query head of this wave within its kv head
+  const int gw = g - hq0 < NHEAD ? g - hq0 : NHEAD;  // query heads of this wave
   const int h0 = kvh * g + hq0;
 
   // ---- tile counts of all sequences and their prefix sums ----
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint32_t r = tok_rows[k][j];
     return r == kMasked ? kMasked : r + (uint32_t)kvh;
   };
-  auto issue = [&](Buf& B, int k) {  // k <= K: the table row K is masked
+  auto issue = [&](Buf& B, int k) {  // k < K + DEPTH - 1: rows from K on are masked
     B.live = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -417,7 +424,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       seg_first = gk == lo;
     }
     seg_to_end = (info.z & kLastOfSplit) != 0;
-    issue(Y, k + 1);
+    issue(Y, k + DEPTH - 1);
 
     // scale words of tokens 16s+n from lane 16s+n
     uint32_t ksw[4], vsw[4];
@@ -563,14 +570,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     wave_sync();  // the digit planes are rewritten by the next tile
   };
 
-  Buf A, Bb;
+  Buf ring[DEPTH];
   for (int c0 = lo; c0 < hi; c0 += kChunk) {
     const int K = hi - c0 < kChunk ? hi - c0 : kChunk;  // tiles of this chunk
     __syncthreads();  // the previous chunk's table is no longer read
     // ---- resolve the chunk's tiles to cache rows ----
-    for (int e = tid; e < (K + 1) * 64; e += NT) {
+    for (int e = tid; e < (K + DEPTH - 1) * 64; e += NT) {
       const int k = e >> 6, j = e & 63;  // k is the same across a wave
-      if (k == K) {
+      if (k >= K) {
         tok_rows[k][j] = kMasked;
         continue;
       }
@@ -609,21 +616,25 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     __syncthreads();
 
-    issue(A, 0);  // the first tile's loads overlap the query set-up
-    for (int k = 0; k < K; k += 2) {
-      process(A, Bb, k, c0);
-      if (k + 1 >= K) break;
-      process(Bb, A, k + 1, c0);
+    // the first tiles' loads overlap the query set-up
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) issue(ring[u], u);
+    for (int k = 0; k < K; k += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        if (k + u >= K) break;
+        process(ring[u], ring[(u + DEPTH - 1) % DEPTH], k + u, c0);
+      }
     }
   }
   emit();
 }
 
-template <int W>
+template <int W, int NH, int DEPTH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = (size_t)(p.B + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_int4_mfma_kernel<W>), dim3(blocks), dim3(64 * W), lds, st, p);
+  hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -645,10 +656,10 @@ hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1>(p, st);
-    case 2: return launch<2>(p, st);
-    case 4: return launch<4>(p, st);
-    default: return launch<8>(p, st);
+    case 1: return launch<1, 1, 2>(p, st);
+    case 2: return launch<2, 1, 2>(p, st);
+    case 4: return launch<4, 1, 2>(p, st);
+    default: return launch<8, 1, 2>(p, st);
   }
 }
 
