@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     wave_sync();
   };
 
-  Buf A, Bb;
+  Buf ring[2];
   for (int c0 = lo; c0 < hi; c0 += kChunk) {
     const int K = hi - c0 < kChunk ? hi - c0 : kChunk;
     __syncthreads();
@@ -475,11 +475,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       }
     }
     __syncthreads();
-    issue(A, 0);
+    issue(ring[0], 0);
+    // the two register sets as a ring indexed by the unrolled position (the
+    // compiler keeps them apart without copies or spills)
     for (int k = 0; k < K; k += 2) {
-      process(A, Bb, k, c0);
-      if (k + 1 >= K) break;
-      process(Bb, A, k + 1, c0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (k + u >= K) break;
+        process(ring[u], ring[u ^ 1], k + u, c0);
+      }
     }
   }
   emit();
