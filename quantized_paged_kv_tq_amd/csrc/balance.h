@@ -67,18 +67,20 @@ __device__ __forceinline__ int range_owner(int x, int N, int nw) {
 }
 
 // Kv heads per workgroup and workgroups per kv-head group of the balanced
-// layout (host side; the piece region is sized by the same rule). A wave
+// layout (host side; the piece region is sized by the default rule). A wave
 // serves four query heads of one kv head, so a kv head with g query heads
-// takes ceil(g / 4) waves; a workgroup has at most 8 waves.
-inline int balance_heads_per_wg(int hk, int g) {
+// takes ceil(g / 4) waves (a layout whose waves serve all of a kv head's
+// query heads passes g = 4); a workgroup has at most max_waves waves and
+// the grid at most `budget`.
+inline int balance_heads_per_wg(int hk, int g, int max_waves = 8) {
   const int qs = (g + 3) / 4;
   int w = 1;
-  while (w * 2 * qs <= 8 && hk % (w * 2) == 0) w *= 2;
+  while (w * 2 * qs <= max_waves && hk % (w * 2) == 0) w *= 2;
   return w;
 }
-inline int balance_max_wgs(int hk, int g) {
+inline int balance_max_wgs(int hk, int g, int budget = kWaveBudget) {
   const int qs = (g + 3) / 4;
-  const int n = kWaveBudget / (hk * qs);
+  const int n = budget / (hk * qs);
   return n < 1 ? 1 : n;
 }
 

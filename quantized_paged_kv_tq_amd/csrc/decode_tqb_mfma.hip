@@ -23,7 +23,11 @@
 //
 // Work decomposition, tile table, pieces and ping-pong register sets follow
 // the INT4 path (balance.h): equal ranges of the global 64-token tile list,
-// one wave per four query heads of a kv head.
+// one wave per four query heads of a kv head for g <= 4. For g = 5 .. 8 one
+// wave serves all query heads of its kv head (two MFMA row sets), so the
+// unpacking of each tile's 3-bit keys and values, which bounds this kernel,
+// is done once per kv head instead of by two waves; that wave needs more
+// than 256 registers and runs alone on its SIMD.
 //
 // Slot layout (D = 128): bytes [0, 48) key indices (LSB-first 3-bit
 // stream), [48, 50) fp16 norm, [50, 98) value indices, [98, 100) fp16
@@ -93,17 +97,23 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
   return __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)sh);
 }
 
-template <int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_tqb_kernel(DecodeParams p) {
+// NH: MFMA row sets of four query heads per wave; the bit planes and value
+// operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
+// (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
+// runs one wave per SIMD.
+template <int W, int NH>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+void decode_tqb_kernel(DecodeParams p) {
   constexpr int NT = 64 * W;
-  __shared__ __attribute__((aligned(16))) uint32_t p8[W][4][4][16];  // weight digit planes
-  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][2][64][4];  // query digit image
+  constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
+  __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
+  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2][64][4];  // query digit image
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
   __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
-  __shared__ float accl[W][8][64];  // fp32 value accumulators, lane-major
+  __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
   extern __shared__ int prefix[];
 
   const int tid = threadIdx.x;
@@ -113,13 +123,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int lg = lane >> 4;
   const int grp = blockIdx.x / p.nw;
   const int wg = blockIdx.x - grp * p.nw;
-  const int qs_n = (p.g + 3) >> 2;
+  const int qs_n = (p.g + NHEAD - 1) / NHEAD;
   const int kvl = wave / qs_n;
   const int qsub = wave - kvl * qs_n;
   const int kvh = grp * p.wgh + kvl;
   const int g = p.g;
-  const int hq0 = 4 * qsub;
-  const int gw = g - hq0 < 4 ? g - hq0 : 4;
+  const int hq0 = NHEAD * qsub;
+  const int gw = g - hq0 < NHEAD ? g - hq0 : NHEAD;
   const int h0 = kvh * g + hq0;
 
   // Coefficients of the centroid table (uniform), for the index bits
@@ -251,21 +261,24 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
 
   // ---- online softmax state of the current segment ----
-  float mref, l, zacc;  // per lane: head lg of this wave
-  float(*acc)[64] = accl[wave];
-  v4i cacc[8];
+  float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
+  float(*acc)[64] = accl[wave];       // acc[8r + i][lane]
+  v4i cacc[NH][8];
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
   int since_flush = 0;
   auto reset = [&]() {
-    mref = -INFINITY;
-    l = 0.0f;
-    zacc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i][lane] = 0.0f;
-      cacc[i] = v4i{0, 0, 0, 0};
+    for (int r = 0; r < NH; ++r) {
+      mref[r] = -INFINITY;
+      l[r] = 0.0f;
+      zacc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[8 * r + i][lane] = 0.0f;
+        cacc[r][i] = v4i{0, 0, 0, 0};
+      }
     }
     ev = 0;
     sref = 0.0f;
@@ -274,23 +287,26 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
   // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
   // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
-  auto flush = [&](float alpha) {
+  auto flush = [&](const float (&alpha)[NH]) {
     const float pinv = exp2i(-ev);
-    if (!empty) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e0 = (float)cacc[i].x, e1 = (float)cacc[i].y;
-        const float e2 = (float)cacc[i].z, e3 = (float)cacc[i].w;
-        const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-        acc[i][lane] = __builtin_fmaf(val, pinv, acc[i][lane]) * alpha;
-        cacc[i] = v4i{0, 0, 0, 0};
+    for (int r = 0; r < NH; ++r) {
+      if (!empty) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
+          const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+          const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+          acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
+          cacc[r][i] = v4i{0, 0, 0, 0};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[8 * r + i][lane] *= alpha[r];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][lane] *= alpha;
+      l[r] *= alpha[r];
+      zacc[r] *= alpha[r];
     }
-    l *= alpha;
-    zacc *= alpha;
     empty = true;
   };
 
@@ -299,22 +315,23 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // below 2^27 and split into four balanced base-128 digits; the image for
   // MFMA chunk kc: lane (m = 4h' + piece, g), dword j, byte bb holds the
   // digit of dim 32g + 16kc + 4j + bb -- the byte order of the bit planes.
-  v4i qa[2];
-  float qsum, qf;  // this lane's head (lg): sum of the scaled query, score scale
+  v4i qa[NH][2];
+  float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
   auto load_query = [&](int b) {
-    float qx[4][2];
+    float qx[NHEAD][2];
     const float s0 = p.rot_signs ? p.rot_signs[lane] : 1.0f;
     const float s1 = p.rot_signs ? p.rot_signs[lane + 64] : 1.0f;
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
+    for (int hh = 0; hh < NHEAD; ++hh) {
       const bool ok = hh < gw;
       const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (ok ? hh : 0)) * D;
       qx[hh][0] = ok ? qrow[lane] * s0 : 0.0f;
       qx[hh][1] = ok ? qrow[lane + 64] * s1 : 0.0f;
     }
-    uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0]);
+    uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0][0]);
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
+    for (int hh = 0; hh < NHEAD; ++hh) {
+      const int r = hh >> 2, hp = hh & 3;
       float x0 = qx[hh][0], x1 = qx[hh][1];
       {
         const float a = x0 + x1, c = x0 - x1;
@@ -342,49 +359,59 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int pc = 0; pc < 4; ++pc) {
           const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
           v = (v - dk) >> 7;
-          const int L = 16 * gg + 4 * hh + pc;
-          img[((kc * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
+          const int L = 16 * gg + 4 * hp + pc;
+          img[(((r * 2 + kc) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
           dsum[pc] = (e ? dsum[pc] : 0.0f) + (float)dk;
         }
       }
       float t[4];
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) t[pc] = group_sum<64>(dsum[pc]);
-      if (hh == lg) {
-        qsum = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(t[3], 128.0f, t[2]), 128.0f, t[1]), 128.0f, t[0]);
+      if (hp == lg) {
+        qsum[r] = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(t[3], 128.0f, t[2]), 128.0f, t[1]), 128.0f, t[0]);
         // score in base-2 units = sm_scale / sqrt(D) * log2(e) * 2^-E * norm * (integer dot)
-        qf = p.sm_scale * 0.08838834764831845f * kLog2e * exp2i(-E);
+        qf[r] = p.sm_scale * 0.08838834764831845f * kLog2e * exp2i(-E);
       }
     }
     wave_sync();
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][kc][lane][0]);
-      qa[kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
-    }
+    for (int r = 0; r < NH; ++r)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
+        qa[r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
+      }
   };
 
   // ---------------- segment bookkeeping ----------------
   int seg_b = -1, seg_s = 0;
   bool seg_from_start = false, seg_to_end = false, seg_first = false;
   auto emit = [&]() {
-    flush(1.0f);
-    const bool whole = seg_from_start && seg_to_end;
-    const float lt = row16_sum(l);
-    const float zt = row16_sum(zacc);
-    const int hh = lg;
-    if (hh < gw) {
-      float* out;
-      if (whole)
-        out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
-      else
-        out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
-                       kvl * g + hq0 + hh) * (D + 1);
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      float* dst = out + 8 * ln;
+    {
+      float one[NH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = (acc[i][lane] + zt) * inv;
-      if (ln == 0) out[D] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+      for (int r = 0; r < NH; ++r) one[r] = 1.0f;
+      flush(one);
+    }
+    const bool whole = seg_from_start && seg_to_end;
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const float lt = row16_sum(l[r]);
+      const float zt = row16_sum(zacc[r]);
+      const int hh = 4 * r + lg;
+      if (hh < gw) {
+        float* out;
+        if (whole)
+          out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
+        else
+          out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
+                         kvl * g + hq0 + hh) * (D + 1);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        float* dst = out + 8 * ln;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = (acc[8 * r + i][lane] + zt) * inv;
+        if (ln == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
+      }
     }
   };
 
@@ -406,8 +433,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // keep every use of X's registers after the next tile's loads
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- scores: lane (n, g) gets head g, token 16s + n ----
-    float sc[4];
+    // ---- scores: lane (n, g) gets head 4r + g, token 16s + n ----
+    float sc[NH][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
@@ -418,9 +445,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       // one bit plane at a time: two MFMAs (dims 32g + 16kc + ...), then its
       // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
       // digit planes of head g, token 16s+n
-      auto plane_dot = [&](auto sel) -> float {
+      auto plane_dot = [&](auto sel, float (&out)[NH]) {
         constexpr int S = decltype(sel)::value;  // 1..7: product; 8 + S: parity
-        v4i c = v4i{0, 0, 0, 0};
+        v4i c[NH];
+#pragma unroll
+        for (int r = 0; r < NH; ++r) c[r] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           uint32_t pl[4];
@@ -442,32 +471,41 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
             pl[j] = m;
           }
-          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[kc], v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]},
-                                                    c, 0, 0, 0);
+          const v4i bpl = v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
+#pragma unroll
+          for (int r = 0; r < NH; ++r) c[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[r][kc], bpl, c[r], 0, 0, 0);
         }
-        return __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c.w, 128.0f, (float)c.z), 128.0f, (float)c.y),
-                              128.0f, (float)c.x);
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+          out[r] = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c[r].w, 128.0f, (float)c[r].z), 128.0f,
+                                                 (float)c[r].y), 128.0f, (float)c[r].x);
       };
-      float dot;
+      float dot[NH];
       if (anti) {
         // odd Walsh terms: planes b0, b1, b2, b0^b1^b2
-        const float t = plane_dot(std::integral_constant<int, 9>{}) * ga[1] +
-                        plane_dot(std::integral_constant<int, 10>{}) * ga[2] +
-                        plane_dot(std::integral_constant<int, 12>{}) * ga[4] +
-                        plane_dot(std::integral_constant<int, 15>{}) * ga[7];
-        dot = __builtin_fmaf(ga[1] + ga[2] + ga[4] + ga[7], qsum, -2.0f * t);
+        float t1[NH], t2[NH], t4[NH], t7[NH];
+        plane_dot(std::integral_constant<int, 9>{}, t1);
+        plane_dot(std::integral_constant<int, 10>{}, t2);
+        plane_dot(std::integral_constant<int, 12>{}, t4);
+        plane_dot(std::integral_constant<int, 15>{}, t7);
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          const float t = t1[r] * ga[1] + t2[r] * ga[2] + t4[r] * ga[4] + t7[r] * ga[7];
+          dot[r] = __builtin_fmaf(ga[1] + ga[2] + ga[4] + ga[7], qsum[r], -2.0f * t);
+        }
       } else {
-        dot = al[0] * qsum;
-        dot = __builtin_fmaf(al[1], plane_dot(std::integral_constant<int, 1>{}), dot);
-        dot = __builtin_fmaf(al[2], plane_dot(std::integral_constant<int, 2>{}), dot);
-        dot = __builtin_fmaf(al[3], plane_dot(std::integral_constant<int, 3>{}), dot);
-        dot = __builtin_fmaf(al[4], plane_dot(std::integral_constant<int, 4>{}), dot);
-        dot = __builtin_fmaf(al[5], plane_dot(std::integral_constant<int, 5>{}), dot);
-        dot = __builtin_fmaf(al[6], plane_dot(std::integral_constant<int, 6>{}), dot);
-        dot = __builtin_fmaf(al[7], plane_dot(std::integral_constant<int, 7>{}), dot);
+        float t[NH];
+#pragma unroll
+        for (int r = 0; r < NH; ++r) dot[r] = al[0] * qsum[r];
+#define TQK_PLANE(S)                                                         \
+        plane_dot(std::integral_constant<int, S>{}, t);                      \
+        for (int r = 0; r < NH; ++r) dot[r] = __builtin_fmaf(al[S], t[r], dot[r]);
+        TQK_PLANE(1) TQK_PLANE(2) TQK_PLANE(3) TQK_PLANE(4) TQK_PLANE(5) TQK_PLANE(6) TQK_PLANE(7)
+#undef TQK_PLANE
       }
       const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
-      sc[s] = fminf(dot * (qf * nrm), mask);
+#pragma unroll
+      for (int r = 0; r < NH; ++r) sc[r][s] = fminf(dot[r] * (qf[r] * nrm), mask);
       // one token block at a time (bounds the live bit planes)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -483,15 +521,24 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 
     // ---- reference maximum / weight scale; flush when they move ----
-    const float tm = row16_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const bool move = tm > mref + (float)kTau;
+    float tm[NH];
+    bool move = false;
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      tm[r] = row16_max(fmaxf(fmaxf(sc[r][0], sc[r][1]), fmaxf(sc[r][2], sc[r][3])));
+      move |= tm[r] > mref[r] + (float)kTau;
+    }
     smax = row16_max(smax);
     // a flush also bounds the int32 digit sums (< 2^31 after 8192 tiles)
     const bool smove = smax >= sref || ++since_flush >= 8192;
     if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
-      const float mn = fmaxf(mref, tm);
-      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
-      mref = mn;
+      float alpha[NH];
+#pragma unroll
+      for (int r = 0; r < NH; ++r) {
+        const float mn = fmaxf(mref[r], tm[r]);
+        alpha[r] = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref[r] - mn);
+        mref[r] = mn;
+      }
       flush(alpha);
       since_flush = 0;
       if (smax > 0.0f) {
@@ -505,48 +552,55 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // A negative scale16 (bytes not written by the encoder) takes signed
     // digits: the digits of p * |scale16| negated as int8.
     const float pscale = exp2i(ev);
-    uint32_t dw[4] = {0, 0, 0, 0};
-    float ps = 0.0f, zs = 0.0f;
-    float pr[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      pr[s] = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[s] - mref);
-      ps += pr[s];
-      zs = __builtin_fmaf(pr[s], vz[s], zs);
-    }
     const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
                                                      vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
-    if (!any_neg) {
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      uint32_t dw[4] = {0, 0, 0, 0};
+      float ps = 0.0f, zs = 0.0f;
+      float pr[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+        pr[s] = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+        ps += pr[s];
+        zs = __builtin_fmaf(pr[s], vz[s], zs);
       }
-    } else {
+      if (!any_neg) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
-        const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
-          dw[kk] |= (d & 255u) << (8 * s);
+          for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
+          const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
+            dw[kk] |= (d & 255u) << (8 * s);
+          }
         }
       }
-    }
-    l += ps;
-    zacc += zs;
+      l[r] += ps;
+      zacc[r] += zs;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) p8[wave][lg][kk][ln] = dw[kk];
+      for (int kk = 0; kk < 4; ++kk) p8[wave][r][lg][kk][ln] = dw[kk];
+    }
     empty = false;
     wave_sync();
 
     // ---- value MFMAs: B operands by 4x4 byte transposes ----
     // u[s][h]: index bytes of dims 8n + 4h .. +3 of token 16s + 4g + kk;
     // vb[4h + i][kk] byte s = dim 8n + 4h + i of token 16s + 4g + kk
-    const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][ln >> 2][ln & 3][4 * lg]);
-    const v4i pa = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+    v4i pa[NH];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][r][ln >> 2][ln & 3][4 * lg]);
+      pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t vb[4][4];
@@ -570,7 +624,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
-        cacc[4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, cacc[4 * h + i], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+          cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -635,13 +691,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   emit();
 }
 
-template <int W>
+template <int W, int NH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = (size_t)(p.B + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_tqb_kernel<W>), dim3(blocks), dim3(64 * W), lds, st, p);
+  hipLaunchKernelGGL((decode_tqb_kernel<W, NH>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
+
+// g = 5 .. 8: one wave serves all query heads of a kv head (NH = 2), so each
+// tile's keys and values are unpacked once instead of by two waves.
+constexpr bool kOneWavePerKvHead = true;
 
 }  // namespace
 
@@ -656,15 +716,28 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
   const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
   if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
+  if (p.g > 4 && kOneWavePerKvHead) {
+    // one wave per kv head at one wave per SIMD: at most 4 waves per
+    // workgroup and per CU (the piece region, sized for two waves per kv
+    // head at 8 per CU, holds the same number of workgroups)
+    p.wgh = balance_heads_per_wg(p.hk, 4, 4);
+    const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh) {
+      case 1: return launch<1, 2>(p, st);
+      case 2: return launch<2, 2>(p, st);
+      default: return launch<4, 2>(p, st);
+    }
+  }
   const int qs = (p.g + 3) / 4;
   p.wgh = balance_heads_per_wg(p.hk, p.g);
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1>(p, st);
-    case 2: return launch<2>(p, st);
-    case 4: return launch<4>(p, st);
-    default: return launch<8>(p, st);
+    case 1: return launch<1, 1>(p, st);
+    case 2: return launch<2, 1>(p, st);
+    case 4: return launch<4, 1>(p, st);
+    default: return launch<8, 1>(p, st);
   }
 }
 

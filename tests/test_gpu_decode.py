@@ -347,3 +347,20 @@ def test_tq_mse3_u3_balanced_few_tiles(seq, S):
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
     got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
     assert_close(got, ref, lse, ref_lse, "seq %s S=%d" % (seq, S))
+
+
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("hq,hk", [(10, 2), (12, 2), (14, 2), (16, 2), (32, 4)],
+                         ids=["g5", "g6", "g7", "g8", "g8x4"])
+def test_tq_mse3_u3_query_groups_of_five_to_eight(hq, hk, antisymmetric):
+    """g = 5 .. 8 on the matrix-core path: one wave serves all query heads
+    of a kv head (two MFMA row sets; heads past g padded); random slots,
+    empty and one-token sequences, split and range boundaries."""
+    seq = [0, 1, 300, 777, 65, 2000]
+    w = W.custom_decode_workload(350 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    cache = W.random_tq_mse3_u3_cache(w, oracle.tq_slot_bytes(128, *B_FMT))
+    cen = _random_centroids(350 + hq, antisymmetric)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
+    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
