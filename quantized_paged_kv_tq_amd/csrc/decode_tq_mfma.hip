@@ -19,7 +19,12 @@
 //
 // Work decomposition, tile table, pieces and ping-pong register sets follow
 // the INT4 path (balance.h): equal ranges of the global 64-token tile list,
-// one wave per four query heads of a kv head.
+// one wave per four query heads of a kv head for g <= 4. For g = 5 .. 8 one
+// wave serves all query heads of its kv head (two MFMA row sets): each
+// tile's keys are converted to bf16 and its value nibbles transposed once
+// per kv head instead of by two waves, and each wave's loads are its own
+// (two waves of a kv head fetched the same lines). That wave needs more
+// than 256 registers and runs alone on its SIMD.
 #include "balance.h"
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -77,16 +82,22 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_tq_fp8_kernel(DecodeParams p) {
+// NH: MFMA row sets of four query heads per wave; a tile's keys are
+// converted and its value nibbles transposed once for all 4 * NH heads. NH =
+// 2 (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
+// runs one wave per SIMD.
+template <int W, int NH>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+void decode_tq_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * W;
-  __shared__ __attribute__((aligned(16))) uint32_t p8[W][4][4][16];  // weight digit planes
+  constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
+  __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
   __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
-  __shared__ float accl[W][8][64];  // fp32 value accumulators, lane-major
+  __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
   extern __shared__ int prefix[];
 
   const int tid = threadIdx.x;
@@ -96,13 +107,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int lg = lane >> 4;
   const int grp = blockIdx.x / p.nw;
   const int wg = blockIdx.x - grp * p.nw;
-  const int qs_n = (p.g + 3) >> 2;
+  const int qs_n = (p.g + NHEAD - 1) / NHEAD;
   const int kvl = wave / qs_n;
   const int qsub = wave - kvl * qs_n;
   const int kvh = grp * p.wgh + kvl;
   const int g = p.g;
-  const int hq0 = 4 * qsub;
-  const int gw = g - hq0 < 4 ? g - hq0 : 4;
+  const int hq0 = NHEAD * qsub;
+  const int gw = g - hq0 < NHEAD ? g - hq0 : NHEAD;
   const int h0 = kvh * g + hq0;
 
   // ---- tile counts of all sequences and their prefix sums ----
@@ -189,21 +200,24 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
 
   // ---- online softmax state of the current segment ----
-  float mref, l, zacc;  // per lane: head lg of this wave
-  float(*acc)[64] = accl[wave];
-  v4i cacc[8];
+  float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
+  float(*acc)[64] = accl[wave];       // acc[8r + i][lane]
+  v4i cacc[NH][8];
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
   int since_flush = 0;
   auto reset = [&]() {
-    mref = -INFINITY;
-    l = 0.0f;
-    zacc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      acc[i][lane] = 0.0f;
-      cacc[i] = v4i{0, 0, 0, 0};
+    for (int r = 0; r < NH; ++r) {
+      mref[r] = -INFINITY;
+      l[r] = 0.0f;
+      zacc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[8 * r + i][lane] = 0.0f;
+        cacc[r][i] = v4i{0, 0, 0, 0};
+      }
     }
     ev = 0;
     sref = 0.0f;
@@ -212,58 +226,64 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   };
   // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
   // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
-  auto flush = [&](float alpha) {
+  auto flush = [&](const float (&alpha)[NH]) {
     const float pinv = exp2i(-ev);
-    if (!empty) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e0 = (float)cacc[i].x, e1 = (float)cacc[i].y;
-        const float e2 = (float)cacc[i].z, e3 = (float)cacc[i].w;
-        const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-        acc[i][lane] = __builtin_fmaf(val, pinv, acc[i][lane]) * alpha;
-        cacc[i] = v4i{0, 0, 0, 0};
+    for (int r = 0; r < NH; ++r) {
+      if (!empty) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
+          const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+          const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+          acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
+          cacc[r][i] = v4i{0, 0, 0, 0};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[8 * r + i][lane] *= alpha[r];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][lane] *= alpha;
+      l[r] *= alpha[r];
+      zacc[r] *= alpha[r];
     }
-    l *= alpha;
-    zacc *= alpha;
     empty = true;
   };
 
   // ---------------- query of sequence b: three bf16 parts ----------------
   // A operand of MFMA kb for lane (m = 4h + part, g): 8 bf16 of dims
   // 32g + 8kb .. 32g + 8kb + 7 (part 3: zero)
-  v8bf16 qa[4];
+  v8bf16 qa[NH][4];
   float qf;
   auto load_query = [&](int b) {
-    const int hq = ln >> 2, part = ln & 3;
-    const bool ok = hq < gw && part < 3;
-    const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
-      const float4 c = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
-      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-      uint32_t w[4];
+    for (int r = 0; r < NH; ++r) {
+      const int hq = 4 * r + (ln >> 2), part = ln & 3;
+      const bool ok = hq < gw && part < 3;
+      const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        uint32_t pr[2];
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
+        const float4 c = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
+        const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float v = x[j + e];
-          const uint32_t bh = bf16_bits(v);
-          const float r1 = v - u2f(bh << 16);
-          const uint32_t bm = bf16_bits(r1);
-          const float r2 = r1 - u2f(bm << 16);
-          const uint32_t bl = bf16_bits(r2);
-          const uint32_t sel = part == 0 ? bh : (part == 1 ? bm : bl);
-          pr[e] = ok ? sel : 0u;
+        for (int j = 0; j < 8; j += 2) {
+          uint32_t pr[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float v = x[j + e];
+            const uint32_t bh = bf16_bits(v);
+            const float r1 = v - u2f(bh << 16);
+            const uint32_t bm = bf16_bits(r1);
+            const float r2 = r1 - u2f(bm << 16);
+            const uint32_t bl = bf16_bits(r2);
+            const uint32_t sel = part == 0 ? bh : (part == 1 ? bm : bl);
+            pr[e] = ok ? sel : 0u;
+          }
+          w[j >> 1] = pr[0] | (pr[1] << 16);
         }
-        w[j >> 1] = pr[0] | (pr[1] << 16);
+        qa[r][kb] = __builtin_bit_cast(v8bf16, v4u{w[0], w[1], w[2], w[3]});
       }
-      qa[kb] = __builtin_bit_cast(v8bf16, v4u{w[0], w[1], w[2], w[3]});
     }
     qf = p.sm_scale * kLog2e;
   };
@@ -272,23 +292,31 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   int seg_b = -1, seg_s = 0;
   bool seg_from_start = false, seg_to_end = false, seg_first = false;
   auto emit = [&]() {
-    flush(1.0f);
-    const bool whole = seg_from_start && seg_to_end;
-    const float lt = row16_sum(l);
-    const float zt = row16_sum(zacc);
-    const int hh = lg;
-    if (hh < gw) {
-      float* out;
-      if (whole)
-        out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
-      else
-        out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
-                       kvl * g + hq0 + hh) * (D + 1);
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      float* dst = out + 8 * ln;
+    {
+      float one[NH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = (acc[i][lane] + zt) * inv;
-      if (ln == 0) out[D] = lt > 0.0f ? (mref + __log2f(lt)) * kLn2 : -INFINITY;
+      for (int r = 0; r < NH; ++r) one[r] = 1.0f;
+      flush(one);
+    }
+    const bool whole = seg_from_start && seg_to_end;
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const float lt = row16_sum(l[r]);
+      const float zt = row16_sum(zacc[r]);
+      const int hh = 4 * r + lg;
+      if (hh < gw) {
+        float* out;
+        if (whole)
+          out = p.ws + (((int64_t)seg_b * p.hq + h0 + hh) * p.splits + seg_s) * (D + 1);
+        else
+          out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
+                         kvl * g + hq0 + hh) * (D + 1);
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        float* dst = out + 8 * ln;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = (acc[8 * r + i][lane] + zt) * inv;
+        if (ln == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
+      }
     }
   };
 
@@ -315,11 +343,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int s = 0; s < 4; ++s) sz[s] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz);
 
-    // ---- scores: lane (n, g) gets head g, token 16s + n ----
-    float sc[4];
+    // ---- scores: lane (n, g) gets head 4r + g, token 16s + n ----
+    float sc[NH][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      v4f c[NH];
+#pragma unroll
+      for (int r = 0; r < NH; ++r) c[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         // key bytes 8kb .. 8kb + 7 of this lane's 32 -> 8 bf16
@@ -330,10 +360,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         const v2bf16 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
         const v2bf16 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
         const v8bf16 kb8 = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], kb8, c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < NH; ++r) c[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[r][kb], kb8, c[r], 0, 0, 0);
       }
       const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
-      sc[s] = fminf((c.x + c.y + c.z) * qf, mask);
+#pragma unroll
+      for (int r = 0; r < NH; ++r) sc[r][s] = fminf((c[r].x + c[r].y + c[r].z) * qf, mask);
     }
     float vsc[4], vz[4];
     float smax = 0.0f;
@@ -345,14 +377,23 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 
     // ---- reference maximum / weight scale; flush when they move ----
-    const float tm = row16_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const bool move = tm > mref + (float)kTau;
+    float tm[NH];
+    bool move = false;
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      tm[r] = row16_max(fmaxf(fmaxf(sc[r][0], sc[r][1]), fmaxf(sc[r][2], sc[r][3])));
+      move |= tm[r] > mref[r] + (float)kTau;
+    }
     smax = row16_max(smax);
     const bool smove = smax >= sref || ++since_flush >= 8192;
     if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
-      const float mn = fmaxf(mref, tm);
-      const float alpha = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
-      mref = mn;
+      float alpha[NH];
+#pragma unroll
+      for (int r = 0; r < NH; ++r) {
+        const float mn = fmaxf(mref[r], tm[r]);
+        alpha[r] = (mn == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mref[r] - mn);
+        mref[r] = mn;
+      }
       flush(alpha);
       since_flush = 0;
       if (smax > 0.0f) {
@@ -367,46 +408,53 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // one (any bytes are accepted) takes signed digits: the digits of
     // p * |scale16|, negated as int8, which the i8 MFMA sums exactly too.
     const float pscale = exp2i(ev);
-    uint32_t dw[4] = {0, 0, 0, 0};
-    float ps = 0.0f, zs = 0.0f;
-    float pr[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      pr[s] = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[s] - mref);
-      ps += pr[s];
-      zs = __builtin_fmaf(pr[s], vz[s], zs);
-    }
     const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
                                                      vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
-    if (!any_neg) {
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      uint32_t dw[4] = {0, 0, 0, 0};
+      float ps = 0.0f, zs = 0.0f;
+      float pr[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+        pr[s] = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+        ps += pr[s];
+        zs = __builtin_fmaf(pr[s], vz[s], zs);
       }
-    } else {
+      if (!any_neg) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
-        const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
-          dw[kk] |= (d & 255u) << (8 * s);
+          for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
+          const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
+            dw[kk] |= (d & 255u) << (8 * s);
+          }
         }
       }
-    }
-    l += ps;
-    zacc += zs;
+      l[r] += ps;
+      zacc[r] += zs;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) p8[wave][lg][kk][ln] = dw[kk];
+      for (int kk = 0; kk < 4; ++kk) p8[wave][r][lg][kk][ln] = dw[kk];
+    }
     empty = false;
     wave_sync();
 
     // ---- value MFMAs: B operands by nibble transpose, in two halves ----
-    const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][ln >> 2][ln & 3][4 * lg]);
-    const v4i pa = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+    v4i pa[NH];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][r][ln >> 2][ln & 3][4 * lg]);
+      pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t vb[4][4];
@@ -426,7 +474,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
-        cacc[4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa, vbi, cacc[4 * h + i], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+          cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
       }
     }
     wave_sync();
@@ -489,13 +539,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   emit();
 }
 
-template <int W>
+template <int W, int NH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = (size_t)(p.B + 1) * sizeof(int);
-  hipLaunchKernelGGL((decode_tq_fp8_kernel<W>), dim3(blocks), dim3(64 * W), lds, st, p);
+  hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
+
+// g = 5 .. 8: one wave serves all query heads of a kv head (NH = 2), so each
+// tile's keys are converted once instead of by two waves.
+constexpr bool kOneWavePerKvHead = true;
 
 }  // namespace
 
@@ -509,15 +563,28 @@ hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
   const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
   if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
+  if (p.g > 4 && kOneWavePerKvHead) {
+    // one wave per kv head at one wave per SIMD: at most 4 waves per
+    // workgroup and per CU (the piece region, sized for two waves per kv
+    // head at 8 per CU, holds the same number of workgroups)
+    p.wgh = balance_heads_per_wg(p.hk, 4, 4);
+    const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh) {
+      case 1: return launch<1, 2>(p, st);
+      case 2: return launch<2, 2>(p, st);
+      default: return launch<4, 2>(p, st);
+    }
+  }
   const int qs = (p.g + 3) / 4;
   p.wgh = balance_heads_per_wg(p.hk, p.g);
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1>(p, st);
-    case 2: return launch<2>(p, st);
-    case 4: return launch<4>(p, st);
-    default: return launch<8>(p, st);
+    case 1: return launch<1, 1>(p, st);
+    case 2: return launch<2, 1>(p, st);
+    case 4: return launch<4, 1>(p, st);
+    default: return launch<8, 1>(p, st);
   }
 }
 

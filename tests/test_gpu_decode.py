@@ -364,3 +364,17 @@ def test_tq_mse3_u3_query_groups_of_five_to_eight(hq, hk, antisymmetric):
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
     got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
     assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+
+
+@pytest.mark.parametrize("hq,hk", [(10, 2), (12, 2), (14, 2), (16, 2), (32, 4)],
+                         ids=["g5", "g6", "g7", "g8", "g8x4"])
+def test_tq_fp8_u4_query_groups_of_five_to_eight(hq, hk):
+    """FP8 keys + 4-bit values at g = 5 .. 8: one wave serves all query
+    heads of a kv head; random slots, empty and one-token sequences."""
+    seq = [0, 1, 300, 777, 65, 2000]
+    w = W.custom_decode_workload(360 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    cache = W.random_tq_fp8_u4_cache(w, oracle.tq_slot_bytes(128, *A_FMT))
+    q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
+    ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT)
+    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
