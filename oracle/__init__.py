@@ -26,7 +26,7 @@ _lib = None
 
 # Format codes of the combined TurboQuant slot (oracle-side numbering).
 KEY_FP8, KEY_MSE3, KEY_MSE4 = 1, 2, 3
-VAL_U3, VAL_U4 = 1, 2
+VAL_U3, VAL_U4, VAL_FP8 = 1, 2, 3
 DT_F32, DT_F16, DT_BF16 = 0, 1, 2
 
 

@@ -412,15 +412,19 @@ int orc_int4_decode(const float* q, const uint8_t* key_cache,
 /* ------------------------------------------------------------------------ */
 /* TurboQuant combined-slot cache ([tq]).                                    */
 /* key_fmt: 1 FP8 E4M3, 2 centroid 3-bit, 3 centroid 4-bit.                  */
-/* val_fmt: 1 uniform 3-bit, 2 uniform 4-bit.                                */
+/* val_fmt: 1 uniform 3-bit, 2 uniform 4-bit, 3 FP8 E4M3 (the stage-1        */
+/* signature documents value bits "4 or 8=FP8" with D value bytes for FP8;   */
+/* its body decodes only 3 and 4 bits, so FP8 values are read as D E4M3      */
+/* codes with no scale or zero, like FP8 keys).                              */
 /* Slot layout (reading of _tq_decode_stage1's addressing, the pages never   */
 /* define key_packed_size or the padding): key region of KPS bytes (FP8: d   */
 /* codes; centroid: ceil(d*b/8) bytes of indices then the fp16 norm, so      */
-/* KPS = MSE_BYTES + 2), value data of ceil(d*vb/8) bytes, fp16 scale, fp16  */
-/* zero; total rounded up to 16 bytes with zero padding.                     */
+/* KPS = MSE_BYTES + 2), value data of ceil(d*vb/8) bytes (FP8: d), then for */
+/* uniform values the fp16 scale and fp16 zero; total rounded up to 16 bytes */
+/* with zero padding.                                                        */
 /* ------------------------------------------------------------------------ */
 static int key_bits(int key_fmt) { return key_fmt == 2 ? 3 : key_fmt == 3 ? 4 : 8; }
-static int val_bits(int val_fmt) { return val_fmt == 1 ? 3 : 4; }
+static int val_bits(int val_fmt) { return val_fmt == 1 ? 3 : val_fmt == 2 ? 4 : 8; }
 static int key_region(int d, int key_fmt) {
   if (key_fmt == 1) return d;
   return (d * key_bits(key_fmt) + 7) / 8 + 2;
@@ -428,8 +432,8 @@ static int key_region(int d, int key_fmt) {
 static int val_data_bytes(int d, int val_fmt) { return (d * val_bits(val_fmt) + 7) / 8; }
 
 int orc_tq_slot_bytes(int d, int key_fmt, int val_fmt) {
-  if (key_fmt < 1 || key_fmt > 3 || val_fmt < 1 || val_fmt > 2) return -1;
-  int raw = key_region(d, key_fmt) + val_data_bytes(d, val_fmt) + 4;
+  if (key_fmt < 1 || key_fmt > 3 || val_fmt < 1 || val_fmt > 3) return -1;
+  int raw = key_region(d, key_fmt) + val_data_bytes(d, val_fmt) + (val_fmt == 3 ? 0 : 4);
   return (raw + 15) / 16 * 16;
 }
 
@@ -553,6 +557,13 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
         s[kps - 2] = (uint8_t)(n16 & 0xFF);
         s[kps - 1] = (uint8_t)(n16 >> 8);
       }
+      if (val_fmt == 3) {
+        for (int i = 0; i < d; ++i) {
+          float x = v[i] > 448.0f ? 448.0f : (v[i] < -448.0f ? -448.0f : v[i]);
+          s[kps + i] = orc_f32_to_e4m3(x);
+        }
+        continue;
+      }
       float mn = INFINITY, mx = -INFINITY;
       for (int i = 0; i < d; ++i) {
         if (v[i] < mn) mn = v[i];
@@ -623,10 +634,15 @@ static double tq_score(void* p, int64_t t) {
   return c->sm_scale * nrm * dot;
 }
 
-/* [tq] _tq_decode_stage1, value: idx * scale16 + zero16 (3- or 4-bit). */
+/* [tq] _tq_decode_stage1, value: idx * scale16 + zero16 (3- or 4-bit);
+ * FP8 values: e4m3(byte). */
 static void tq_value(void* p, int64_t t, double* v) {
   tq_ctx* c = p;
   const uint8_t* vd = tq_slot(c, t) + key_region(c->d, c->key_fmt);
+  if (c->val_fmt == 3) {
+    for (int i = 0; i < c->d; ++i) v[i] = (double)orc_e4m3_to_f32(vd[i]);
+    return;
+  }
   int vb = val_bits(c->val_fmt);
   int vdb = val_data_bytes(c->d, c->val_fmt);
   double sc = (double)orc_f16_to_f32((uint16_t)(vd[vdb] | (vd[vdb + 1] << 8)));

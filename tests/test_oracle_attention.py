@@ -143,6 +143,12 @@ def test_tq_slot_sizes():
     assert oracle.tq_slot_bytes(128, oracle.KEY_MSE3, oracle.VAL_U3) == 112
     assert oracle.tq_slot_bytes(128, oracle.KEY_MSE4, oracle.VAL_U4) == 144
     assert oracle.tq_slot_bytes(64, oracle.KEY_FP8, oracle.VAL_U3) == 96
+    # FP8 values: D E4M3 codes, no scale or zero
+    assert oracle.tq_slot_bytes(128, oracle.KEY_FP8, oracle.VAL_FP8) == 256
+    assert oracle.tq_slot_bytes(128, oracle.KEY_MSE3, oracle.VAL_FP8) == 192   # 50 + 128
+    assert oracle.tq_slot_bytes(256, oracle.KEY_MSE4, oracle.VAL_FP8) == 400   # 130 + 256
+    assert oracle.tq_slot_bytes(256, oracle.KEY_MSE3, oracle.VAL_U3) == 208    # 98 + 96 + 4
+    assert oracle.tq_slot_bytes(128, oracle.KEY_FP8, 4) == -1
 
 
 def _tq_case(key_fmt, val_fmt, wid=30, B=2, hq=4, hk=2, d=128, bs=16, seq=(40, 19)):
@@ -163,7 +169,7 @@ def _tq_case(key_fmt, val_fmt, wid=30, B=2, hq=4, hk=2, d=128, bs=16, seq=(40, 1
 def _tq_fields(cache, key_fmt, val_fmt, d, cen):
     """Decode one slot array [.., sb] with numpy/torch library routines."""
     kb = {oracle.KEY_FP8: 8, oracle.KEY_MSE3: 3, oracle.KEY_MSE4: 4}[key_fmt]
-    vb = 3 if val_fmt == oracle.VAL_U3 else 4
+    vb = {oracle.VAL_U3: 3, oracle.VAL_U4: 4, oracle.VAL_FP8: 8}[val_fmt]
     if key_fmt == oracle.KEY_FP8:
         kps = d
         kv = torch.from_numpy(cache[..., :d].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -176,6 +182,9 @@ def _tq_fields(cache, key_fmt, val_fmt, d, cen):
         kv = cen.astype(np.float64)[idx]
         norm = cache[..., mb:mb + 2].copy().view(np.float16)[..., 0].astype(np.float64)
     vdb = (d * vb + 7) // 8
+    if val_fmt == oracle.VAL_FP8:
+        vals = torch.from_numpy(cache[..., kps:kps + d].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        return kv, norm, vals
     bits = np.unpackbits(cache[..., kps:kps + vdb], axis=-1, bitorder="little")
     vidx = (bits.reshape(*bits.shape[:-1], d, vb) * (1 << np.arange(vb))).sum(-1)
     f16 = cache[..., kps + vdb:kps + vdb + 4].copy().view(np.float16).astype(np.float64)
@@ -184,13 +193,15 @@ def _tq_fields(cache, key_fmt, val_fmt, d, cen):
 
 
 @pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3),
-                                 (oracle.KEY_MSE4, oracle.VAL_U4), (oracle.KEY_FP8, oracle.VAL_U3)])
+                                 (oracle.KEY_MSE4, oracle.VAL_U4), (oracle.KEY_FP8, oracle.VAL_U3),
+                                 (oracle.KEY_FP8, oracle.VAL_FP8), (oracle.KEY_MSE3, oracle.VAL_FP8)])
 @pytest.mark.parametrize("norm_correction", [0, 1])
-def test_tq_decode_matches_library_brute_force(fmt, norm_correction):
+@pytest.mark.parametrize("d", [128, 256])
+def test_tq_decode_matches_library_brute_force(fmt, norm_correction, d):
     key_fmt, val_fmt = fmt
     if key_fmt == oracle.KEY_FP8 and norm_correction:
         pytest.skip("norm correction applies to centroid keys only")
-    w, q, cache, cen, k, v = _tq_case(key_fmt, val_fmt)
+    w, q, cache, cen, k, v = _tq_case(key_fmt, val_fmt, d=d)
     d = w.d
     H = scipy.linalg.hadamard(d).astype(np.float64) / np.sqrt(d)
     kv, norm, vals = _tq_fields(cache, key_fmt, val_fmt, d, cen)
@@ -291,3 +302,30 @@ def test_tq_centroid_encoder_fp32_agrees_with_fp64(key_fmt, bits, d):
         ulp = np.spacing(np.abs(want16).astype(np.float16)).astype(np.float64)
         assert np.all(np.abs(n16.astype(np.float64) - want16.astype(np.float64)) <= ulp)
         assert (n16 == want16).mean() > 0.99
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_tq_fp8_value_bytes_are_library_e4m3(d):
+    """FP8 values (value bits 8): the D bytes after the key region are
+    torch's float8_e4m3fn codes of clamp(v, +-448), the rest of the slot is
+    zero (no scale or zero point)."""
+    rng = np.random.default_rng(40 + d)
+    T, hk = 20, 2
+    k = rng.standard_normal((T, hk, d)).astype(np.float32)
+    v = (rng.standard_normal((T, hk, d)) * rng.choice([1e-3, 1.0, 100.0, 1e3], (T, hk, 1))).astype(np.float32)
+    v[0, 0, :4] = [500.0, -600.0, 0.0, -0.0]
+    sb = oracle.tq_slot_bytes(d, oracle.KEY_FP8, oracle.VAL_FP8)
+    cache = np.full((2, 16, hk, sb), 0xA5, np.uint8)
+    slots = np.arange(T, dtype=np.int64)
+    slots[3] = -1
+    oracle.tq_encode(k, v, oracle.KEY_FP8, oracle.VAL_FP8, None, None, slots, cache)
+    want_v = torch.from_numpy(np.clip(v, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    want_k = torch.from_numpy(np.clip(k, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    flat = cache.reshape(32, hk, sb)
+    for t in range(T):
+        if t == 3:
+            assert np.all(flat[t] == 0xA5)
+            continue
+        np.testing.assert_array_equal(flat[t, :, :d], want_k[t])
+        np.testing.assert_array_equal(flat[t, :, d:2 * d], want_v[t])
+        assert np.all(flat[t, :, 2 * d:] == 0)
