@@ -58,6 +58,7 @@ extern "C" {
 #define TQ_VAL_INT4 0 /* separate INT4 cache + scale words (with TQ_KEY_INT4) */
 #define TQ_VAL_U3 1   /* combined slot: 3-bit uniform, fp16 scale and zero    */
 #define TQ_VAL_U4 2   /* combined slot: 4-bit uniform, fp16 scale and zero    */
+#define TQ_VAL_FP8 3  /* combined slot: D bytes of OCP E4M3FN, no scale/zero */
 
 /* tq_decode_args.flags */
 #define TQ_FLAG_GENERIC 1u /* force the format-generic vector kernel         */
@@ -119,6 +120,10 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
  *            u = 0 when norm == 0
  *     idx_i = argmin_j |u_i - centroids[j]| (fp32; ties to the lower j),
  *            packed LSB first in ceil(D*b/8) bytes, then fp16(norm);
+ *   TQ_VAL_FP8   D value bytes = e4m3(clamp(v, +-448)) (RNE) after the key
+ *                region (the value-bits parameter of _tq_decode_stage1 is
+ *                documented as 4 or 8 = FP8; the stage decodes only 3 and 4
+ *                bits, so this layout is a reading);
  *   values (b = 3 / 4 for TQ_VAL_U3 / U4):
  *     scale = max(fl((max v - min v) / (2^b - 1)), 1e-6), zero = min v (+0
  *     for a zero minimum), both stored fp16 (RNE); idx = clamp(rint(
@@ -134,7 +139,7 @@ int tq_reshape_and_cache_int4(const void* key, const void* value, int32_t kv_dty
  *   kv_cache        device, [num_blocks, block_size, Hk, slot_bytes] u8,
  *                   slot_bytes >= tq_slot_bytes(D, key_fmt, val_fmt), a
  *                   multiple of 16
- *   D in {64, 128}. num_tokens == 0 returns TQ_OK without launching.
+ *   D in {64, 128, 256}. num_tokens == 0 returns TQ_OK without launching.
  *   Alignment: key, value, rot_signs, kv_cache 16 B; slot_mapping 8 B;
  *   centroids 4 B. num_tokens * Hk < 2^31. Slots must be unique.
  */
@@ -167,15 +172,18 @@ int tq_encode_and_cache(const void* key, const void* value, int32_t kv_dtype,
  *     be NULL: all +1); score = sm_scale * norm16 * (q_rot . c[idx]), with
  *     c / sqrt(sum c^2 + 1e-16) when norm_correction != 0.
  *   TQ_VAL_U3 / U4: v = idx * scale16 + zero16.
+ *   TQ_VAL_FP8: v = e4m3(byte).
  * Combined slot layout (TQ formats): key region (FP8: D bytes; centroid:
  * ceil(D*b/8) bytes of LSB-first b-bit indices then the fp16 norm), value
- * indices (ceil(D*vb/8) bytes, LSB-first), fp16 scale, fp16 zero, padding to
+ * data (U3 / U4: ceil(D*vb/8) bytes of LSB-first indices, then fp16 scale
+ * and fp16 zero; FP8: D codes), padding to
  * slot_bytes = tq_slot_bytes(D, key_fmt, val_fmt).
  *
  * Block-table entries outside [0, num_blocks) are never dereferenced (the
  * result for that sequence is then unspecified); seq_len is clamped to
  * max_blocks * block_size; seq_len == 0 gives out = 0 and lse = -inf.
- * Supported: D in {64, 128}; Hq % Hk == 0 and Hq / Hk <= 16;
+ * Supported: D in {64, 128} (and 256 for the TQ formats); Hq % Hk == 0 and
+ * Hq / Hk <= 16;
  * 1 <= num_kv_splits <= 256; block_size >= 1.
  */
 typedef struct tq_decode_args {
@@ -218,7 +226,8 @@ typedef struct tq_decode_args {
  * the piece slots of the balanced INT4 decode, which spreads the tiles of all
  * splits evenly over the workgroups and writes a split cut between two
  * workgroups as pieces that stage 2 merges like splits (2 * nw * Hq * (D+1)
- * fp32, nw = max(1, 2048 / Hk)). Returns 0 for invalid sizes.
+ * fp32, nw = max(1, 2048 / (Hk * ceil(Hq / Hk / 4)))). Returns 0 for invalid
+ * sizes.
  */
 size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hk, int32_t D,
                                  int32_t num_kv_splits);

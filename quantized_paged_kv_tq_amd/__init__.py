@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libtq_amd.so")
 TQ_OK, TQ_EINVAL, TQ_ENOTSUP, TQ_ELAUNCH = 0, -1, -2, -3
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 KEY_INT4, KEY_FP8, KEY_MSE3, KEY_MSE4 = 0, 1, 2, 3
-VAL_INT4, VAL_U3, VAL_U4 = 0, 1, 2
+VAL_INT4, VAL_U3, VAL_U4, VAL_FP8 = 0, 1, 2, 3
 FLAG_GENERIC = 1
 
 

@@ -33,9 +33,10 @@ int launched(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int key_bits(int key_fmt) { return key_fmt == TQ_KEY_MSE3 ? 3 : (key_fmt == TQ_KEY_MSE4 ? 4 : 8); }
-int val_bits(int val_fmt) { return val_fmt == TQ_VAL_U3 ? 3 : 4; }
+int val_bits(int val_fmt) { return val_fmt == TQ_VAL_U3 ? 3 : (val_fmt == TQ_VAL_U4 ? 4 : 8); }
 
-// Combined TurboQuant slot: key region, value indices, fp16 scale, fp16 zero.
+// Combined TurboQuant slot: key region, value data (indices or E4M3 codes),
+// then fp16 scale and fp16 zero for uniform values.
 int key_region_bytes(int d, int key_fmt) {
   if (key_fmt == TQ_KEY_FP8) return d;
   return (d * key_bits(key_fmt) + 7) / 8 + 2;
@@ -53,8 +54,8 @@ int tq_version(void) { return 2; }
 int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt) {
   if (D <= 0 || D > 1024 || (D & (D - 1)) != 0) return -1;
   if (key_fmt < TQ_KEY_FP8 || key_fmt > TQ_KEY_MSE4) return -1;
-  if (val_fmt != TQ_VAL_U3 && val_fmt != TQ_VAL_U4) return -1;
-  const int raw = key_region_bytes(D, key_fmt) + value_index_bytes(D, val_fmt) + 4;
+  if (val_fmt != TQ_VAL_U3 && val_fmt != TQ_VAL_U4 && val_fmt != TQ_VAL_FP8) return -1;
+  const int raw = key_region_bytes(D, key_fmt) + value_index_bytes(D, val_fmt) + (val_fmt == TQ_VAL_FP8 ? 0 : 4);
   return (raw + 15) / 16 * 16;
 }
 
@@ -113,8 +114,8 @@ int tq_encode_and_cache(const void* key, const void* value, int32_t kv_dtype,
                         void* stream) {
   if (num_tokens < 0) return fail(TQ_EINVAL, "num_tokens < 0");
   if (num_kv_heads <= 0) return fail(TQ_EINVAL, "num_kv_heads must be positive");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(TQ_ENOTSUP, "head_dim %d not supported (64, 128)", head_dim);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(TQ_ENOTSUP, "head_dim %d not supported (64, 128, 256)", head_dim);
   if (kv_dtype != TQ_DTYPE_F32 && kv_dtype != TQ_DTYPE_F16 && kv_dtype != TQ_DTYPE_BF16)
     return fail(TQ_ENOTSUP, "kv_dtype %d not supported", kv_dtype);
   const int sb = tq_slot_bytes(head_dim, key_fmt, val_fmt);
@@ -182,7 +183,8 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   if (a->Hq / a->Hk > 16) return fail(TQ_ENOTSUP, "Hq / Hk > 16");
   if (a->D <= 0 || a->D % 2 != 0 || (a->D & (a->D - 1)) != 0)
     return fail(TQ_EINVAL, "D must be an even power of two (got %d)", a->D);
-  if (a->D != 64 && a->D != 128) return fail(TQ_ENOTSUP, "D %d not supported (64, 128)", a->D);
+  if (a->D != 64 && a->D != 128 && !(a->D == 256 && a->key_fmt != TQ_KEY_INT4))
+    return fail(TQ_ENOTSUP, "D %d not supported (64, 128; 256 for the TurboQuant formats)", a->D);
   if (a->num_kv_splits < 1 || a->num_kv_splits > 256)
     return fail(TQ_EINVAL, "num_kv_splits must be in [1, 256]");
   if (a->block_size <= 0 || a->max_blocks <= 0 || a->num_blocks <= 0)
@@ -191,7 +193,7 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   if (int4 != (a->val_fmt == TQ_VAL_INT4))
     return fail(TQ_ENOTSUP, "INT4 keys pair only with INT4 values");
   if (a->key_fmt < TQ_KEY_INT4 || a->key_fmt > TQ_KEY_MSE4 || a->val_fmt < TQ_VAL_INT4 ||
-      a->val_fmt > TQ_VAL_U4)
+      a->val_fmt > TQ_VAL_FP8)
     return fail(TQ_ENOTSUP, "unknown key/value format");
   if (a->B == 0) {
     g_err[0] = '\0';

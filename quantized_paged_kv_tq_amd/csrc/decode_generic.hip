@@ -3,7 +3,7 @@
 // Covers every key/value format of the library: INT4 (int4_per_token_head.py,
 // _attn_packed and unified_attention_int4) and the TurboQuant combined slot
 // (triton_turboquant_decode.py, _tq_decode_stage1): FP8 or 3/4-bit centroid
-// keys, 3/4-bit uniform values.
+// keys, 3/4-bit uniform or FP8 values; D = 64, 128 or 256.
 //
 // One workgroup (4 waves) per (batch, kv head, head chunk, split). The query
 // heads that share the kv head (up to G of them) are rotated/scaled once into
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
 
   const int32_t* bt = p.block_table + (int64_t)b * p.max_blocks;
   constexpr int KB = (KF == KF_MSE3) ? 3 : 4;  // centroid index bits
-  constexpr int VB = (VF == VF_U3) ? 3 : 4;
+  constexpr int VB = (VF == VF_U3) ? 3 : (VF == VF_FP8 ? 8 : 4);  // value bits
   const int mse_bytes = (D * KB + 7) / 8;
   const int bs = p.block_size;
   const int64_t pg0 = t0 / bs;
@@ -165,9 +165,16 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
       const int vbyte = p.kps + li * VB;
       r.w[3] = s32[vbyte >> 2];
       r.w[4] = s32[(vbyte >> 2) + 1];
-      const int sbyte = p.kps + p.vdb;
-      r.w[5] = s32[sbyte >> 2];
-      r.w[6] = s32[(sbyte >> 2) + 1];
+      if constexpr (VF == VF_FP8) {
+        // 8 codes from an unaligned byte offset span 3 dwords (centroid keys:
+        // KPS = 2 mod 4, and the slot padding holds the third dword); FP8
+        // keys leave the codes dword-aligned
+        if (p.kps & 3) r.w[5] = s32[(vbyte >> 2) + 2];
+      } else {
+        const int sbyte = p.kps + p.vdb;
+        r.w[5] = s32[sbyte >> 2];
+        r.w[6] = s32[(sbyte >> 2) + 1];
+      }
     }
     return r;
   };
@@ -217,6 +224,15 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeParams p) {
       const float vsc = u2f(sw & 0xFFFFFFF0u);
 #pragma unroll
       for (int j = 0; j < 8; ++j) vd[j] = ((float)((w >> (4 * j)) & 0xFu) - zp) * vsc;
+    } else if constexpr (VF == VF_FP8) {
+      const uint32_t sh = (uint32_t)(p.kps + li * VB) & 3;
+      const uint32_t w0 = __builtin_amdgcn_alignbyte(r.w[4], r.w[3], sh);
+      const uint32_t w1 = __builtin_amdgcn_alignbyte(r.w[5], r.w[4], sh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vd[j] = e4m3_to_f32((w0 >> (8 * j)) & 0xFFu);
+        vd[j + 4] = e4m3_to_f32((w1 >> (8 * j)) & 0xFFu);
+      }
     } else {
       const uint32_t w = __builtin_amdgcn_alignbyte(r.w[4], r.w[3], (p.kps + li * VB) & 3);
       const uint32_t sz = __builtin_amdgcn_alignbyte(r.w[6], r.w[5], (p.kps + p.vdb) & 3);
@@ -318,13 +334,18 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t st) {
 template <int D>
 hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
   switch (p.key_fmt * 4 + p.val_fmt) {
-    case KF_INT4 * 4 + VF_INT4: return launch_g<D, KF_INT4, VF_INT4>(p, st);
+    case KF_INT4 * 4 + VF_INT4:
+      if constexpr (D == 256) return hipErrorNotSupported;  // INT4: D = 64, 128
+      else return launch_g<D, KF_INT4, VF_INT4>(p, st);
     case KF_FP8 * 4 + VF_U3: return launch_g<D, KF_FP8, VF_U3>(p, st);
     case KF_FP8 * 4 + VF_U4: return launch_g<D, KF_FP8, VF_U4>(p, st);
     case KF_MSE3 * 4 + VF_U3: return launch_g<D, KF_MSE3, VF_U3>(p, st);
     case KF_MSE3 * 4 + VF_U4: return launch_g<D, KF_MSE3, VF_U4>(p, st);
     case KF_MSE4 * 4 + VF_U3: return launch_g<D, KF_MSE4, VF_U3>(p, st);
     case KF_MSE4 * 4 + VF_U4: return launch_g<D, KF_MSE4, VF_U4>(p, st);
+    case KF_FP8 * 4 + VF_FP8: return launch_g<D, KF_FP8, VF_FP8>(p, st);
+    case KF_MSE3 * 4 + VF_FP8: return launch_g<D, KF_MSE3, VF_FP8>(p, st);
+    case KF_MSE4 * 4 + VF_FP8: return launch_g<D, KF_MSE4, VF_FP8>(p, st);
     default: return hipErrorNotSupported;
   }
 }
@@ -334,6 +355,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
 hipError_t launch_decode_generic(const DecodeParams& p, hipStream_t st) {
   if (p.d == 128) return launch_d<128>(p, st);
   if (p.d == 64) return launch_d<64>(p, st);
+  if (p.d == 256) return launch_d<256>(p, st);
   return hipErrorNotSupported;
 }
 

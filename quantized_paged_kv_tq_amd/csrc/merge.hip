@@ -204,12 +204,16 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t st) {
     } else {
       if (pg == 1) TQ_MERGE(128, false, 1); else if (pg == 2) TQ_MERGE(128, false, 2); else TQ_MERGE(128, false, 4);
     }
-  } else {
+  } else if (p.d == 64) {
     if (rot) {
       if (pg == 1) TQ_MERGE(64, true, 1); else if (pg == 2) TQ_MERGE(64, true, 2); else TQ_MERGE(64, true, 4);
     } else {
       if (pg == 1) TQ_MERGE(64, false, 1); else if (pg == 2) TQ_MERGE(64, false, 2); else TQ_MERGE(64, false, 4);
     }
+  } else {
+    // D = 256: the TurboQuant formats only (no inverse rotation)
+    if (rot) return hipErrorNotSupported;
+    if (pg == 1) TQ_MERGE(256, false, 1); else if (pg == 2) TQ_MERGE(256, false, 2); else TQ_MERGE(256, false, 4);
   }
 #undef TQ_MERGE
   return hipGetLastError();

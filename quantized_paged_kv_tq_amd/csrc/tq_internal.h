@@ -30,7 +30,7 @@ hipError_t launch_fwht128_fp8(const void* x, int64_t rows, uint8_t* y, float* sc
 
 // Key/value formats (same numbering as the public header).
 enum { KF_INT4 = 0, KF_FP8 = 1, KF_MSE3 = 2, KF_MSE4 = 3 };
-enum { VF_INT4 = 0, VF_U3 = 1, VF_U4 = 2 };
+enum { VF_INT4 = 0, VF_U3 = 1, VF_U4 = 2, VF_FP8 = 3 };
 
 struct TqWriteParams {
   const void* key;

@@ -39,9 +39,9 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t ele
 }
 
 // FWHT of a row held as two 8-element halves per lane over LPR lanes (sg[k]
-// = +1 / -1 for the lower / upper lane of lane distance 2^k).
+// = +1 / -1 for the lower / upper lane of lane distance 2^k; LPR <= 16).
 template <int LPR>
-__device__ __forceinline__ void fwht_row(float x[16], const float sg[3]) {
+__device__ __forceinline__ void fwht_row(float x[16], const float sg[4]) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -58,6 +58,7 @@ __device__ __forceinline__ void fwht_row(float x[16], const float sg[3]) {
     if constexpr (LPR >= 2) x[j] = butterfly16<1>(x[j], sg[0]);
     if constexpr (LPR >= 4) x[j] = butterfly16<2>(x[j], sg[1]);
     if constexpr (LPR >= 8) x[j] = butterfly16<4>(x[j], sg[2]);
+    if constexpr (LPR >= 16) x[j] = butterfly16<8>(x[j], sg[3]);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {

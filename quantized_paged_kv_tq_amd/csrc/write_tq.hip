@@ -109,7 +109,7 @@ __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* 
                                                     const float (&cen)[1 << KB], bool fast,
                                                     const float (&thr)[(1 << KB) - 1],
                                                     const float* rot_signs, int kps,
-                                                    const float sg[3]) {
+                                                    const float sg[4]) {
   constexpr int LPR = D / 16;
   float hs[2];
 #pragma unroll
@@ -124,11 +124,12 @@ __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* 
     q2[0] = q2[0] + q2[2];
     q2[4] = q2[4] + q2[6];
     hs[hf] = q2[0] + q2[4];
-    // strides 8 .. D/4: lanes li ^ 1, li ^ 2, (li ^ 4); the sum of a pair
-    // is the same in both lanes
+    // strides 8 .. D/4: lanes li ^ 1, li ^ 2, li ^ 4, li ^ 8; the sum of a
+    // pair is the same in both lanes
     if constexpr (LPR >= 2) hs[hf] = hs[hf] + dpp_xor<1>(hs[hf]);
     if constexpr (LPR >= 4) hs[hf] = hs[hf] + dpp_xor<2>(hs[hf]);
     if constexpr (LPR >= 8) hs[hf] = hs[hf] + dpp_xor<4>(hs[hf]);
+    if constexpr (LPR >= 16) hs[hf] = hs[hf] + dpp_xor<8>(hs[hf]);
   }
   const float nrm = __builtin_sqrtf(hs[0] + hs[1]);
   float y[16];
@@ -146,7 +147,8 @@ __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* 
     for (int j = 0; j < 16; ++j) y[j] = v[j];
   }
   fwht_row<LPR>(y, sg);
-  const float rs = D == 128 ? 0.0883883461356163f : 0.125f;  // fp32 1/sqrt(D)
+  // fp32 1/sqrt(D)
+  const float rs = D == 128 ? 0.0883883461356163f : (D == 64 ? 0.125f : 0.0625f);
   const float wn = nrm > 0.0f ? rs / nrm : 0.0f;
   uint32_t q[16];
   if (fast) {  // uniform
@@ -200,9 +202,9 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
   if constexpr (KB != 8) {
     if (!values) fast = centroid_thresholds<NC>(cen, a.centroids, thr);
   }
-  float sg[3];
+  float sg[4];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
+  for (int k = 0; k < 4; ++k) sg[k] = (li >> k) & 1 ? -1.0f : 1.0f;
 
   float x[R][16];
   int64_t slot[R];
@@ -248,6 +250,29 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
       }
     }
     // ---- values ----
+    if (a.vb == 8) {  // FP8 values (uniform): D E4M3 codes, no scale or zero
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float c0 = __builtin_amdgcn_fmed3f(v[2 * j], -448.0f, 448.0f);
+        const float c1 = __builtin_amdgcn_fmed3f(v[2 * j + 1], -448.0f, 448.0f);
+        const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false) & 0xFFFFu;
+        if (j & 1) w[j >> 1] |= pk << 16;
+        else w[j >> 1] = pk;
+      }
+      // the value region starts at an even byte (KPS is D or ceil(D*b/8) + 2)
+      uint16_t* v0 = reinterpret_cast<uint16_t*>(s + a.kps + 8 * li);
+      uint16_t* v1 = reinterpret_cast<uint16_t*>(s + a.kps + D / 2 + 8 * li);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        v0[2 * k] = (uint16_t)w[k];
+        v0[2 * k + 1] = (uint16_t)(w[k] >> 16);
+        v1[2 * k] = (uint16_t)w[2 + k];
+        v1[2 * k + 1] = (uint16_t)(w[2 + k] >> 16);
+      }
+      for (int i = a.kps + a.vdb + li; i < a.slot_bytes; i += LPR) s[i] = 0;
+      continue;
+    }
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) {
@@ -313,9 +338,14 @@ hipError_t launch_write_tq(const TqWriteParams& p, hipStream_t st) {
   a.slot_bytes = p.slot_bytes;
   a.key_fmt = p.key_fmt;
   a.kb = p.key_fmt == KF_MSE3 ? 3 : (p.key_fmt == KF_MSE4 ? 4 : 8);
-  a.vb = p.val_fmt == VF_U3 ? 3 : 4;
+  a.vb = p.val_fmt == VF_U3 ? 3 : (p.val_fmt == VF_U4 ? 4 : 8);
   a.kps = p.kps;
   a.vdb = p.vdb;
+  if (p.d == 256) {
+    if (p.dtype == TQ_DT_BF16) return launch<256, TQ_DT_BF16>(a, st);
+    if (p.dtype == TQ_DT_F16) return launch<256, TQ_DT_F16>(a, st);
+    return launch<256, TQ_DT_F32>(a, st);
+  }
   if (p.d == 128) {
     if (p.dtype == TQ_DT_BF16) return launch<128, TQ_DT_BF16>(a, st);
     if (p.dtype == TQ_DT_F16) return launch<128, TQ_DT_F16>(a, st);

@@ -171,3 +171,14 @@ def test_tq_writer_validation(L):
     assert f(16, 16, tq.DTYPE_BF16, 5, 8, 128, tq.KEY_FP8, tq.VAL_U4, 16, None, None, 8,
              208, 4, 16, None) == tq.TQ_EINVAL  # misaligned cache
     assert "kv_cache" in tq.last_error()
+
+
+def test_tq_slot_bytes_match_the_oracle():
+    """The library's slot sizes equal the oracle's for every TurboQuant key
+    and value format (FP8 values included) at D = 64, 128, 256."""
+    import oracle
+    for d in (64, 128, 256):
+        for kf in (tq.KEY_FP8, tq.KEY_MSE3, tq.KEY_MSE4):
+            for vf in (tq.VAL_U3, tq.VAL_U4, tq.VAL_FP8):
+                assert tq.tq_slot_bytes(d, kf, vf) == oracle.tq_slot_bytes(d, kf, vf), (d, kf, vf)
+    assert tq.tq_slot_bytes(128, tq.KEY_FP8, 4) == -1

@@ -378,3 +378,43 @@ def test_tq_fp8_u4_query_groups_of_five_to_eight(hq, hk):
     ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
     got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT)
     assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+
+
+
+# ---------------------------------------------------------------------------
+# Read-side variants on the generic kernel: FP8 values, D = 256
+
+N2_FMTS = [(oracle.KEY_FP8, oracle.VAL_FP8), (oracle.KEY_MSE3, oracle.VAL_FP8),
+           (oracle.KEY_MSE4, oracle.VAL_FP8), (oracle.KEY_MSE4, oracle.VAL_U3)]
+
+
+@pytest.mark.parametrize("fmt", N2_FMTS, ids=[str(f) for f in N2_FMTS])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_tq_fp8_values_and_head_dims(fmt, d):
+    seq = [0, 1, 77, 300]
+    w = W.custom_decode_workload(370 + d + 3 * fmt[0] + fmt[1], len(seq), 8, 2, d, 16, 3, seq, 4, "bf16")
+    rs = None if fmt[0] == oracle.KEY_FP8 else W.rht_signs(d, round_idx=6)
+    cache, cen = tq_case(w, *fmt, rot_signs=rs)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, rs, *fmt, 0,
+                                    w.num_splits, w.sm_scale)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, rot_signs=rs)
+    assert_close(got, ref, lse, ref_lse, "fmt %s d=%d" % (fmt, d))
+
+
+@pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3)],
+                         ids=["fp8_u4", "mse3_u3"])
+@pytest.mark.parametrize("norm_correction", [False, True])
+def test_tq_head_dim_256_shapes(fmt, norm_correction):
+    """D = 256 on the formats the matrix-core kernels take at D = 128 (the
+    generic kernel serves D = 256), g from 1 to 8, norm correction."""
+    if fmt[0] == oracle.KEY_FP8 and norm_correction:
+        pytest.skip("norm correction applies to centroid keys only")
+    for (B, hq, hk, seq, S) in [(2, 8, 8, [300, 1], 4), (3, 16, 2, [129, 0, 640], 5)]:
+        w = W.custom_decode_workload(380 + hq + S, B, hq, hk, 256, 16, S, seq, 3, "bf16")
+        cache, cen = tq_case(w, *fmt)
+        q = W.query(w, bf16_valued=True)
+        ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, *fmt,
+                                        int(norm_correction), S, w.sm_scale)
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, norm_correction=norm_correction)
+        assert_close(got, ref, lse, ref_lse, "fmt %s B=%d" % (fmt, B))

@@ -225,3 +225,30 @@ def test_tq_encode_centroid_tables(case):
     slots = rng.permutation(T).astype(np.int64)
     cen = _table_cases(d)[case]
     _encode_both(k, v, "f32", slots, 6, 16, hk, d, oracle.KEY_MSE3, oracle.VAL_U3, cen=cen)
+
+
+
+N2_FMTS = [(oracle.KEY_FP8, oracle.VAL_FP8), (oracle.KEY_MSE3, oracle.VAL_FP8),
+           (oracle.KEY_MSE4, oracle.VAL_FP8)]
+
+
+@pytest.mark.parametrize("fmt", N2_FMTS, ids=[str(f) for f in N2_FMTS])
+@pytest.mark.parametrize("d,hk,T", [(128, 4, 300), (64, 3, 257), (256, 2, 129)])
+def test_tq_encode_fp8_values_bit_exact(fmt, d, hk, T):
+    """FP8 values (D E4M3 codes after the key region, no scale or zero)."""
+    wl = W.write_workload(num_tokens=T, hk=hk, d=d, block_size=16, skip_frac=0.1, dtype="bf16",
+                          wid=80 + d + hk + 7 * fmt[0])
+    _encode_both(wl["key"], wl["value"], "bf16", wl["slot_mapping"], wl["num_blocks"], 16, hk, d,
+                 *fmt)
+
+
+@pytest.mark.parametrize("fmt", TQ_FMTS, ids=[str(f) for f in TQ_FMTS])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tq_encode_head_dim_256(fmt, dtype):
+    """D = 256: sixteen lanes per row; rot signs on centroid keys."""
+    d, hk, T = 256, 2, 133
+    wl = W.write_workload(num_tokens=T, hk=hk, d=d, block_size=16, skip_frac=0.05, dtype=dtype,
+                          wid=90 + 7 * fmt[0] + fmt[1])
+    rs = None if fmt[0] == oracle.KEY_FP8 else W.rht_signs(d, round_idx=5)
+    _encode_both(wl["key"], wl["value"], dtype, wl["slot_mapping"], wl["num_blocks"], 16, hk, d,
+                 *fmt, rot_signs=rs)
