@@ -17,7 +17,9 @@ stage 2 kernels), timed with HIP events on the stream it runs on.
 bounded sample of the same step on the host cores.
 
 Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
-tq_mixed_b, write (65536 tokens x 8 heads x 128 bf16), tq_write_a /
+tq_mixed_b, tq_fp8_values (C3's shape, FP8 keys and values),
+tq_mixed_b_d256 (C3B's formats at D=256), write (65536 tokens x 8 heads x
+128 bf16), tq_write_a /
 tq_write_b (the TurboQuant slot writer on the same rows), fwht (1,048,576
 rows), copy (device copy used to calibrate the HBM byte counters).
 """
@@ -312,49 +314,67 @@ def run_other(args, torch, tq, W):
         t = _time_loop(torch, stream, lambda i: b.copy_(a), args.warmup, args.steps)
         line = dict(workload="copy: device-to-device copy of 512 MiB", us=t * 1e6,
                     read_bytes=n, write_bytes=n, TBps=2 * n / t / 1e12)
-    elif name in ("tq_mixed_a", "tq_mixed_b"):
-        w = W.decode_workload("tq_mixed")
-        fmt = (tq.KEY_FP8, tq.VAL_U4) if name.endswith("a") else (tq.KEY_MSE3, tq.VAL_U3)
+    elif name in TQ_DECODES:
+        fmt, d = TQ_DECODES[name]
+        fmt = tuple(getattr(tq, f) for f in fmt)
+        w = W.decode_workload("tq_mixed", d=d)
         sb = tq.tq_slot_bytes(w.d, *fmt)
         shape = (w.num_blocks, w.block_size, w.hk, sb)
         nbytes_cache = int(np.prod(shape))
         ncopies = max(2, -(-512 * 2 ** 20 // nbytes_cache) + 1)
         g = torch.Generator(device=dev)
         g.manual_seed(3)
+        kb = {tq.KEY_FP8: 8, tq.KEY_MSE3: 3, tq.KEY_MSE4: 4}[fmt[0]]
+        vb = {tq.VAL_U3: 3, tq.VAL_U4: 4, tq.VAL_FP8: 8}[fmt[1]]
+        kps = w.d if fmt[0] == tq.KEY_FP8 else (w.d * kb + 7) // 8 + 2
+        vdb = (w.d * vb + 7) // 8
         caches = []
         for c in range(ncopies):
             cache = torch.randint(0, 256, shape, dtype=torch.uint8, device=dev, generator=g)
             if fmt[0] == tq.KEY_FP8:  # no NaN codes in the key bytes
                 cache[..., :w.d] &= 0x77
+            if fmt[1] == tq.VAL_FP8:  # nor in the value bytes
+                cache[..., kps:kps + w.d] &= 0x77
             # fp16 scale / zero / norm fields: small positive values
-            kps = w.d if fmt[0] == tq.KEY_FP8 else (w.d * 3 + 7) // 8 + 2
-            vdb = (w.d * (4 if fmt[1] == tq.VAL_U4 else 3) + 7) // 8
-            for off in ([kps + vdb, kps + vdb + 2] + ([kps - 2] if fmt[0] != tq.KEY_FP8 else [])):
+            offs = ([kps + vdb, kps + vdb + 2] if fmt[1] != tq.VAL_FP8 else []) + \
+                ([kps - 2] if fmt[0] != tq.KEY_FP8 else [])
+            for off in offs:
                 cache[..., off] = 0x00
                 cache[..., off + 1] = 0x2C
             caches.append(cache)
         q = torch.from_numpy(W.query(w, bf16_valued=True)).to(dev)
         bt = torch.from_numpy(w.block_table).to(dev)
         sl = torch.from_numpy(w.seq_lens).to(dev)
-        cen = torch.linspace(-0.2, 0.2, 8, device=dev)
+        cen = torch.linspace(-0.2, 0.2, 1 << kb, device=dev) if fmt[0] != tq.KEY_FP8 else None
         ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.hk, w.d, w.num_splits) // 4,
                          dtype=torch.float32, device=dev)
         calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
-                                   key_fmt=fmt[0], val_fmt=fmt[1],
-                                   centroids=cen if fmt[0] != tq.KEY_FP8 else None,
+                                   key_fmt=fmt[0], val_fmt=fmt[1], centroids=cen,
                                    workspace=ws)[0] for c in caches]
         t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
-        slot_used = (w.d + w.d // 2 + 4) if fmt[0] == tq.KEY_FP8 else (w.d * 3 // 8 + 2 + w.d * 3 // 8 + 4)
+        slot_used = kps + vdb + (0 if fmt[1] == tq.VAL_FP8 else 4)  # padding not counted
         kv = int(w.seq_lens.sum()) * w.hk * slot_used
         parts = w.B * w.hq * w.num_splits * (w.d + 1) * 8
         nbytes = kv + parts + w.B * w.hq * (8 * w.d + 4)
-        line = dict(workload="%s: B=16 Hq=32 Hk=4 D=128 seq 16384 S=32" % name, us=t * 1e6,
+        line = dict(workload="%s: B=16 Hq=32 Hk=4 D=%d seq 16384 S=32, %s keys + %s values" % (
+                        name, w.d, TQ_KEY_NAMES[fmt[0]], TQ_VAL_NAMES[fmt[1]]), us=t * 1e6,
                     algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
     else:
         raise SystemExit("unknown workload %s" % name)
     line.update(steps=args.steps, warmup=args.warmup)
     print(json.dumps(line), flush=True)
+
+
+# TurboQuant decode workloads: C3's shape with the given slot format and D
+TQ_DECODES = {
+    "tq_mixed_a": (("KEY_FP8", "VAL_U4"), 128),
+    "tq_mixed_b": (("KEY_MSE3", "VAL_U3"), 128),
+    "tq_fp8_values": (("KEY_FP8", "VAL_FP8"), 128),
+    "tq_mixed_b_d256": (("KEY_MSE3", "VAL_U3"), 256),
+}
+TQ_KEY_NAMES = {1: "FP8", 2: "3-bit centroid", 3: "4-bit centroid"}
+TQ_VAL_NAMES = {1: "3-bit uniform", 2: "4-bit uniform", 3: "FP8"}
 
 
 def main():

@@ -102,14 +102,15 @@ def _page_tables(wid, B, seq_lens, block_size, max_blocks, num_blocks=None):
     return nb, bt, slot_mapping
 
 
-def decode_workload(name: str) -> DecodeWorkload:
+def decode_workload(name: str, d: int = 128) -> DecodeWorkload:
     """Shapes of the INT4 and TurboQuant decode workloads.
 
     tiny_int4      B=2 Hq=4 Hk=1 D=64 bs=16 seq {37,100}, 32-page pool, S=4, f16 K/V
     llama8b_int4   B=32 Hq=32 Hk=8 D=128 bs=16 seq ~ U{1024..8192}, S=8, bf16 K/V
     llama8b_int4_8k  as above with every seq_len = 8192
     long_int4      B=1 Hq=64 Hk=8 D=128 bs=64 seq 131072, S=64
-    tq_mixed       B=16 Hq=32 Hk=4 D=128 bs=16 seq 16384, S=32
+    tq_mixed       B=16 Hq=32 Hk=4 D=128 bs=16 seq 16384, S=32 (d selects
+                   another head dimension for the same shape)
     """
     if name == "tiny_int4":
         seq = np.array([37, 100], np.int32)
@@ -137,7 +138,7 @@ def decode_workload(name: str) -> DecodeWorkload:
     if name == "tq_mixed":
         seq = np.full(16, 16384, np.int32)
         nb, bt, sm = _page_tables(3, 16, seq, 16, 1024)
-        return DecodeWorkload(name, 3, 16, 32, 4, 128, 16, 32, seq, nb, 1024, bt, sm)
+        return DecodeWorkload(name, 3, 16, 32, 4, d, 16, 32, seq, nb, 1024, bt, sm)
     raise KeyError(name)
 
 
