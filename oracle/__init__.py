@@ -91,6 +91,12 @@ def lib():
             L.orc_fp8_pow2_scale.restype = f32
             L.orc_fp8_pow2_scale.argtypes = [f32]
             L.orc_convert.argtypes = [i32, C.c_void_p, C.c_void_p, i64]
+            L.orc_exp_f32.restype = f32
+            L.orc_exp_f32.argtypes = [f32]
+            L.orc_kpool_compress_and_write.restype = i32
+            L.orc_kpool_compress_and_write.argtypes = [
+                P(u16), C.c_void_p, i32, P(f32), P(i64), P(u8), i64, i32, i32,
+                P(u8), i64, i32, i32, P(u8), P(f32)]
             _lib = L
     return _lib
 
@@ -285,3 +291,51 @@ def fwht128_quant_fp8(x_bf16_bits):
     if rows:
         lib().orc_fwht128_quant_fp8(_p(x, C.c_uint16), rows, _p(y, C.c_uint8), _p(s, C.c_float))
     return y, s
+
+
+# ------------------------------------------------ pooled key compression
+_SCORE_DT = {"f32": DT_F32, "f16": DT_F16, "bf16": DT_BF16}
+
+
+def exp_f32(x):
+    """e^x rounded to the nearest fp32 (the kpool softmax exponential)."""
+    return lib().orc_exp_f32(float(np.float32(x)))
+
+
+def kpool_compress_and_write(slot_k_bits, slot_score, ape, loc=None, kv_cache=None,
+                             write_mask=None, round_scale=True,
+                             return_compressed=False, score_dtype="f32"):
+    """[kpool] kpool_compress_and_write_cache on host arrays.
+
+    slot_k_bits: [n, P, 128] uint16 bf16 bit patterns. slot_score: [n, P, 128]
+    float32 for score_dtype "f32", else uint16 f16 / bf16 bit patterns.
+    ape: [P, 128] float32. loc: [n] int64 flat entry index. kv_cache:
+    [num_blocks, block_size, 132] uint8, written in place. write_mask: [n]
+    bool or None. Returns (codes [n, 128] u8, scales [n] f32) when
+    ``return_compressed``, else None.
+    """
+    k = np.ascontiguousarray(slot_k_bits, np.uint16)
+    n, P, hd = k.shape
+    sdt = _SCORE_DT[score_dtype]
+    sc = np.ascontiguousarray(slot_score, np.float32 if sdt == DT_F32 else np.uint16)
+    assert sc.shape == k.shape
+    a = np.ascontiguousarray(ape, np.float32)
+    assert a.shape == (P, hd)
+    lo = None if loc is None else np.ascontiguousarray(loc, np.int64)
+    wm = None if write_mask is None else np.ascontiguousarray(write_mask, np.uint8)
+    nb = bs = 0
+    if kv_cache is not None:
+        assert kv_cache.dtype == np.uint8 and kv_cache.flags.c_contiguous
+        nb, bs = kv_cache.shape[0], kv_cache.shape[1]
+        assert kv_cache.shape[2] == hd + 4
+    ck = cs = None
+    if return_compressed:
+        ck = np.zeros((n, hd), np.uint8)
+        cs = np.zeros(n, np.float32)
+    rc = lib().orc_kpool_compress_and_write(
+        _p(k, C.c_uint16), sc.ctypes.data, sdt, _p(a, C.c_float), _p(lo, C.c_int64),
+        _p(wm, C.c_uint8), n, P, hd, _p(kv_cache, C.c_uint8), nb, bs,
+        1 if round_scale else 0, _p(ck, C.c_uint8), _p(cs, C.c_float))
+    if rc != 0:
+        raise ValueError("kpool_compress_and_write: invalid arguments")
+    return (ck, cs) if return_compressed else None

@@ -718,6 +718,109 @@ void orc_fwht128_quant_fp8(const uint16_t* x_bf16, int64_t rows, uint8_t* y,
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* [kpool] _kpool_softmax_rotate_write_cache_kernel and its host wrapper     */
+/* kpool_compress_and_write_cache: one pool of P tokens -> one indexer entry. */
+/*   per dimension d: m_d = max_s (score[s,d] + ape[s,d]);                   */
+/*   p[s,d] = e^(score[s,d] + ape[s,d] - m_d); den_d = sum_s p[s,d];          */
+/*   acc_d = sum_s k[s,d] p[s,d]; x_d = fp32(bf16(acc_d / den_d));            */
+/*   then the Hadamard-128 path of fwht128_quant_fp8 (fp32 butterflies,      */
+/*   x fl32(1/sqrt(128)), bf16 round), absmax with a 1e-4 floor, and either  */
+/*   the power-of-two scale (round_scale) or absmax * fl32(1/448); codes are */
+/*   e4m3(clamp(x / scale, +-448)). Everything is fp32 with one rounding per */
+/*   operation, slots in order 0 .. P-1.                                     */
+/* Readings: the exponential is e^x rounded once to fp32 (orc_exp_f32); the  */
+/* per-slot accumulation acc += k * p is one fused multiply-add (the pages'  */
+/* compiler fuses that multiply-add by default); den += p is a plain add.    */
+/* ------------------------------------------------------------------------ */
+
+/* e^x rounded to the nearest fp32. The double exp is accurate to about one
+ * double ulp, far inside half an fp32 ulp, so one rounding to fp32 gives
+ * the correctly rounded value except when e^x lies within ~2^-52 relative
+ * of an fp32 rounding midpoint. */
+float orc_exp_f32(float x) { return (float)exp((double)x); }
+
+/* Indexer page of [kpool] kpool_compress_and_write_cache: a page of
+ * block_size entries is block_size * (head_dim + 4) bytes; entry t's head_dim
+ * E4M3 codes start at byte t * head_dim and its fp32 scale at byte
+ * block_size * head_dim + 4 t. Masked pools (write_mask[i] == 0) produce
+ * nothing; locations outside [0, num_blocks * block_size) are not written
+ * (reading, as for the other writers). Inputs: slot_k [n, P, 128] bf16 bits,
+ * slot_score [n, P, 128] in score_dtype (0 f32, 1 f16, 2 bf16), ape [P, 128]
+ * f32. Either output may be absent, not both; the compressed output is not
+ * taken together with a write mask (the pages refuse that pairing). */
+int orc_kpool_compress_and_write(const uint16_t* slot_k, const void* slot_score,
+                                 int score_dtype, const float* ape,
+                                 const int64_t* loc, const uint8_t* write_mask,
+                                 int64_t n_pools, int pool_size, int head_dim,
+                                 uint8_t* kv_cache, int64_t num_blocks,
+                                 int block_size, int round_scale,
+                                 uint8_t* compressed_k, float* compressed_scale) {
+  const float inv_sqrt128 = 0.08838834764831845f;
+  const float inv_448 = (float)(1.0 / 448.0);
+  if (head_dim != 128 || pool_size < 1 || n_pools < 0) return -1;
+  if (!kv_cache && !compressed_k) return -1;
+  if (write_mask && compressed_k) return -1;
+  if ((compressed_k == NULL) != (compressed_scale == NULL)) return -1;
+  if (kv_cache && (!loc || num_blocks < 0 || block_size < 1)) return -1;
+  const int64_t page_bytes = (int64_t)block_size * (head_dim + 4);
+  float x[128];
+  uint8_t q[128];
+  for (int64_t i = 0; i < n_pools; ++i) {
+    if (write_mask && !write_mask[i]) continue;
+    for (int d = 0; d < 128; ++d) {
+      float m = -INFINITY;
+      for (int s = 0; s < pool_size; ++s) {
+        int64_t e = (i * pool_size + s) * 128 + d;
+        float v = load_elem(slot_score, score_dtype, e) + ape[s * 128 + d];
+        if (v > m) m = v;
+      }
+      float acc = 0.0f, den = 0.0f;
+      for (int s = 0; s < pool_size; ++s) {
+        int64_t e = (i * pool_size + s) * 128 + d;
+        float v = load_elem(slot_score, score_dtype, e) + ape[s * 128 + d];
+        float p = orc_exp_f32(v - m);
+        den = den + p;
+        acc = fmaf(orc_bf16_to_f32(slot_k[e]), p, acc);
+      }
+      x[d] = orc_bf16_to_f32(orc_f32_to_bf16(acc / den));
+    }
+    orc_fwht_f32(x, 128);
+    float amax = 0.0f;
+    for (int d = 0; d < 128; ++d) {
+      x[d] = orc_bf16_to_f32(orc_f32_to_bf16(x[d] * inv_sqrt128));
+      if (fabsf(x[d]) > amax) amax = fabsf(x[d]);
+    }
+    float sc;
+    if (round_scale) {
+      sc = orc_fp8_pow2_scale(amax);
+    } else {
+      if (!(amax > 1e-4f)) amax = 1e-4f;
+      sc = amax * inv_448;
+    }
+    for (int d = 0; d < 128; ++d) {
+      float v = x[d] / sc;
+      if (v < -448.0f) v = -448.0f;
+      if (v > 448.0f) v = 448.0f;
+      q[d] = orc_f32_to_e4m3(v);
+    }
+    if (kv_cache) {
+      int64_t l = loc[i];
+      if (l >= 0 && l < num_blocks * (int64_t)block_size) {
+        int64_t pg = l / block_size, off = l % block_size;
+        uint8_t* page = kv_cache + pg * page_bytes;
+        memcpy(page + off * 128, q, 128);
+        memcpy(page + (int64_t)block_size * 128 + off * 4, &sc, 4);
+      }
+    }
+    if (compressed_k) {
+      memcpy(compressed_k + i * 128, q, 128);
+      compressed_scale[i] = sc;
+    }
+  }
+  return 0;
+}
+
 /* Element-wise array forms of the scalar converters (kind: 0 f32->bf16,
  * 1 bf16->f32, 2 f32->f16, 3 f16->f32, 4 f32->e4m3, 5 e4m3->f32). */
 void orc_convert(int kind, const void* in, void* out, int64_t n) {

@@ -80,6 +80,16 @@ float orc_fp8_pow2_scale(float absmax);
 void orc_fwht128_quant_fp8(const uint16_t* x_bf16, int64_t rows, uint8_t* y,
                            float* scale);
 
+/* ---- pooled-softmax key compression into the FP8 indexer page ---- */
+float orc_exp_f32(float x);
+int orc_kpool_compress_and_write(const uint16_t* slot_k, const void* slot_score,
+                                 int score_dtype, const float* ape,
+                                 const int64_t* loc, const uint8_t* write_mask,
+                                 int64_t n_pools, int pool_size, int head_dim,
+                                 uint8_t* kv_cache, int64_t num_blocks,
+                                 int block_size, int round_scale,
+                                 uint8_t* compressed_k, float* compressed_scale);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,6 +209,31 @@ def fwht_rows(rows=1048576, wid=6):
     return to_bits(x, "bf16")
 
 
+def kpool_workload(n_pools=262144, pool_size=4, score_dtype="bf16", block_size=64,
+                   mask_frac=0.0, skip_frac=0.0, score_offset=0.0, wid=11):
+    """Pooled key-compression workload: slot_k [n, P, 128] bf16 ~ N(0,1);
+    slot_score [n, P, 128] ~ N(score_offset, 1) in score_dtype; ape [P, 128]
+    f32 ~ N(0, 0.25); loc = a seeded permutation of the n entries of an
+    indexer cache of ceil(n / block_size) pages, with round(skip_frac*n)
+    seeded entries set to -1; write_mask = None, or True with probability
+    1 - mask_frac per pool."""
+    g = rng(wid, 1)
+    k = g.standard_normal((n_pools, pool_size, 128), dtype=np.float32)
+    sc = g.standard_normal((n_pools, pool_size, 128), dtype=np.float32) + np.float32(score_offset)
+    ape = (0.5 * rng(wid, 2).standard_normal((pool_size, 128))).astype(np.float32)
+    nb = max(1, (n_pools + block_size - 1) // block_size)
+    loc = rng(wid, 3).permutation(n_pools).astype(np.int64)
+    n_skip = int(round(skip_frac * n_pools))
+    if n_skip:
+        loc[rng(wid, 4).choice(n_pools, n_skip, replace=False)] = -1
+    mask = None
+    if mask_frac > 0:
+        mask = rng(wid, 5).random(n_pools) >= mask_frac
+    return dict(slot_k=to_bits(k, "bf16"), slot_score=to_bits(sc, score_dtype), ape=ape,
+                loc=loc, write_mask=mask, num_blocks=nb, block_size=block_size,
+                pool_size=pool_size, score_dtype=score_dtype)
+
+
 def random_tq_fp8_u4_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=8):
     """Random FP8-key / 4-bit-value TurboQuant slots: key bytes uniform over
     the finite E4M3 codes (0x7F / 0xFF, the NaN codes, are replaced by
