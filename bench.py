@@ -17,11 +17,12 @@ stage 2 kernels), timed with HIP events on the stream it runs on.
 bounded sample of the same step on the host cores.
 
 Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
-tq_mixed_b, tq_fp8_values (C3's shape, FP8 keys and values),
-tq_mixed_b_d256 (C3B's formats at D=256), write (65536 tokens x 8 heads x
-128 bf16), tq_write_a /
-tq_write_b (the TurboQuant slot writer on the same rows), fwht (1,048,576
-rows), copy (device copy used to calibrate the HBM byte counters).
+tq_mixed_b, tq_fp8_values (the tq_mixed shape with FP8 keys and values),
+tq_mixed_b_d256 (3-bit centroid keys and values at D=256), write (65536
+tokens x 8 heads x 128 bf16), tq_write_a / tq_write_b (the TurboQuant slot
+writer on the same rows), fwht (1,048,576 rows), kpool (pooled-softmax key
+compression: 262144 pools of 4 tokens), copy (device copy used to calibrate
+the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -307,6 +308,28 @@ def run_other(args, torch, tq, W):
         line = dict(workload="fwht: fwht128_quant_fp8 1048576 rows x 128 bf16", us=t * 1e6,
                     algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
+    elif name == "kpool":
+        wl = W.kpool_workload()
+        n, P, hd = wl["slot_k"].shape
+        bs = wl["block_size"]
+        per = n * P * hd * 2 * 2 + wl["num_blocks"] * bs * (hd + 4)
+        ncopies = max(2, -(-1024 * 2 ** 20 // per))
+        sk = torch.from_numpy(wl["slot_k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ss = torch.from_numpy(wl["slot_score"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ape = torch.from_numpy(wl["ape"]).to(dev)
+        loc = torch.from_numpy(wl["loc"]).to(dev)
+        calls = []
+        for c in range(ncopies):
+            cache = torch.zeros(wl["num_blocks"], bs, hd + 4, dtype=torch.uint8, device=dev)
+            calls.append(tq.prepare_kpool(cache, sk.clone(), ss.clone(), ape, loc))
+        t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
+        # per pool: P*128 bf16 keys and scores read, its location, one entry
+        # (128 codes + 4-byte scale) written; the [P, 128] bias once
+        nbytes = n * (P * hd * 2 * 2 + 8 + hd + 4) + P * hd * 4
+        line = dict(workload="kpool: tq_kpool_compress_and_write_cache %d pools x %d tokens x %d, "
+                             "bf16 keys and scores -> FP8 indexer entries (block %d)" % (n, P, hd, bs),
+                    us=t * 1e6, algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
+                    pct_peak=100 * nbytes / t / PEAK_HBM)
     elif name == "copy":
         n = 512 * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -366,7 +389,7 @@ def run_other(args, torch, tq, W):
     print(json.dumps(line), flush=True)
 
 
-# TurboQuant decode workloads: C3's shape with the given slot format and D
+# TurboQuant decode workloads: the tq_mixed shape (B=16 Hq=32 Hk=4, seq 16384) with the given slot format and D
 TQ_DECODES = {
     "tq_mixed_a": (("KEY_FP8", "VAL_U4"), 128),
     "tq_mixed_b": (("KEY_MSE3", "VAL_U3"), 128),

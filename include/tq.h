@@ -1,13 +1,16 @@
 /*
  * tq.h -- C ABI of the MI355X (gfx950) quantized paged-KV decode library.
  *
- * Four operations, each enqueued on the caller's HIP stream:
+ * Five operations, each enqueued on the caller's HIP stream:
  *   tq_reshape_and_cache_int4  randomized Hadamard rotation + INT4 cache write
  *   tq_encode_and_cache        TurboQuant combined-slot cache write (FP8 or
  *                              centroid keys, uniform 3/4-bit values)
  *   tq_decode_attention        split-KV decode attention over a paged,
  *                              sub-byte-quantized cache (stage 1 + stage 2)
  *   fwht128_quant_fp8          Hadamard-128 + power-of-two-scale FP8 quantizer
+ *   tq_kpool_compress_and_write_cache
+ *                              pooled-softmax key compression into the FP8
+ *                              indexer page
  *
  * Sources (web pages of a vLLM fork, cited by title and section):
  *   int4_per_token_head.py       reshape_and_cache_int4, unified_attention_int4,
@@ -15,7 +18,9 @@
  *                                single_rht, fast_hadamard_transform
  *   triton_turboquant_decode.py  triton_turboquant_decode_attention,
  *                                _tq_decode_stage1 (and its stage-2 launch)
- *   kpool_compress.py            fwht128_quant_fp8, _fwht_quant_kernel
+ *   kpool_compress.py            fwht128_quant_fp8, _fwht_quant_kernel,
+ *                                kpool_compress_and_write_cache,
+ *                                _kpool_softmax_rotate_write_cache_kernel
  *
  * Conventions for every entry point
  *   - Pointers named "device" are HIP device pointers owned by the caller; the
@@ -250,6 +255,48 @@ int tq_decode_attention(const tq_decode_args* args, void* stream);
  */
 int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
                       float* scale, void* stream);
+
+/*
+ * Pooled-softmax key compression into the FP8 indexer page (kpool_compress.py,
+ * kpool_compress_and_write_cache and _kpool_softmax_rotate_write_cache_kernel).
+ * One entry per pool of pool_size tokens (P). Per pool i and dimension d:
+ *   v[s] = score[i,s,d] + ape[s,d]           (fp32; s = 0 .. P-1)
+ *   m = max_s v[s]; p[s] = e^(v[s] - m)     (e^x rounded to nearest fp32)
+ *   den = sum_s p[s]; acc = sum_s k[i,s,d] * p[s]   (fp32, slot order, the
+ *                                           product-sum one fused multiply-add)
+ *   x[d] = fp32(bf16(acc / den))
+ * then x = fp32(bf16(FWHT(x) * fl(1/sqrt 128))) as in fwht128_quant_fp8,
+ *   absmax = max(max|x|, 1e-4); scale = 2^ceil(log2(fl(absmax * fl(1/448))))
+ *   when round_scale, else fl(absmax * fl(1/448));
+ *   codes = e4m3_rne(clamp(x / scale, -448, 448)).
+ * Bit-exact function of the inputs.
+ *   slot_k      device [n_pools, pool_size, head_dim] bf16, 16-B aligned
+ *   slot_score  device [n_pools, pool_size, head_dim] in score_dtype
+ *               (TQ_DTYPE_F32 / F16 / BF16), 16-B aligned
+ *   ape         device [pool_size, head_dim] f32 position bias, 16-B aligned
+ *   loc         device [n_pools] int64 flat entry index (page = loc /
+ *               block_size, row = loc % block_size); needed with kv_cache.
+ *               Entries outside [0, num_blocks * block_size) are not written.
+ *   write_mask  device [n_pools] u8 (0: the pool writes nothing), or NULL
+ *   head_dim    must be 128 (TQ_ENOTSUP otherwise)
+ *   kv_cache    device [num_blocks, block_size, head_dim + 4] u8, or NULL: a
+ *               page holds the block_size entries' codes first (128 B each,
+ *               row order), then their fp32 scales at byte block_size * 128
+ *   round_scale nonzero: power-of-two scales
+ *   compressed_k, compressed_scale
+ *               device [n_pools, head_dim] E4M3 (8-B aligned) and [n_pools]
+ *               f32, both or neither; every pool's entry is returned there
+ *               (not allowed together with write_mask)
+ * At least one of kv_cache and compressed_k is required. n_pools == 0
+ * returns TQ_OK without launching. Pools with equal loc race.
+ */
+int tq_kpool_compress_and_write_cache(const void* slot_k, const void* slot_score,
+                                      int32_t score_dtype, const float* ape, const int64_t* loc,
+                                      const uint8_t* write_mask, int64_t n_pools,
+                                      int32_t pool_size, int32_t head_dim, uint8_t* kv_cache,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t round_scale, uint8_t* compressed_k,
+                                      float* compressed_scale, void* stream);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,9 @@ in the library's HIP kernels. torch supplies device memory and streams.
     tq_encode_and_cache         TurboQuant combined-slot cache write
     tq_decode_attention         split-KV decode (stage 1 + stage 2)
     fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
+    tq_kpool_compress_and_write_cache
+                                pooled-softmax key compression into the
+                                FP8 indexer page
 
 The library is loaded on first use; when it is missing or cannot be loaded
 the call raises (there is no fallback implementation).
@@ -72,6 +75,10 @@ SYMBOLS = {
     "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "tq_kpool_compress_and_write_cache": (C.c_int, [
+        C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+        C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
+        C.c_void_p, C.c_void_p]),
 }
 
 
@@ -316,3 +323,69 @@ def fwht128_quant_fp8(x, y=None, scale=None, stream=None):
         raise ValueError("y must be [rows, 128], scale [rows, 1]")
     _check(lib().fwht128_quant_fp8(_ptr(x), rows, _ptr(y), _ptr(scale), _stream(stream, x.device)))
     return y, scale
+
+
+def prepare_kpool(kv_cache, slot_k, slot_score, ape, loc, *, write_mask=None, round_scale=True,
+                  compressed_k=None, compressed_scale=None):
+    """Validate and marshal a tq_kpool_compress_and_write_cache call (see
+    Prepared). kv_cache may be None when compressed_k/compressed_scale are
+    given."""
+    if slot_k.dim() != 3:
+        raise ValueError("slot_k must be [n_pools, pool_size, head_dim]")
+    n, P, hd = slot_k.shape
+    _need(slot_k, torch.bfloat16, "slot_k")
+    if slot_score.dtype not in _DT:
+        raise TypeError("unsupported slot_score dtype %s" % slot_score.dtype)
+    _need(slot_score, slot_score.dtype, "slot_score")
+    _need(ape, torch.float32, "ape")
+    if slot_score.shape != slot_k.shape or tuple(ape.shape) != (P, hd):
+        raise ValueError("slot_score must match slot_k, ape must be [pool_size, head_dim]")
+    keep = [slot_k, slot_score, ape]
+    nb = bs = 0
+    if kv_cache is not None:
+        _need(kv_cache, torch.uint8, "kv_cache")
+        if kv_cache.dim() != 3 or kv_cache.shape[2] != hd + 4:
+            raise ValueError("kv_cache must be [num_blocks, block_size, head_dim + 4]")
+        nb, bs = kv_cache.shape[0], kv_cache.shape[1]
+        _need(loc, torch.int64, "loc")
+        if loc.shape != (n,):
+            raise ValueError("loc must be [n_pools]")
+        keep += [kv_cache, loc]
+    if write_mask is not None:
+        if write_mask.dtype not in (torch.bool, torch.uint8):
+            raise TypeError("write_mask must be bool or uint8")
+        _need(write_mask, write_mask.dtype, "write_mask")
+        if write_mask.shape != (n,):
+            raise ValueError("write_mask must be [n_pools]")
+        keep.append(write_mask)
+    if compressed_k is not None:
+        if compressed_k.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError("compressed_k must be float8_e4m3fn or uint8")
+        _need(compressed_k, compressed_k.dtype, "compressed_k")
+        _need(compressed_scale, torch.float32, "compressed_scale")
+        if tuple(compressed_k.shape) != (n, hd) or compressed_scale.numel() != n:
+            raise ValueError("compressed_k must be [n_pools, head_dim], compressed_scale [n_pools]")
+        keep += [compressed_k, compressed_scale]
+    args = (_ptr(slot_k), _ptr(slot_score), _DT[slot_score.dtype], _ptr(ape),
+            _ptr(loc) if kv_cache is not None else None, _ptr(write_mask), n, P, hd,
+            _ptr(kv_cache), nb, bs, 1 if round_scale else 0, _ptr(compressed_k),
+            _ptr(compressed_scale))
+    return Prepared(lib().tq_kpool_compress_and_write_cache, args, keep)
+
+
+def tq_kpool_compress_and_write_cache(kv_cache, slot_k, slot_score, ape, loc, *, write_mask=None,
+                                      round_scale=True, return_compressed=False,
+                                      write_cache=True, stream=None):
+    """Compress each pool of slot_k [n, P, 128] bf16 (softmax over P of
+    slot_score + ape, per dimension) into one FP8 entry written at loc [n] of
+    the indexer cache [num_blocks, block_size, 132] u8. Returns (codes [n, 128]
+    float8_e4m3fn, scales [n] f32) when return_compressed, else None."""
+    n, _, hd = slot_k.shape
+    ck = cs = None
+    if return_compressed:
+        ck = torch.empty(n, hd, dtype=torch.float8_e4m3fn, device=slot_k.device)
+        cs = torch.empty(n, dtype=torch.float32, device=slot_k.device)
+    prepare_kpool(kv_cache if write_cache else None, slot_k, slot_score, ape, loc,
+                  write_mask=write_mask, round_scale=round_scale, compressed_k=ck,
+                  compressed_scale=cs).run(stream, slot_k.device)
+    return (ck, cs) if return_compressed else None

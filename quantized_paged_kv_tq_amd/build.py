@@ -22,7 +22,7 @@ ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc", "-I" + INCLUDE]
-NO_CONTRACT = {"write_int4.hip", "write_tq.hip", "fwht_fp8.hip"}
+NO_CONTRACT = {"write_int4.hip", "write_tq.hip", "fwht_fp8.hip", "kpool_compress.hip"}
 
 
 def sources():

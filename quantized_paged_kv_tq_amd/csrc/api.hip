@@ -9,6 +9,7 @@
 #include "tq.h"
 #include "balance.h"
 #include "tq_internal.h"
+#include "kpool.h"
 
 namespace {
 
@@ -172,6 +173,58 @@ int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3, float* 
   return launched(tqk::launch_fwht128_fp8(x_bf16, rows, y_e4m3, scale,
                                           static_cast<hipStream_t>(stream)),
                   "fwht128_quant_fp8");
+}
+
+int tq_kpool_compress_and_write_cache(const void* slot_k, const void* slot_score,
+                                      int32_t score_dtype, const float* ape, const int64_t* loc,
+                                      const uint8_t* write_mask, int64_t n_pools,
+                                      int32_t pool_size, int32_t head_dim, uint8_t* kv_cache,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t round_scale, uint8_t* compressed_k,
+                                      float* compressed_scale, void* stream) {
+  if (head_dim != 128) return fail(TQ_ENOTSUP, "head_dim %d (the Hadamard-128 entry needs 128)", head_dim);
+  if (n_pools < 0 || n_pools > ((int64_t)1 << 32)) return fail(TQ_EINVAL, "n_pools %lld", (long long)n_pools);
+  if (pool_size < 1 || pool_size > 65536) return fail(TQ_EINVAL, "pool_size %d", pool_size);
+  if (score_dtype != TQ_DTYPE_F32 && score_dtype != TQ_DTYPE_F16 && score_dtype != TQ_DTYPE_BF16)
+    return fail(TQ_EINVAL, "score_dtype %d", score_dtype);
+  if (!kv_cache && !compressed_k) return fail(TQ_EINVAL, "no output: kv_cache and compressed_k are both null");
+  if ((compressed_k == nullptr) != (compressed_scale == nullptr))
+    return fail(TQ_EINVAL, "compressed_k and compressed_scale go together");
+  if (write_mask && compressed_k) return fail(TQ_EINVAL, "a write mask excludes the compressed output");
+  if (kv_cache) {
+    if (block_size < 1 || num_blocks < 1) return fail(TQ_EINVAL, "num_blocks %lld, block_size %d",
+                                                      (long long)num_blocks, block_size);
+    if (num_blocks > ((int64_t)1 << 40) / ((int64_t)block_size * 132))
+      return fail(TQ_EINVAL, "cache too large");
+    if (!aligned(kv_cache, 4) || !aligned(loc, 8)) return fail(TQ_EINVAL, "misaligned kv_cache (4 B) or loc (8 B)");
+  }
+  if (n_pools == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (!slot_k || !slot_score || !ape) return fail(TQ_EINVAL, "null pointer argument");
+  if (kv_cache && !loc) return fail(TQ_EINVAL, "kv_cache needs loc");
+  if (!aligned(slot_k, 16) || !aligned(slot_score, 16) || !aligned(ape, 16))
+    return fail(TQ_EINVAL, "misaligned slot_k, slot_score or ape (16 B)");
+  if (compressed_k && (!aligned(compressed_k, 8) || !aligned(compressed_scale, 4)))
+    return fail(TQ_EINVAL, "misaligned compressed_k (8 B) or compressed_scale (4 B)");
+  tqk::KpoolParams p;
+  p.slot_k = static_cast<const uint16_t*>(slot_k);
+  p.slot_score = slot_score;
+  p.ape = ape;
+  p.loc = loc;
+  p.mask = write_mask;
+  p.cache = kv_cache;
+  p.ck = compressed_k;
+  p.cs = compressed_scale;
+  p.n_pools = n_pools;
+  p.num_blocks = kv_cache ? num_blocks : 0;
+  p.pool_size = pool_size;
+  p.block_size = kv_cache ? block_size : 1;
+  p.score_dtype = score_dtype;
+  p.round_scale = round_scale ? 1 : 0;
+  return launched(tqk::launch_kpool_compress(p, static_cast<hipStream_t>(stream)),
+                  "tq_kpool_compress_and_write_cache");
 }
 
 int tq_decode_attention(const tq_decode_args* a, void* stream) {

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
                           "tq_encode_and_cache", "tq_decode_workspace_bytes", "tq_slot_bytes",
-                          "tq_decode_attention", "fwht128_quant_fp8"}
+                          "tq_decode_attention", "fwht128_quant_fp8",
+                          "tq_kpool_compress_and_write_cache"}
     raw = C.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -182,3 +183,31 @@ def test_tq_slot_bytes_match_the_oracle():
             for vf in (tq.VAL_U3, tq.VAL_U4, tq.VAL_FP8):
                 assert tq.tq_slot_bytes(d, kf, vf) == oracle.tq_slot_bytes(d, kf, vf), (d, kf, vf)
     assert tq.tq_slot_bytes(128, tq.KEY_FP8, 4) == -1
+
+
+def test_kpool_validation(L):
+    f = L.tq_kpool_compress_and_write_cache
+    # (slot_k, slot_score, score_dtype, ape, loc, write_mask, n_pools, pool_size, head_dim,
+    #  kv_cache, num_blocks, block_size, round_scale, compressed_k, compressed_scale, stream)
+    ok = dict(sk=16, ss=16, dt=tq.DTYPE_BF16, ape=16, loc=16, wm=None, n=5, P=4, hd=128,
+              kc=16, nb=4, bs=64, rs=1, ck=None, cs=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["sk"], a["ss"], a["dt"], a["ape"], a["loc"], a["wm"], a["n"], a["P"], a["hd"],
+                 a["kc"], a["nb"], a["bs"], a["rs"], a["ck"], a["cs"], None)
+
+    assert call(n=0) == tq.TQ_OK and tq.last_error() == ""
+    assert call(hd=64) == tq.TQ_ENOTSUP
+    assert call(P=0) == tq.TQ_EINVAL
+    assert call(n=-1) == tq.TQ_EINVAL
+    assert call(dt=7) == tq.TQ_EINVAL
+    assert call(kc=None) == tq.TQ_EINVAL                    # no output at all
+    assert call(kc=None, ck=16) == tq.TQ_EINVAL             # compressed_scale missing
+    assert call(kc=None, ck=16, cs=16, wm=16) == tq.TQ_EINVAL  # mask with compressed output
+    assert call(loc=None) == tq.TQ_EINVAL                   # cache without locations
+    assert call(bs=0) == tq.TQ_EINVAL
+    assert call(sk=None) == tq.TQ_EINVAL
+    assert call(sk=8) == tq.TQ_EINVAL                       # misaligned
+    assert call(kc=None, ck=4, cs=16) == tq.TQ_EINVAL       # misaligned compressed_k
+    assert tq.last_error() != ""
