@@ -75,6 +75,10 @@ def lib():
                 P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32),
                 P(f32), i32, i32, i32, i32, i32, i32, f64, P(i32), i32,
                 P(f64), P(f64)]
+            L.orc_int4_prefill.restype = i32
+            L.orc_int4_prefill.argtypes = [
+                P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32), P(i32), i32,
+                P(f32), i32, i32, i32, i32, f64, i32, f64, P(f32), P(f64)]
             L.orc_tq_slot_bytes.restype = i32
             L.orc_tq_slot_bytes.argtypes = [i32, i32, i32]
             L.orc_lloyd_max_gaussian.argtypes = [i32, P(f64)]
@@ -227,6 +231,31 @@ def int4_decode(q, key_cache, value_cache, k_scale, v_scale, block_table,
 
 
 # ------------------------------------------------------------- TurboQuant
+def int4_prefill(q, key_cache, value_cache, k_scale, v_scale, block_table, cu_seqlens_q,
+                 seq_lens, signs, sm_scale, window=0, softcap=0.0, sinks=None):
+    """[int4] _attn_packed 2D mode: q [T, Hq, D] f32 -> out [T, Hq, D] f64.
+    window = 1 + window_size[0] (0: none); softcap 0: none; sinks [Hq] or None."""
+    q = np.ascontiguousarray(q, np.float32)
+    T, hq, d = q.shape
+    hk = key_cache.shape[2]
+    bt = np.ascontiguousarray(block_table, np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q, np.int32)
+    sl = np.ascontiguousarray(seq_lens, np.int32)
+    assert cu.shape == (sl.shape[0] + 1,) and cu[-1] == T
+    sk = None if sinks is None else np.ascontiguousarray(sinks, np.float32)
+    out = np.zeros((T, hq, d), np.float64)
+    rc = lib().orc_int4_prefill(
+        _p(q, C.c_float), _p(np.ascontiguousarray(key_cache), C.c_uint8),
+        _p(np.ascontiguousarray(value_cache), C.c_uint8), _p(np.ascontiguousarray(k_scale), C.c_float),
+        _p(np.ascontiguousarray(v_scale), C.c_float), _p(bt, C.c_int32), bt.shape[1],
+        _p(cu, C.c_int32), _p(sl, C.c_int32), sl.shape[0],
+        _p(np.ascontiguousarray(signs, np.float32), C.c_float), hq, hk, d, key_cache.shape[1],
+        float(sm_scale), int(window), float(softcap), _p(sk, C.c_float), _p(out, C.c_double))
+    if rc != 0:
+        raise ValueError("int4_prefill: invalid arguments")
+    return out
+
+
 def tq_slot_bytes(d, key_fmt, val_fmt):
     return lib().orc_tq_slot_bytes(d, key_fmt, val_fmt)
 

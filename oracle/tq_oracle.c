@@ -409,6 +409,80 @@ int orc_int4_decode(const float* q, const uint8_t* key_cache,
   return 0;
 }
 
+/* [int4] _attn_packed in its "2D" mode (prefill and multi-query), as
+ * unified_attention_int4 wraps it. cu_seqlens_q holds num_seqs + 1 offsets
+ * into the T query tokens; seq_lens the total key count of each sequence
+ * (context + queries), clamped to [0, max_blocks * block_size] as in decode.
+ * Query i of sequence b sits at absolute position pos = (seq_len -
+ * query_len) + i and sees keys t in [0, min(pos + 1, seq_len)) (causal),
+ * and, when window > 0 (window = 1 + window_size[0]), only those with
+ * pos - t < window. Per visible key:
+ *   s_t = (sm_scale / d) * q'.k'_t, then s_t <- c tanh(s_t / c) if c > 0;
+ * with sinks, sink_h joins the denominator only (reading of the absent
+ * init_softmax_M: the running max starts at sink_h with sum 1):
+ *   o' = sum_t e^{s_t} v'_t / (e^{sink_h} + sum_t e^{s_t});
+ * out = RHT^{-1}(o') / d = s * FWHT(o') / d. A query with no visible key
+ * gets out = 0 (with or without a sink). q [T, hq, d] f32; out [T, hq, d]. */
+int orc_int4_prefill(const float* q, const uint8_t* key_cache,
+                     const uint8_t* value_cache, const float* k_scale,
+                     const float* v_scale, const int32_t* block_table,
+                     int max_blocks, const int32_t* cu_seqlens_q,
+                     const int32_t* seq_lens, int num_seqs, const float* signs,
+                     int hq, int hk, int d, int block_size, double sm_scale,
+                     int window, double softcap, const float* sinks,
+                     double* out) {
+  if (d <= 0 || d > 1024 || (d & (d - 1)) != 0 || hk <= 0 || hq % hk != 0)
+    return -1;
+  double qr[1024], kbuf[1024], v[1024], o[1024];
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  for (int b = 0; b < num_seqs; ++b) {
+    int64_t qlen = (int64_t)cu_seqlens_q[b + 1] - cu_seqlens_q[b];
+    int64_t seq = seq_lens[b];
+    if (seq < 0) seq = 0;
+    if (seq > cap) seq = cap;
+    for (int64_t i = 0; i < qlen; ++i) {
+      int64_t tok = cu_seqlens_q[b] + i;
+      int64_t pos = seq - qlen + i;
+      int64_t hi = pos + 1 < seq ? pos + 1 : seq;
+      int64_t lo = 0;
+      if (window > 0 && pos - window + 1 > 0) lo = pos - window + 1;
+      for (int h = 0; h < hq; ++h) {
+        const float* qrow = q + ((size_t)tok * hq + h) * d;
+        for (int k = 0; k < d; ++k) qr[k] = (double)qrow[k] * (double)signs[k];
+        orc_fwht_f64(qr, d);
+        int4_ctx c = {key_cache, value_cache, k_scale, v_scale,
+                      block_table + (size_t)b * max_blocks, block_size, hk,
+                      h / (hq / hk), d, qr, sm_scale / d, kbuf};
+        double m = sinks ? (double)sinks[h] : -INFINITY;
+        for (int64_t t = lo; t < hi; ++t) {
+          double st = int4_score(&c, t);
+          if (softcap > 0) st = softcap * tanh(st / softcap);
+          if (st > m) m = st;
+        }
+        double l = sinks ? exp((double)sinks[h] - m) : 0.0;
+        for (int k = 0; k < d; ++k) o[k] = 0.0;
+        for (int64_t t = lo; t < hi; ++t) {
+          double st = int4_score(&c, t);
+          if (softcap > 0) st = softcap * tanh(st / softcap);
+          double pt = exp(st - m);
+          l += pt;
+          int4_value(&c, t, v);
+          for (int k = 0; k < d; ++k) o[k] += pt * v[k];
+        }
+        double* dst = out + ((size_t)tok * hq + h) * d;
+        if (hi <= lo) {
+          for (int k = 0; k < d; ++k) dst[k] = 0.0;
+          continue;
+        }
+        for (int k = 0; k < d; ++k) o[k] /= l;
+        orc_fwht_f64(o, d);
+        for (int k = 0; k < d; ++k) dst[k] = o[k] * (double)signs[k] / d;
+      }
+    }
+  }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* TurboQuant combined-slot cache ([tq]).                                    */
 /* key_fmt: 1 FP8 E4M3, 2 centroid 3-bit, 3 centroid 4-bit.                  */

@@ -59,6 +59,15 @@ int orc_int4_decode(const float* q, const uint8_t* key_cache,
                     const int32_t* rows, int n_rows,
                     double* out, double* lse);
 
+int orc_int4_prefill(const float* q, const uint8_t* key_cache,
+                     const uint8_t* value_cache, const float* k_scale,
+                     const float* v_scale, const int32_t* block_table,
+                     int max_blocks, const int32_t* cu_seqlens_q,
+                     const int32_t* seq_lens, int num_seqs, const float* signs,
+                     int hq, int hk, int d, int block_size, double sm_scale,
+                     int window, double softcap, const float* sinks,
+                     double* out);
+
 /* ---- TurboQuant combined-slot formats ---- */
 int orc_tq_slot_bytes(int d, int key_fmt, int val_fmt);
 void orc_lloyd_max_gaussian(int levels, double* centroids);

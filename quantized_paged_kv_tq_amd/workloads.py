@@ -186,6 +186,25 @@ def query(w: DecodeWorkload, bf16_valued: bool = False) -> np.ndarray:
     return q
 
 
+def prefill_queries(w: DecodeWorkload, query_lens, bf16_valued: bool = False):
+    """Multi-query (prefill) queries over a decode workload whose seq_lens
+    count context + query tokens: cu_seqlens_q [B + 1] int32 and q [T, Hq, D]
+    fp32 ~ N(0,1), T = sum(query_lens)."""
+    ql = np.asarray(query_lens, np.int64)
+    assert ql.shape == (w.B,)
+    cu = np.zeros(w.B + 1, np.int32)
+    cu[1:] = np.cumsum(ql)
+    q = rng(w.wid, 6).standard_normal((int(cu[-1]), w.hq, w.d), dtype=np.float32)
+    if bf16_valued:
+        q = bits_to_f32(to_bits(q, "bf16"), "bf16")
+    return cu, q
+
+
+def sink_values(w: DecodeWorkload, spread: float = 2.0):
+    """Per-query-head attention sinks [Hq] fp32 ~ U(-spread, spread)."""
+    return rng(w.wid, 7).uniform(-spread, spread, w.hq).astype(np.float32)
+
+
 def write_workload(num_tokens=65536, hk=8, d=128, block_size=16, skip_frac=0.05,
                    dtype="bf16", wid=5):
     """Cache-write workload: K/V [T, Hk, D], slot_mapping = a seeded
