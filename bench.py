@@ -21,8 +21,9 @@ tq_mixed_b, tq_fp8_values (the tq_mixed shape with FP8 keys and values),
 tq_mixed_b_d256 (3-bit centroid keys and values at D=256), write (65536
 tokens x 8 heads x 128 bf16), tq_write_a / tq_write_b (the TurboQuant slot
 writer on the same rows), fwht (1,048,576 rows), kpool (pooled-softmax key
-compression: 262144 pools of 4 tokens), copy (device copy used to calibrate
-the HBM byte counters).
+compression: 262144 pools of 4 tokens), prefill_int4 (multi-query INT4
+attention: 4 sequences of 1024 context + 1024 query tokens), copy (device
+copy used to calibrate the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -330,6 +331,33 @@ def run_other(args, torch, tq, W):
                              "bf16 keys and scores -> FP8 indexer entries (block %d)" % (n, P, hd, bs),
                     us=t * 1e6, algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
+    elif name == "prefill_int4":
+        # chunked prefill at the Llama-3-8B head shape: 4 sequences, each with
+        # 1024 cached context tokens and 1024 new query tokens
+        ctx, ql = np.full(4, 1024), np.full(4, 1024)
+        w = W.custom_decode_workload(12, 4, 32, 8, 128, 16, 1, ctx + ql)
+        cu, q = W.prefill_queries(w, ql)
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        shape = (w.num_blocks, w.block_size, w.hk, w.d // 2)
+        kc = torch.randint(0, 256, shape, dtype=torch.uint8, device=dev, generator=g)
+        vc = torch.randint(0, 256, shape, dtype=torch.uint8, device=dev, generator=g)
+        # scale words: |scale| in [2^-6, 2^-2) with a zero point in the low nibble
+        sc = torch.rand(shape[:3], device=dev, generator=g) * 0.24 + 0.016
+        ks = (sc.view(torch.int32) & ~0xF | 7).view(torch.float32)
+        vs = ks.clone()
+        call, out = tq.prepare_prefill(
+            torch.from_numpy(q).to(dev), kc, vc, torch.from_numpy(w.block_table).to(dev),
+            torch.from_numpy(cu).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+            k_scale_cache=ks, v_scale_cache=vs,
+            rht_signs=torch.from_numpy(W.rht_signs(w.d)).to(dev), sm_scale=w.sm_scale)
+        t = _time_loop(torch, stream, lambda i: call.run(sp), args.warmup, args.steps)
+        pairs = int(sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2 for c, n in zip(ctx, ql)))
+        flops = 4 * pairs * w.hq * w.d
+        line = dict(workload="prefill_int4: tq_prefill_attention_int4, 4 sequences x (1024 "
+                             "context + 1024 query tokens), Hq=32 Hk=8 D=128 bs=16, INT4 K/V",
+                    us=t * 1e6, query_tokens_per_s=float(ql.sum()) / t,
+                    visible_pairs=pairs, attention_TFLOPs=flops / t / 1e12)
     elif name == "copy":
         n = 512 * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)

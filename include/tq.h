@@ -1,13 +1,16 @@
 /*
  * tq.h -- C ABI of the MI355X (gfx950) quantized paged-KV decode library.
  *
- * Five operations, each enqueued on the caller's HIP stream:
+ * Six operations, each enqueued on the caller's HIP stream:
  *   tq_reshape_and_cache_int4  randomized Hadamard rotation + INT4 cache write
  *   tq_encode_and_cache        TurboQuant combined-slot cache write (FP8 or
  *                              centroid keys, uniform 3/4-bit values)
  *   tq_decode_attention        split-KV decode attention over a paged,
  *                              sub-byte-quantized cache (stage 1 + stage 2)
  *   fwht128_quant_fp8          Hadamard-128 + power-of-two-scale FP8 quantizer
+ *   tq_prefill_attention_int4  multi-query (prefill) attention over the INT4
+ *                              cache: causal, sliding window, softcap, sinks,
+ *                              fp32 or FP8 output
  *   tq_kpool_compress_and_write_cache
  *                              pooled-softmax key compression into the FP8
  *                              indexer page
@@ -255,6 +258,58 @@ int tq_decode_attention(const tq_decode_args* args, void* stream);
  */
 int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
                       float* scale, void* stream);
+
+/*
+ * Multi-query (prefill) attention over the INT4 caches (int4_per_token_head.py,
+ * _attn_packed in its 2D mode as unified_attention_int4 wraps it). The query
+ * tokens of num_seqs sequences are packed: sequence b owns tokens
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and has seq_lens[b] keys in the cache
+ * (context + its queries, clamped to max_blocks * block_size). Query i of
+ * sequence b sits at pos = seq_lens[b] - query_len + i and sees keys t with
+ * t <= pos and, when window > 0, pos - t < window (window = 1 +
+ * window_size[0]; 0 means none). With q' = RHT(q) = FWHT(s * q):
+ *   score_t = (sm_scale / D) * q'.k'_t      (k' the dequantized rotated key)
+ *   score_t <- softcap * tanh(score_t / softcap)   when softcap > 0
+ *   o' = sum_t e^{score_t} v'_t / (e^{sinks[h]} + sum_t e^{score_t})
+ *        (the sink term only when sinks != NULL)
+ *   out = s * FWHT(o') / D;  out = e4m3_rne(clamp(out * fl(1/output_scale[0]),
+ *        -448, 448)) when output_scale != NULL.
+ * A query with no visible key gets out = 0. GQA: kv head = h / (Hq / Hk).
+ *   query         device [num_tokens, Hq, D] f32
+ *   cu_seqlens_q  device [num_seqs + 1] int32, non-decreasing, last = num_tokens
+ *   seq_lens      device [num_seqs] int32
+ *   block_table   device [num_seqs, max_blocks] int32; entries outside
+ *                 [0, num_blocks) read as masked tokens
+ *   caches        as tq_reshape_and_cache_int4 writes them
+ *   rht_signs     device [D] +-1 f32
+ *   sinks         device [Hq] f32 or NULL; output_scale device [1] f32 or NULL
+ *   out           device [num_tokens, Hq, D]: f32, or u8 E4M3 codes when
+ *                 output_scale is set
+ * D = 64 or 128 (TQ_ENOTSUP otherwise). num_tokens == 0 returns TQ_OK
+ * without launching.
+ */
+typedef struct {
+  uint32_t struct_size; /* sizeof(tq_prefill_args) */
+  int32_t num_seqs, Hq, Hk, D, block_size, max_blocks;
+  int32_t window;       /* 1 + window_size[0]; 0: no window */
+  int64_t num_tokens, num_blocks;
+  float sm_scale;
+  float softcap;        /* 0: none */
+  const float* query;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const float* k_scale_cache;
+  const float* v_scale_cache;
+  const float* rht_signs;
+  const float* sinks;
+  const float* output_scale;
+  void* out;
+} tq_prefill_args;
+
+int tq_prefill_attention_int4(const tq_prefill_args* args, void* stream);
 
 /*
  * Pooled-softmax key compression into the FP8 indexer page (kpool_compress.py,

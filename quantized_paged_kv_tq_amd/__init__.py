@@ -8,6 +8,8 @@ in the library's HIP kernels. torch supplies device memory and streams.
     tq_encode_and_cache         TurboQuant combined-slot cache write
     tq_decode_attention         split-KV decode (stage 1 + stage 2)
     fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
+    tq_prefill_attention_int4   multi-query (prefill) attention over the
+                                INT4 cache
     tq_kpool_compress_and_write_cache
                                 pooled-softmax key compression into the
                                 FP8 indexer page
@@ -37,6 +39,19 @@ class TQError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__("%s (code %d)" % (msg, code))
         self.code = code
+
+
+class PrefillArgs(C.Structure):
+    _fields_ = [
+        ("struct_size", C.c_uint32), ("num_seqs", C.c_int32), ("Hq", C.c_int32),
+        ("Hk", C.c_int32), ("D", C.c_int32), ("block_size", C.c_int32),
+        ("max_blocks", C.c_int32), ("window", C.c_int32), ("num_tokens", C.c_int64),
+        ("num_blocks", C.c_int64), ("sm_scale", C.c_float), ("softcap", C.c_float),
+        ("query", C.c_void_p), ("cu_seqlens_q", C.c_void_p), ("seq_lens", C.c_void_p),
+        ("block_table", C.c_void_p), ("key_cache", C.c_void_p), ("value_cache", C.c_void_p),
+        ("k_scale_cache", C.c_void_p), ("v_scale_cache", C.c_void_p), ("rht_signs", C.c_void_p),
+        ("sinks", C.c_void_p), ("output_scale", C.c_void_p), ("out", C.c_void_p),
+    ]
 
 
 class DecodeArgs(C.Structure):
@@ -75,6 +90,7 @@ SYMBOLS = {
     "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "tq_prefill_attention_int4": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
     "tq_kpool_compress_and_write_cache": (C.c_int, [
         C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
         C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
@@ -389,3 +405,68 @@ def tq_kpool_compress_and_write_cache(kv_cache, slot_k, slot_score, ape, loc, *,
                   write_mask=write_mask, round_scale=round_scale, compressed_k=ck,
                   compressed_scale=cs).run(stream, slot_k.device)
     return (ck, cs) if return_compressed else None
+
+
+def prepare_prefill(query, key_cache, value_cache, block_table, cu_seqlens_q, seq_lens, *,
+                    k_scale_cache, v_scale_cache, rht_signs, sm_scale=None, window=0,
+                    softcap=0.0, sinks=None, output_scale=None, out=None):
+    """Validate and marshal a tq_prefill_attention_int4 call; returns (Prepared, out).
+    out is [T, Hq, D] f32, or float8_e4m3fn when output_scale ([1] f32) is given."""
+    T, hq, d = query.shape
+    _need(query, torch.float32, "query")
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _need(t, torch.uint8, n)
+    for t, n in ((k_scale_cache, "k_scale_cache"), (v_scale_cache, "v_scale_cache"),
+                 (rht_signs, "rht_signs")):
+        _need(t, torch.float32, n)
+    for t, n in ((block_table, "block_table"), (cu_seqlens_q, "cu_seqlens_q"),
+                 (seq_lens, "seq_lens")):
+        _need(t, torch.int32, n)
+    nb, bs, hk, _ = key_cache.shape
+    if tuple(key_cache.shape) != (nb, bs, hk, d // 2) or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shape must be [NB, bs, Hk, D/2]")
+    ns = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (ns + 1,) or block_table.dim() != 2 or block_table.shape[0] != ns:
+        raise ValueError("cu_seqlens_q must be [num_seqs + 1], block_table [num_seqs, max_blocks]")
+    keep = [query, key_cache, value_cache, block_table, cu_seqlens_q, seq_lens, k_scale_cache,
+            v_scale_cache, rht_signs]
+    if sinks is not None:
+        _need(sinks, torch.float32, "sinks")
+        if sinks.shape != (hq,):
+            raise ValueError("sinks must be [Hq]")
+        keep.append(sinks)
+    odt = torch.float32
+    if output_scale is not None:
+        _need(output_scale, torch.float32, "output_scale")
+        keep.append(output_scale)
+        odt = torch.float8_e4m3fn
+    if out is None:
+        out = torch.empty(T, hq, d, dtype=odt, device=query.device)
+    _need(out, odt, "out")
+    if tuple(out.shape) != (T, hq, d):
+        raise ValueError("out must be [T, Hq, D]")
+    keep.append(out)
+    a = PrefillArgs()
+    a.struct_size = C.sizeof(PrefillArgs)
+    a.num_seqs, a.Hq, a.Hk, a.D = ns, hq, hk, d
+    a.block_size, a.max_blocks, a.window = bs, block_table.shape[1], int(window)
+    a.num_tokens, a.num_blocks = T, nb
+    a.sm_scale = float(d ** -0.5 if sm_scale is None else sm_scale)
+    a.softcap = float(softcap)
+    a.query, a.cu_seqlens_q, a.seq_lens = _ptr(query), _ptr(cu_seqlens_q), _ptr(seq_lens)
+    a.block_table, a.key_cache, a.value_cache = _ptr(block_table), _ptr(key_cache), _ptr(value_cache)
+    a.k_scale_cache, a.v_scale_cache, a.rht_signs = (_ptr(k_scale_cache), _ptr(v_scale_cache),
+                                                     _ptr(rht_signs))
+    a.sinks, a.output_scale, a.out = _ptr(sinks), _ptr(output_scale), _ptr(out)
+    keep.append(a)
+    return Prepared(lib().tq_prefill_attention_int4, (C.byref(a),), keep), out
+
+
+def tq_prefill_attention_int4(query, key_cache, value_cache, block_table, cu_seqlens_q, seq_lens,
+                              *, stream=None, **kw):
+    """Multi-query (prefill) attention over the INT4 caches; returns out
+    [T, Hq, D] (f32, or float8_e4m3fn with output_scale)."""
+    call, out = prepare_prefill(query, key_cache, value_cache, block_table, cu_seqlens_q,
+                                seq_lens, **kw)
+    call.run(stream, query.device)
+    return out

@@ -10,6 +10,7 @@
 #include "balance.h"
 #include "tq_internal.h"
 #include "kpool.h"
+#include "prefill.h"
 
 namespace {
 
@@ -225,6 +226,66 @@ int tq_kpool_compress_and_write_cache(const void* slot_k, const void* slot_score
   p.round_scale = round_scale ? 1 : 0;
   return launched(tqk::launch_kpool_compress(p, static_cast<hipStream_t>(stream)),
                   "tq_kpool_compress_and_write_cache");
+}
+
+int tq_prefill_attention_int4(const tq_prefill_args* a, void* stream) {
+  if (!a) return fail(TQ_EINVAL, "null args");
+  if (a->struct_size < sizeof(tq_prefill_args))
+    return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size, sizeof(tq_prefill_args));
+  if (a->num_tokens < 0 || a->num_seqs < 0) return fail(TQ_EINVAL, "negative num_tokens or num_seqs");
+  if (a->D != 64 && a->D != 128) return fail(TQ_ENOTSUP, "D=%d (INT4 prefill supports 64, 128)", a->D);
+  if (a->Hk < 1 || a->Hq < a->Hk || a->Hq % a->Hk != 0)
+    return fail(TQ_EINVAL, "Hq=%d must be a positive multiple of Hk=%d", a->Hq, a->Hk);
+  if (a->block_size < 1 || a->max_blocks < 1 || a->num_blocks < 1)
+    return fail(TQ_EINVAL, "block_size, max_blocks and num_blocks must be positive");
+  if (a->window < 0) return fail(TQ_EINVAL, "window %d < 0", a->window);
+  if (!(a->softcap >= 0.0f) || a->softcap > 3.0e38f) return fail(TQ_EINVAL, "softcap must be finite and >= 0");
+  if (!(a->sm_scale == a->sm_scale) || a->sm_scale > 3.0e38f || a->sm_scale < -3.0e38f)
+    return fail(TQ_EINVAL, "sm_scale must be finite");
+  if (a->num_tokens == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (a->num_seqs < 1) return fail(TQ_EINVAL, "num_tokens > 0 with no sequence");
+  const int g = a->Hq / a->Hk;
+  const int G = g <= 1 ? 1 : (g <= 2 ? 2 : (g <= 4 ? 4 : 8));
+  const int64_t blocks = a->num_tokens * a->Hk * ((g + G - 1) / G);
+  if (blocks > 0x7FFFFFFF) return fail(TQ_EINVAL, "num_tokens * Hk too large for one launch");
+  if (!a->query || !a->cu_seqlens_q || !a->seq_lens || !a->block_table || !a->key_cache ||
+      !a->value_cache || !a->k_scale_cache || !a->v_scale_cache || !a->rht_signs || !a->out)
+    return fail(TQ_EINVAL, "null pointer argument");
+  if (!aligned(a->key_cache, 4) || !aligned(a->value_cache, 4) || !aligned(a->query, 4) ||
+      !aligned(a->k_scale_cache, 4) || !aligned(a->v_scale_cache, 4) ||
+      (!a->output_scale && !aligned(a->out, 4)))
+    return fail(TQ_EINVAL, "misaligned pointer (4 B)");
+  tqk::PrefillParams p;
+  p.q = a->query;
+  p.cu_seqlens = a->cu_seqlens_q;
+  p.seq_lens = a->seq_lens;
+  p.block_table = a->block_table;
+  p.kc = a->key_cache;
+  p.vc = a->value_cache;
+  p.ks = a->k_scale_cache;
+  p.vs = a->v_scale_cache;
+  p.rht_signs = a->rht_signs;
+  p.sinks = a->sinks;
+  p.output_scale = a->output_scale;
+  p.out = a->output_scale ? nullptr : static_cast<float*>(a->out);
+  p.out_fp8 = a->output_scale ? static_cast<uint8_t*>(a->out) : nullptr;
+  p.num_tokens = a->num_tokens;
+  p.num_blocks = a->num_blocks;
+  p.num_seqs = a->num_seqs;
+  p.hq = a->Hq;
+  p.hk = a->Hk;
+  p.d = a->D;
+  p.g = g;
+  p.block_size = a->block_size;
+  p.max_blocks = a->max_blocks;
+  p.window = a->window;
+  p.sm_scale = a->sm_scale;
+  p.softcap = a->softcap;
+  return launched(tqk::launch_prefill_int4(p, static_cast<hipStream_t>(stream)),
+                  "tq_prefill_attention_int4");
 }
 
 int tq_decode_attention(const tq_decode_args* a, void* stream) {

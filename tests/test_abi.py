@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
                           "tq_encode_and_cache", "tq_decode_workspace_bytes", "tq_slot_bytes",
                           "tq_decode_attention", "fwht128_quant_fp8",
-                          "tq_kpool_compress_and_write_cache"}
+                          "tq_kpool_compress_and_write_cache", "tq_prefill_attention_int4"}
     raw = C.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -211,3 +211,53 @@ def test_kpool_validation(L):
     assert call(sk=8) == tq.TQ_EINVAL                       # misaligned
     assert call(kc=None, ck=4, cs=16) == tq.TQ_EINVAL       # misaligned compressed_k
     assert tq.last_error() != ""
+
+
+def test_prefill_args_layout_matches_header(tmp_path):
+    fields = [f[0] for f in tq.PrefillArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "tq.h"\nint main(void){\n'
+                   + "".join('printf("%%zu\\n", offsetof(tq_prefill_args, %s));\n' % f for f in fields)
+                   + 'printf("%zu\\n", sizeof(tq_prefill_args));return 0;}\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    want = [getattr(tq.PrefillArgs, f).offset for f in fields] + [C.sizeof(tq.PrefillArgs)]
+    assert got == want
+
+
+def _pargs(**kw):
+    a = tq.PrefillArgs()
+    a.struct_size = C.sizeof(tq.PrefillArgs)
+    a.num_seqs, a.Hq, a.Hk, a.D = 2, 8, 2, 128
+    a.block_size, a.max_blocks, a.num_tokens, a.num_blocks = 16, 8, 10, 32
+    a.sm_scale = 0.088
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), tq.TQ_ENOTSUP),
+    (dict(D=256), tq.TQ_ENOTSUP),
+    (dict(Hq=6, Hk=4), tq.TQ_EINVAL),
+    (dict(Hk=0), tq.TQ_EINVAL),
+    (dict(block_size=0), tq.TQ_EINVAL),
+    (dict(window=-1), tq.TQ_EINVAL),
+    (dict(softcap=-1.0), tq.TQ_EINVAL),
+    (dict(softcap=float("nan")), tq.TQ_EINVAL),
+    (dict(num_seqs=0), tq.TQ_EINVAL),
+    (dict(struct_size=8), tq.TQ_EINVAL),
+    (dict(), tq.TQ_EINVAL),  # null device pointers
+])
+def test_prefill_rejects_invalid(L, kw, code):
+    a = _pargs(**kw)
+    assert L.tq_prefill_attention_int4(C.byref(a), None) == code
+    assert tq.last_error() != ""
+
+
+def test_prefill_empty_and_null(L):
+    assert L.tq_prefill_attention_int4(None, None) == tq.TQ_EINVAL
+    assert L.tq_prefill_attention_int4(C.byref(_pargs(num_tokens=0)), None) == tq.TQ_OK
+    assert tq.last_error() == ""
