@@ -79,6 +79,10 @@ def lib():
             L.orc_int4_prefill.argtypes = [
                 P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32), P(i32), i32,
                 P(f32), i32, i32, i32, i32, f64, i32, f64, P(f32), P(f64)]
+            L.orc_tq_full_dequant.restype = i32
+            L.orc_tq_full_dequant.argtypes = [
+                P(u8), P(i32), i32, P(f32), i32, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+                P(u16), P(u16)]
             L.orc_tq_slot_bytes.restype = i32
             L.orc_tq_slot_bytes.argtypes = [i32, i32, i32]
             L.orc_lloyd_max_gaussian.argtypes = [i32, P(f64)]
@@ -311,6 +315,26 @@ def tq_decode(q, kv_cache, block_table, seq_lens, centroids, rot_signs, key_fmt,
 
 
 # ---------------------------------------------------------- FWHT-128 + FP8
+def tq_full_dequant(kv_cache, block_table, d, key_fmt, val_fmt, max_seq, num_blocks=None,
+                    centroids=None, norm_correction=False):
+    """[tq] _tq_full_dequant_kv on host arrays: kv_cache [NB, bs, Hk, slot]
+    u8 -> (k, v) [B, Hk, max_seq, d] uint16 fp16 bit patterns."""
+    kv = np.ascontiguousarray(kv_cache, np.uint8)
+    nb, bs, hk, sb = kv.shape
+    bt = np.ascontiguousarray(block_table, np.int32)
+    B = bt.shape[0]
+    cen = None if centroids is None else np.ascontiguousarray(centroids, np.float32)
+    k = np.zeros((B, hk, max_seq, d), np.uint16)
+    v = np.zeros((B, hk, max_seq, d), np.uint16)
+    rc = lib().orc_tq_full_dequant(
+        _p(kv, C.c_uint8), _p(bt, C.c_int32), bt.shape[1], _p(cen, C.c_float), B, hk, d, bs,
+        nb if num_blocks is None else num_blocks, sb, key_fmt, val_fmt,
+        1 if norm_correction else 0, max_seq, _p(k, C.c_uint16), _p(v, C.c_uint16))
+    if rc != 0:
+        raise ValueError("tq_full_dequant: invalid arguments")
+    return k, v
+
+
 def fwht128_quant_fp8(x_bf16_bits):
     """x: [rows, 128] uint16 bf16 bit patterns -> (y [rows,128] u8, scale [rows] f32)."""
     x = np.ascontiguousarray(x_bf16_bits, np.uint16)

@@ -755,6 +755,68 @@ int orc_tq_decode(const float* q, const uint8_t* kv_cache,
   return 0;
 }
 
+/* [tq] _tq_full_dequant_kv: every position pos < max_seq of every (b, kv
+ * head), read through the block table (page = block_table[b, pos / bs]),
+ * rebuilt as fp16 rows of k_out / v_out [B, hk, max_seq, d]. The page takes
+ * no sequence lengths; positions whose page lies outside [0, num_blocks)
+ * are written as zeros here (reading: the page would read outside the
+ * cache). Keys: FP8 -> fp32 -> fp16; centroid keys c[idx] (LSB-first b-bit
+ * indices), with norm correction c * (1 / sqrt(sum_d c^2 + 1e-16)) (the sum
+ * in dimension order), then fl32(norm16 * c) -> fp16. Values: 3/4-bit
+ * uniform fma(idx, scale16, zero16) in fp32 -> fp16 (one rounding, the
+ * page compiler's contraction); other value widths (FP8 values) give zeros,
+ * as the page's kernel does. All fp16 roundings are to nearest even. */
+int orc_tq_full_dequant(const uint8_t* kv_cache, const int32_t* block_table,
+                        int max_blocks, const float* centroids, int B, int hk,
+                        int d, int block_size, int64_t num_blocks,
+                        int slot_bytes, int key_fmt, int val_fmt,
+                        int norm_correction, int max_seq, uint16_t* k_out,
+                        uint16_t* v_out) {
+  if (d <= 0 || d > 1024 || (d & (d - 1)) != 0) return -1;
+  if (key_fmt < 1 || key_fmt > 3 || val_fmt < 1 || val_fmt > 3) return -1;
+  if (slot_bytes < orc_tq_slot_bytes(d, key_fmt, val_fmt)) return -1;
+  if (max_seq < 0 || (int64_t)max_seq > (int64_t)max_blocks * block_size) return -1;
+  const int kb = key_bits(key_fmt), vb = val_bits(val_fmt);
+  const int mse_bytes = (d * kb + 7) / 8, kps = key_region(d, key_fmt);
+  const int vdb = val_data_bytes(d, val_fmt);
+  float c[1024];
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < hk; ++h)
+      for (int pos = 0; pos < max_seq; ++pos) {
+        size_t o = (((size_t)b * hk + h) * max_seq + pos) * d;
+        int64_t page = block_table[(size_t)b * max_blocks + pos / block_size];
+        if (page < 0 || page >= num_blocks) {
+          for (int i = 0; i < d; ++i) k_out[o + i] = v_out[o + i] = 0;
+          continue;
+        }
+        const uint8_t* slot = kv_cache +
+            ((page * block_size + pos % block_size) * hk + h) * (int64_t)slot_bytes;
+        if (key_fmt == 1) {
+          for (int i = 0; i < d; ++i) k_out[o + i] = orc_f32_to_f16(orc_e4m3_to_f32(slot[i]));
+        } else {
+          for (int i = 0; i < d; ++i) c[i] = centroids[get_bits(slot, i, kb)];
+          if (norm_correction) {
+            float ss = 0.0f;
+            for (int i = 0; i < d; ++i) ss = ss + c[i] * c[i];
+            float inv = 1.0f / sqrtf(ss + 1e-16f);
+            for (int i = 0; i < d; ++i) c[i] = c[i] * inv;
+          }
+          float nrm = orc_f16_to_f32((uint16_t)(slot[mse_bytes] | (slot[mse_bytes + 1] << 8)));
+          for (int i = 0; i < d; ++i) k_out[o + i] = orc_f32_to_f16(nrm * c[i]);
+        }
+        if (val_fmt == 3) {
+          for (int i = 0; i < d; ++i) v_out[o + i] = 0;
+        } else {
+          const uint8_t* vs = slot + kps;
+          float sc = orc_f16_to_f32((uint16_t)(vs[vdb] | (vs[vdb + 1] << 8)));
+          float zr = orc_f16_to_f32((uint16_t)(vs[vdb + 2] | (vs[vdb + 3] << 8)));
+          for (int i = 0; i < d; ++i)
+            v_out[o + i] = orc_f32_to_f16(fmaf((float)get_bits(vs, i, vb), sc, zr));
+        }
+      }
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* [kpool] _fwht_quant_kernel / fwht128_quant_fp8, per 128-wide bf16 row:   */
 /*   x = fp32(row); seven butterfly stages (strides 1..64) in fp32;         */

@@ -84,6 +84,13 @@ int orc_tq_decode(const float* q, const uint8_t* kv_cache,
                   int norm_correction, int num_splits, double sm_scale,
                   const int32_t* rows, int n_rows, double* out, double* lse);
 
+int orc_tq_full_dequant(const uint8_t* kv_cache, const int32_t* block_table,
+                        int max_blocks, const float* centroids, int B, int hk,
+                        int d, int block_size, int64_t num_blocks,
+                        int slot_bytes, int key_fmt, int val_fmt,
+                        int norm_correction, int max_seq, uint16_t* k_out,
+                        uint16_t* v_out);
+
 /* ---- Hadamard-128 + power-of-two-scale FP8 ---- */
 float orc_fp8_pow2_scale(float absmax);
 void orc_fwht128_quant_fp8(const uint16_t* x_bf16, int64_t rows, uint8_t* y,

@@ -275,6 +275,40 @@ def random_tq_fp8_u4_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=8):
     return cache
 
 
+def random_tq_cache(w: DecodeWorkload, key_fmt: int, val_fmt: int, slot_bytes: int,
+                    wid_tensor=10):
+    """Random TurboQuant slots of any format (key_fmt 1 FP8 / 2 centroid-3 /
+    3 centroid-4, val_fmt 1 U3 / 2 U4 / 3 FP8): uniform bytes, with E4M3 NaN
+    codes (0x7F / 0xFF) replaced by 0x7E / 0xFE, fp16 norms in [2^-2, 2^4),
+    fp16 value scales of either sign with magnitude in [2^-6, 2^0) and fp16
+    zeros in [-2, 2)."""
+    g = rng(w.wid, wid_tensor)
+    d = w.d
+    shp = (w.num_blocks, w.block_size, w.hk)
+    cache = g.integers(0, 256, size=shp + (slot_bytes,), dtype=np.uint8)
+
+    def f16_field(off, vals):
+        cache[..., off:off + 2] = vals.astype(np.float16)[..., None].view(np.uint8).reshape(shp + (2,))
+
+    if key_fmt == 1:
+        kps = d
+        keys = cache[..., :d]
+        keys[(keys & 0x7F) == 0x7F] -= 1
+    else:
+        mse = (d * (3 if key_fmt == 2 else 4) + 7) // 8
+        kps = mse + 2
+        f16_field(mse, np.exp2(g.uniform(-2, 4, size=shp)))
+    if val_fmt == 3:
+        vals = cache[..., kps:kps + d]
+        vals[(vals & 0x7F) == 0x7F] -= 1
+    else:
+        vdb = (d * (3 if val_fmt == 1 else 4) + 7) // 8
+        sign = np.where(g.random(size=shp) < 0.25, -1.0, 1.0)
+        f16_field(kps + vdb, sign * np.exp2(g.uniform(-6, 0, size=shp)))
+        f16_field(kps + vdb + 2, g.uniform(-2, 2, size=shp))
+    return cache
+
+
 def random_tq_mse3_u3_cache(w: DecodeWorkload, slot_bytes: int, wid_tensor=9):
     """Random 3-bit-centroid-key / 3-bit-value TurboQuant slots: uniform index
     bytes, fp16 norms in [2^-2, 2^4), fp16 value scales of either sign with
