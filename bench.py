@@ -22,8 +22,9 @@ tq_mixed_b_d256 (3-bit centroid keys and values at D=256), write (65536
 tokens x 8 heads x 128 bf16), tq_write_a / tq_write_b (the TurboQuant slot
 writer on the same rows), fwht (1,048,576 rows), kpool (pooled-softmax key
 compression: 262144 pools of 4 tokens), prefill_int4 (multi-query INT4
-attention: 4 sequences of 1024 context + 1024 query tokens), copy (device
-copy used to calibrate the HBM byte counters).
+attention: 4 sequences of 1024 context + 1024 query tokens), tq_dequant
+(bulk TurboQuant dequant of the tq_mixed cache to fp16), copy (device copy
+used to calibrate the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -358,6 +359,30 @@ def run_other(args, torch, tq, W):
                              "context + 1024 query tokens), Hq=32 Hk=8 D=128 bs=16, INT4 K/V",
                     us=t * 1e6, query_tokens_per_s=float(ql.sum()) / t,
                     visible_pairs=pairs, attention_TFLOPs=flops / t / 1e12)
+    elif name == "tq_dequant":
+        # bulk dequant of the tq_mixed cache (B=16 Hk=4 D=128, 16384 tokens each,
+        # FP8 keys + 4-bit values, 208-B slots) to fp16 K/V
+        w = W.decode_workload("tq_mixed")
+        sb = tq.tq_slot_bytes(w.d, tq.KEY_FP8, tq.VAL_U4)
+        g = torch.Generator(device=dev)
+        g.manual_seed(9)
+        cache = torch.randint(0, 256, (w.num_blocks, w.block_size, w.hk, sb), dtype=torch.uint8,
+                              device=dev, generator=g)
+        cache[..., :w.d][(cache[..., :w.d] & 0x7F) == 0x7F] -= 1  # no E4M3 NaN codes
+        # fp16 value scale 2^-4 and zero 0 (bits 0x2C00, 0x0000) after the indices
+        cache[..., w.d + 64] = 0x00
+        cache[..., w.d + 65] = 0x2C
+        cache[..., w.d + 66:w.d + 68] = 0
+        call, k, v = tq.prepare_full_dequant(cache, torch.from_numpy(w.block_table).to(dev),
+                                             head_dim=w.d, key_fmt=tq.KEY_FP8, val_fmt=tq.VAL_U4,
+                                             max_seq=int(w.seq_lens.max()))
+        t = _time_loop(torch, stream, lambda i: call.run(sp), args.warmup, args.steps)
+        rows = w.B * w.hk * int(w.seq_lens.max())
+        nbytes = rows * (sb + 2 * w.d * 2) + w.block_table.size * 4
+        line = dict(workload="tq_dequant: tq_full_dequant_kv B=16 Hk=4 D=128 16384 tokens, FP8 keys "
+                             "+ U4 values (208-B slots) -> fp16 K/V", us=t * 1e6,
+                    algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
+                    pct_peak=100 * nbytes / t / PEAK_HBM)
     elif name == "copy":
         n = 512 * 2 ** 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)

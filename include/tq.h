@@ -1,7 +1,7 @@
 /*
  * tq.h -- C ABI of the MI355X (gfx950) quantized paged-KV decode library.
  *
- * Six operations, each enqueued on the caller's HIP stream:
+ * Seven operations, each enqueued on the caller's HIP stream:
  *   tq_reshape_and_cache_int4  randomized Hadamard rotation + INT4 cache write
  *   tq_encode_and_cache        TurboQuant combined-slot cache write (FP8 or
  *                              centroid keys, uniform 3/4-bit values)
@@ -11,6 +11,7 @@
  *   tq_prefill_attention_int4  multi-query (prefill) attention over the INT4
  *                              cache: causal, sliding window, softcap, sinks,
  *                              fp32 or FP8 output
+ *   tq_full_dequant_kv         bulk TurboQuant slot dequant to fp16 K/V rows
  *   tq_kpool_compress_and_write_cache
  *                              pooled-softmax key compression into the FP8
  *                              indexer page
@@ -20,7 +21,8 @@
  *                                _reshape_cache_int4_kernel, _attn_packed,
  *                                single_rht, fast_hadamard_transform
  *   triton_turboquant_decode.py  triton_turboquant_decode_attention,
- *                                _tq_decode_stage1 (and its stage-2 launch)
+ *                                _tq_decode_stage1 (and its stage-2 launch),
+ *                                _tq_full_dequant_kv
  *   kpool_compress.py            fwht128_quant_fp8, _fwht_quant_kernel,
  *                                kpool_compress_and_write_cache,
  *                                _kpool_softmax_rotate_write_cache_kernel
@@ -310,6 +312,33 @@ typedef struct {
 } tq_prefill_args;
 
 int tq_prefill_attention_int4(const tq_prefill_args* args, void* stream);
+
+/*
+ * Bulk dequantization of the TurboQuant combined-slot cache to fp16 rows
+ * (triton_turboquant_decode.py, _tq_full_dequant_kv). For every b < B, kv
+ * head h and position pos < max_seq, the slot at page block_table[b, pos /
+ * block_size], row pos % block_size, head h becomes
+ *   k_out[b, h, pos, :]  FP8 keys: fp16(e4m3); centroid keys:
+ *                        fp16(fl32(norm16 * c[idx])), c[idx] first scaled by
+ *                        1/sqrt(sum_d c^2 + 1e-16) when norm_correction
+ *   v_out[b, h, pos, :]  3/4-bit values: fp16(fmaf(idx, scale16, zero16));
+ *                        FP8 values: 0 (the page's kernel writes zeros for
+ *                        value widths other than 3 and 4)
+ * (fp16 rounding to nearest even). No sequence lengths are taken: positions
+ * past a sequence read whatever page the table names; a page outside
+ * [0, num_blocks) gives zero rows.
+ *   kv_cache     device [num_blocks, block_size, Hk, slot_bytes] u8, 16-B aligned;
+ *                slot_bytes >= tq_slot_bytes(D, key_fmt, val_fmt), a multiple of 16
+ *   block_table  device [B, max_blocks] int32; max_seq <= max_blocks * block_size
+ *   centroids    device [2^bits] f32 (centroid keys; else ignored)
+ *   k_out, v_out device [B, Hk, max_seq, D] fp16, 16-B aligned
+ * D = 64, 128 or 256. B * Hk * max_seq == 0 returns TQ_OK without launching.
+ */
+int tq_full_dequant_kv(const uint8_t* kv_cache, const int32_t* block_table, int32_t max_blocks,
+                       const float* centroids, int32_t B, int32_t Hk, int32_t D,
+                       int32_t block_size, int64_t num_blocks, int32_t slot_bytes,
+                       int32_t key_fmt, int32_t val_fmt, int32_t norm_correction,
+                       int32_t max_seq, void* k_out, void* v_out, void* stream);
 
 /*
  * Pooled-softmax key compression into the FP8 indexer page (kpool_compress.py,

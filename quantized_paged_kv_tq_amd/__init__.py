@@ -10,6 +10,7 @@ in the library's HIP kernels. torch supplies device memory and streams.
     fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
     tq_prefill_attention_int4   multi-query (prefill) attention over the
                                 INT4 cache
+    tq_full_dequant_kv          bulk TurboQuant slot dequant to fp16 K/V
     tq_kpool_compress_and_write_cache
                                 pooled-softmax key compression into the
                                 FP8 indexer page
@@ -91,6 +92,10 @@ SYMBOLS = {
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "tq_prefill_attention_int4": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
+    "tq_full_dequant_kv": (C.c_int, [
+        C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+        C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+        C.c_void_p, C.c_void_p, C.c_void_p]),
     "tq_kpool_compress_and_write_cache": (C.c_int, [
         C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
         C.c_int32, C.c_int32, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p,
@@ -470,3 +475,40 @@ def tq_prefill_attention_int4(query, key_cache, value_cache, block_table, cu_seq
                                 seq_lens, **kw)
     call.run(stream, query.device)
     return out
+
+
+def prepare_full_dequant(kv_cache, block_table, *, head_dim, key_fmt, val_fmt, max_seq,
+                         centroids=None, norm_correction=False, k_out=None, v_out=None):
+    """Validate and marshal a tq_full_dequant_kv call; returns (Prepared, k, v)
+    with k, v [B, Hk, max_seq, D] float16."""
+    _need(kv_cache, torch.uint8, "kv_cache")
+    _need(block_table, torch.int32, "block_table")
+    if kv_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("kv_cache must be [NB, bs, Hk, slot_bytes], block_table [B, max_blocks]")
+    nb, bs, hk, sb = kv_cache.shape
+    B = block_table.shape[0]
+    keep = [kv_cache, block_table]
+    if centroids is not None:
+        _need(centroids, torch.float32, "centroids")
+        keep.append(centroids)
+    shape = (B, hk, max_seq, head_dim)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.float16, device=kv_cache.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.float16, device=kv_cache.device)
+    for t, n in ((k_out, "k_out"), (v_out, "v_out")):
+        _need(t, torch.float16, n)
+        if tuple(t.shape) != shape:
+            raise ValueError("%s must be [B, Hk, max_seq, D]" % n)
+        keep.append(t)
+    args = (_ptr(kv_cache), _ptr(block_table), block_table.shape[1], _ptr(centroids), B, hk,
+            head_dim, bs, nb, sb, key_fmt, val_fmt, 1 if norm_correction else 0, max_seq,
+            _ptr(k_out), _ptr(v_out))
+    return Prepared(lib().tq_full_dequant_kv, args, keep), k_out, v_out
+
+
+def tq_full_dequant_kv(kv_cache, block_table, *, stream=None, **kw):
+    """Dequantize every TurboQuant slot below max_seq to fp16 (k, v) [B, Hk, max_seq, D]."""
+    call, k, v = prepare_full_dequant(kv_cache, block_table, **kw)
+    call.run(stream, kv_cache.device)
+    return k, v

@@ -288,6 +288,55 @@ int tq_prefill_attention_int4(const tq_prefill_args* a, void* stream) {
                   "tq_prefill_attention_int4");
 }
 
+int tq_full_dequant_kv(const uint8_t* kv_cache, const int32_t* block_table, int32_t max_blocks,
+                       const float* centroids, int32_t B, int32_t Hk, int32_t D,
+                       int32_t block_size, int64_t num_blocks, int32_t slot_bytes,
+                       int32_t key_fmt, int32_t val_fmt, int32_t norm_correction,
+                       int32_t max_seq, void* k_out, void* v_out, void* stream) {
+  if (D != 64 && D != 128 && D != 256) return fail(TQ_ENOTSUP, "D=%d (64, 128, 256)", D);
+  if (key_fmt < TQ_KEY_FP8 || key_fmt > TQ_KEY_MSE4 || val_fmt < TQ_VAL_U3 || val_fmt > TQ_VAL_FP8)
+    return fail(TQ_ENOTSUP, "key_fmt %d / val_fmt %d is not a TurboQuant slot format", key_fmt, val_fmt);
+  if (B < 0 || Hk < 1 || max_seq < 0 || block_size < 1 || max_blocks < 1 || num_blocks < 1)
+    return fail(TQ_EINVAL, "bad sizes");
+  const int need = tq_slot_bytes(D, key_fmt, val_fmt);
+  if (slot_bytes < need || slot_bytes % 16 != 0)
+    return fail(TQ_EINVAL, "slot_bytes %d (need a multiple of 16 >= %d)", slot_bytes, need);
+  if ((int64_t)max_seq > (int64_t)max_blocks * block_size)
+    return fail(TQ_EINVAL, "max_seq %d > max_blocks * block_size", max_seq);
+  const int64_t rows = (int64_t)B * Hk * max_seq;
+  if (rows == 0) {
+    g_err[0] = '\0';
+    return TQ_OK;
+  }
+  if (rows / (256 / (D / 8)) >= 0x7FFFFFFF) return fail(TQ_EINVAL, "too many rows");
+  if (!kv_cache || !block_table || !k_out || !v_out || (key_fmt != TQ_KEY_FP8 && !centroids))
+    return fail(TQ_EINVAL, "null pointer argument");
+  if (!aligned(kv_cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(TQ_EINVAL, "misaligned kv_cache, k_out or v_out (16 B)");
+  tqk::DequantParams p;
+  p.kv = kv_cache;
+  p.block_table = block_table;
+  p.centroids = centroids;
+  p.k_out = static_cast<uint16_t*>(k_out);
+  p.v_out = static_cast<uint16_t*>(v_out);
+  p.num_blocks = num_blocks;
+  p.B = B;
+  p.hk = Hk;
+  p.d = D;
+  p.block_size = block_size;
+  p.max_blocks = max_blocks;
+  p.slot_bytes = slot_bytes;
+  p.key_fmt = key_fmt;
+  p.val_fmt = val_fmt;
+  p.norm_correction = norm_correction ? 1 : 0;
+  p.max_seq = max_seq;
+  p.kps = key_region_bytes(D, key_fmt);
+  p.vdb = value_index_bytes(D, val_fmt);
+  p.mse_bytes = (D * key_bits(key_fmt) + 7) / 8;
+  return launched(tqk::launch_tq_full_dequant(p, static_cast<hipStream_t>(stream)),
+                  "tq_full_dequant_kv");
+}
+
 int tq_decode_attention(const tq_decode_args* a, void* stream) {
   if (!a) return fail(TQ_EINVAL, "null args");
   if (a->struct_size < sizeof(tq_decode_args))

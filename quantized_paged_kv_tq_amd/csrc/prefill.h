@@ -1,6 +1,7 @@
-// Internal launch interface of the INT4 multi-query (prefill) attention
-// (int4_per_token_head.py, _attn_packed in its 2D mode). Arguments arrive
-// validated.
+// Internal launch interfaces of the prefill-side read paths: the INT4
+// multi-query attention (int4_per_token_head.py, _attn_packed in its 2D
+// mode) and the bulk TurboQuant dequant (triton_turboquant_decode.py,
+// _tq_full_dequant_kv). Arguments arrive validated.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,5 +27,17 @@ struct PrefillParams {
   float sm_scale, softcap;
 };
 hipError_t launch_prefill_int4(const PrefillParams& p, hipStream_t st);
+
+struct DequantParams {
+  const uint8_t* kv;          // [num_blocks, bs, hk, slot_bytes]
+  const int32_t* block_table; // [B, max_blocks]
+  const float* centroids;     // [2^key bits] (centroid keys)
+  uint16_t* k_out;            // [B, hk, max_seq, d] fp16
+  uint16_t* v_out;
+  int64_t num_blocks;
+  int B, hk, d, block_size, max_blocks, slot_bytes, key_fmt, val_fmt, norm_correction, max_seq;
+  int kps, vdb, mse_bytes;    // key region, value data and index bytes of the slot
+};
+hipError_t launch_tq_full_dequant(const DequantParams& p, hipStream_t st);
 
 }  // namespace tqk

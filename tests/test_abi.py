@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
                           "tq_encode_and_cache", "tq_decode_workspace_bytes", "tq_slot_bytes",
                           "tq_decode_attention", "fwht128_quant_fp8",
-                          "tq_kpool_compress_and_write_cache", "tq_prefill_attention_int4"}
+                          "tq_kpool_compress_and_write_cache", "tq_prefill_attention_int4",
+                          "tq_full_dequant_kv"}
     raw = C.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -261,3 +262,25 @@ def test_prefill_empty_and_null(L):
     assert L.tq_prefill_attention_int4(None, None) == tq.TQ_EINVAL
     assert L.tq_prefill_attention_int4(C.byref(_pargs(num_tokens=0)), None) == tq.TQ_OK
     assert tq.last_error() == ""
+
+
+def test_full_dequant_validation(L):
+    f = L.tq_full_dequant_kv
+    # (kv, bt, max_blocks, cen, B, Hk, D, bs, nb, slot_bytes, key_fmt, val_fmt, nc, max_seq, k, v, stream)
+    ok = dict(kv=16, bt=16, mb=4, cen=16, B=2, hk=2, D=128, bs=16, nb=8, sb=208, kf=tq.KEY_FP8,
+              vf=tq.VAL_U4, nc=0, ms=64, k=16, v=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["kv"], a["bt"], a["mb"], a["cen"], a["B"], a["hk"], a["D"], a["bs"], a["nb"],
+                 a["sb"], a["kf"], a["vf"], a["nc"], a["ms"], a["k"], a["v"], None)
+
+    assert call(ms=0) == tq.TQ_OK and tq.last_error() == ""
+    assert call(D=96) == tq.TQ_ENOTSUP
+    assert call(kf=tq.KEY_INT4, vf=tq.VAL_INT4) == tq.TQ_ENOTSUP
+    assert call(sb=192) == tq.TQ_EINVAL          # smaller than the slot
+    assert call(sb=216) == tq.TQ_EINVAL          # not a multiple of 16
+    assert call(ms=65) == tq.TQ_EINVAL           # beyond max_blocks * block_size
+    assert call(kf=tq.KEY_MSE3, vf=tq.VAL_U3, sb=112, cen=None) == tq.TQ_EINVAL
+    assert call(kv=None) == tq.TQ_EINVAL
+    assert call(k=8) == tq.TQ_EINVAL             # misaligned output
