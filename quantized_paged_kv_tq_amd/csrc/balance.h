@@ -35,12 +35,18 @@ struct SeqSplits {
   int TLast;  // tiles of the last split
 };
 
-__device__ __forceinline__ SeqSplits seq_splits(const DecodeParams& p, int b) {
+// Sequence length b clamped to [0, block-table capacity].
+__device__ __forceinline__ int clamped_seq(const DecodeParams& p, int b) {
   int64_t s64 = p.seq_lens[b];
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
   s64 = s64 < 0 ? 0 : (s64 > cap ? cap : s64);
+  return (int)s64;
+}
+
+// Split geometry of a sequence of `seq` tokens (already clamped).
+__device__ __forceinline__ SeqSplits splits_of(const DecodeParams& p, int seq) {
   SeqSplits r;
-  r.seq = (int)s64;
+  r.seq = seq;
   if (r.seq == 0) {
     r.L = r.n = r.TL = r.TLast = 0;
     return r;
@@ -50,6 +56,10 @@ __device__ __forceinline__ SeqSplits seq_splits(const DecodeParams& p, int b) {
   r.TL = (r.L + kTileTokens - 1) / kTileTokens;
   r.TLast = (r.seq - (r.n - 1) * r.L + kTileTokens - 1) / kTileTokens;
   return r;
+}
+
+__device__ __forceinline__ SeqSplits seq_splits(const DecodeParams& p, int b) {
+  return splits_of(p, clamped_seq(p, b));
 }
 
 __device__ __forceinline__ int seq_tiles(const SeqSplits& q) {
@@ -64,6 +74,61 @@ __device__ __forceinline__ int range_lo(int w, int N, int nw) {
 // range_lo(w) <= x.
 __device__ __forceinline__ int range_owner(int x, int N, int nw) {
   return (int)(((int64_t)(x + 1) * nw - 1) / N);
+}
+
+// LDS the stage-1 prologue needs: prefix[B + 1] followed by seql[B].
+inline size_t balance_lds_bytes(int B) { return (size_t)(2 * B + 1) * sizeof(int); }
+
+// Prologue of the balanced stage 1, run by all NT threads of a workgroup:
+// the clamped sequence lengths into seql[0, B), the exclusive prefix sums of
+// their tile counts into prefix[0, B] (workgroup 0 also publishes them to
+// wsx for stage 2). `scan` holds NT / 64 ints. Returns N, the total tile
+// count. Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int balance_prologue(const DecodeParams& p, int* prefix, int* seql,
+                                                int* scan) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (p.B + NT - 1) / NT;  // consecutive sequences per thread
+  int run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      const int sq = clamped_seq(p, b);
+      seql[b] = sq;
+      run += seq_tiles(splits_of(p, sq));
+      prefix[b + 1] = run;
+    }
+  }
+  // inclusive scan of the per-thread sums: across the wave, then waves
+  int incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int N = 0, before = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NT / 64; ++w2) {
+    const int t = scan[w2];
+    N += t;
+    before += w2 < wave ? t : 0;
+  }
+  const int excl = before + incl - run;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b < p.B) {
+      prefix[b + 1] += excl;
+      if (blockIdx.x == 0) p.wsx[b + 1] = prefix[b + 1];
+    }
+  }
+  if (tid == 0) {
+    prefix[0] = 0;
+    if (blockIdx.x == 0) p.wsx[0] = 0;
+  }
+  __syncthreads();
+  return N;
 }
 
 // Kv heads per workgroup and workgroups per kv-head group of the balanced

@@ -124,7 +124,8 @@ void decode_int4_mfma_kernel(DecodeParams p) {
   // fp32 accumulators of the wave's heads, lane-major (touched only when
   // the int32 MFMA sums are folded in, so they need no registers)
   __shared__ float accl[W][NH * 8][64];
-  extern __shared__ int prefix[];  // [B + 1]: tiles of the sequences before b
+  // [B + 1] tiles of the sequences before b, then [B] their clamped lengths
+  extern __shared__ int prefix[];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -143,48 +144,8 @@ void decode_int4_mfma_kernel(DecodeParams p) {
   const int gw = g - hq0 < NHEAD ? g - hq0 : NHEAD;  // query heads of this wave
   const int h0 = kvh * g + hq0;
 
-  // ---- tile counts of all sequences and their prefix sums ----
-  const int per = (p.B + NT - 1) / NT;  // consecutive sequences per thread
-  int run = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) {
-      run += seq_tiles(seq_splits(p, b));
-      prefix[b + 1] = run;
-    }
-  }
-  // inclusive scan of the per-thread sums: across the wave, then waves
-  int incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(incl, off);
-    if (lane >= off) incl += u;
-  }
-  if (lane == 63) scan[wave] = incl;
-  __syncthreads();
-  int N = 0, before = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < W; ++w2) {
-    const int t = scan[w2];
-    N += t;
-    before += w2 < wave ? t : 0;
-  }
-  {
-    const int excl = before + incl - run;
-    for (int i = 0; i < per; ++i) {
-      const int b = tid * per + i;
-      if (b < p.B) {
-        prefix[b + 1] += excl;
-        // stage 2 reads the prefix sums instead of recomputing them
-        if (blockIdx.x == 0) p.wsx[b + 1] = prefix[b + 1];
-      }
-    }
-    if (tid == 0) {
-      prefix[0] = 0;
-      if (blockIdx.x == 0) p.wsx[0] = 0;
-    }
-  }
-  __syncthreads();
+  // ---- sequence lengths and the prefix sums of their tile counts ----
+  const int N = balance_prologue<NT>(p, prefix, prefix + p.B + 1, scan);
   if (N == 0) return;  // uniform: every sequence is empty
   const int lo = range_lo(wg, N, p.nw), hi = range_lo(wg + 1, N, p.nw);
   if (lo >= hi) return;  // uniform: an empty range
@@ -590,7 +551,7 @@ void decode_int4_mfma_kernel(DecodeParams p) {
         else bh = m - 1;
       }
       const int b = bl;
-      const SeqSplits q = seq_splits(p, b);
+      const SeqSplits q = splits_of(p, prefix[p.B + 1 + b]);
       const int r = x - prefix[b];
       int s = r / q.TL;
       if (s > q.n - 1) s = q.n - 1;
@@ -633,7 +594,7 @@ void decode_int4_mfma_kernel(DecodeParams p) {
 template <int W, int NH, int DEPTH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
-  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
+  const size_t lds = balance_lds_bytes(p.B);
   hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }

@@ -98,7 +98,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
   __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
-  extern __shared__ int prefix[];
+  extern __shared__ int prefix[];  // [B + 1] tile prefix sums, then [B] lengths
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -116,46 +116,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   const int gw = g - hq0 < NHEAD ? g - hq0 : NHEAD;
   const int h0 = kvh * g + hq0;
 
-  // ---- tile counts of all sequences and their prefix sums ----
-  const int per = (p.B + NT - 1) / NT;
-  int run = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) {
-      run += seq_tiles(seq_splits(p, b));
-      prefix[b + 1] = run;
-    }
-  }
-  int incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(incl, off);
-    if (lane >= off) incl += u;
-  }
-  if (lane == 63) scan[wave] = incl;
-  __syncthreads();
-  int N = 0, before = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < W; ++w2) {
-    const int t = scan[w2];
-    N += t;
-    before += w2 < wave ? t : 0;
-  }
-  {
-    const int excl = before + incl - run;
-    for (int i = 0; i < per; ++i) {
-      const int b = tid * per + i;
-      if (b < p.B) {
-        prefix[b + 1] += excl;
-        if (blockIdx.x == 0) p.wsx[b + 1] = prefix[b + 1];
-      }
-    }
-    if (tid == 0) {
-      prefix[0] = 0;
-      if (blockIdx.x == 0) p.wsx[0] = 0;
-    }
-  }
-  __syncthreads();
+  // ---- sequence lengths and the prefix sums of their tile counts ----
+  const int N = balance_prologue<NT>(p, prefix, prefix + p.B + 1, scan);
   if (N == 0) return;
   const int lo = range_lo(wg, N, p.nw), hi = range_lo(wg + 1, N, p.nw);
   if (lo >= hi) return;
@@ -500,7 +462,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
         else bh = m - 1;
       }
       const int b = bl;
-      const SeqSplits q = seq_splits(p, b);
+      const SeqSplits q = splits_of(p, prefix[p.B + 1 + b]);
       const int r = x - prefix[b];
       int s = r / q.TL;
       if (s > q.n - 1) s = q.n - 1;
@@ -542,7 +504,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 template <int W, int NH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
-  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
+  const size_t lds = balance_lds_bytes(p.B);
   hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }

@@ -31,6 +31,9 @@ __global__ __launch_bounds__(D * PG) void merge_kernel(DecodeParams p) {
   const int h = bh - b * p.hq;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // the inverse-rotation sign is loaded with the first round trip, not after
+  // the merge
+  const float sgn = ROTATE ? p.rht_signs[tid % D] : 1.0f;
   const SeqSplits q = seq_splits(p, b);
   const int nsplit = q.n;  // non-empty splits are a prefix: s * split_len < seq
 
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(D * PG) void merge_kernel(DecodeParams p) {
       const float pr = acc_l[0][d ^ 64];
       o = (d & 64) ? (pr - o) : (o + pr);
     }
-    o = o * p.rht_signs[d] * (1.0f / (float)D);
+    o = o * sgn * (1.0f / (float)D);
   }
   if (tid < D) {
     p.out[(int64_t)bh * D + d] = o;
