@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void tq_full_dequant_kernel(DequantParams p) {
   }
   if (live) {
     const int64_t o = r * D + li * 8;
-    *reinterpret_cast<uint4*>(p.k_out + o) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    *reinterpret_cast<uint4*>(p.v_out + o) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+    stream_store16(p.k_out + o, kw[0], kw[1], kw[2], kw[3]);
+    stream_store16(p.v_out + o, vw[0], vw[1], vw[2], vw[3]);
   }
 }
 

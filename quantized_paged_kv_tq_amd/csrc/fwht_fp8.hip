@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
     if (row[r] < rows) {
       // elements 8l .. 8l+7 and 64 + 8l .. 64 + 8l + 7
       const uint16_t* src = x_bf16 + row[r] * 128 + li * 8;
-      const uint4 a = *reinterpret_cast<const uint4*>(src);
-      const uint4 b = *reinterpret_cast<const uint4*>(src + 64);
+      const uint4 a = stream_load16(src);
+      const uint4 b = stream_load16(src + 64);
       const uint32_t ws[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -97,9 +97,9 @@ __global__ __launch_bounds__(256) void fwht128_fp8_kernel(const uint16_t* __rest
       w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], v, true);
     }
     if (row[r] < rows) {
-      *reinterpret_cast<uint2*>(y + row[r] * 128 + li * 8) = make_uint2(w[0], w[1]);
-      *reinterpret_cast<uint2*>(y + row[r] * 128 + 64 + li * 8) = make_uint2(w[2], w[3]);
-      if (li == 0) scale_out[row[r]] = u2f(sb);
+      stream_store8(y + row[r] * 128 + li * 8, w[0], w[1]);
+      stream_store8(y + row[r] * 128 + 64 + li * 8, w[2], w[3]);
+      if (li == 0) stream_store4(scale_out + row[r], sb);
     }
   }
 }

@@ -192,4 +192,23 @@ __device__ __forceinline__ uint32_t xcd_logical_block(uint32_t bid, uint32_t nbl
   return (xcd < rem ? xcd * (per + 1u) : rem * (per + 1u) + (xcd - rem) * per) + k;
 }
 
+// Streaming global accesses for data touched once (source rows, written
+// codes): non-temporal hints, so the lines do not displace reused ones.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void stream_store8(void* p, uint32_t a, uint32_t b) {
+  __builtin_nontemporal_store(u32x2{a, b}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void stream_store16(void* p, uint32_t a, uint32_t b, uint32_t c,
+                                               uint32_t d) {
+  __builtin_nontemporal_store(u32x4{a, b, c, d}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void stream_store4(void* p, uint32_t a) {
+  __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+}
+
 }  // namespace tqk

@@ -18,7 +18,7 @@ namespace tqk {
 template <int DT>
 __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t elem, float x[8]) {
   if constexpr (DT == TQ_DT_BF16 || DT == TQ_DT_F16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    const uint4 w = stream_load16(static_cast<const uint16_t*>(base) + elem);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
