@@ -86,12 +86,22 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // converted and its value nibbles transposed once for all 4 * NH heads. NH =
 // 2 (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH>
+//
+// VF8: FP8 E4M3 values (D codes, no scale or zero) instead of 4-bit ones.
+// Every E4M3 value is a bf16 value, so the values convert exactly; the
+// weights p are split into three bf16 parts like the query, and the value
+// sum runs as v_mfma_f32_16x16x32_bf16 with A rows 4h + part (weights of
+// head h) and B = 32 tokens x 16 value dims, dims 8n + i for MFMA i (lane n
+// loads value bytes 8n .. 8n + 7 of its tokens, and a 4x4 byte transpose
+// gives byte i of 4 tokens per register).
+template <int W, int NH, bool VF8>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_tq_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
-  __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
+  __shared__ __attribute__((aligned(16))) uint32_t p8[VF8 ? 1 : W][NH][4][4][16];  // weight digit planes
+  // VF8: bf16 parts of the weights, [part][head][token] per row set
+  __shared__ __attribute__((aligned(16))) uint16_t pbf[VF8 ? W : 1][NH][3][4][64];
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
   __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
@@ -138,6 +148,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     v4u kraw[4][2];
     uint32_t sz, live;
     uint32_t vraw[4][4];
+    uint32_t v8[2][8][2];  // VF8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
   auto slot_of = [&](int k, int j) -> uint32_t { return tok_rows[k][j] + kvh_off; };
@@ -149,6 +160,18 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       B.live |= (o < kMaskedByte ? 1u : 0u) << s;
       B.kraw[s][0] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg), 0, 0);
       B.kraw[s][1] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg + 16u), 0, 0);
+    }
+    if constexpr (VF8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t o = slot_of(k, 32 * h + 8 * lg + j);
+          B.v8[h][j][0] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 8u * ln), 0, 0);
+          B.v8[h][j][1] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 8u * ln + 4u), 0, 0);
+        }
+      }
+      return;
     }
     B.sz = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(slot_of(k, lane) + soff), 0, 0);
 #pragma unroll
@@ -165,6 +188,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
   float(*acc)[64] = accl[wave];       // acc[8r + i][lane]
   v4i cacc[NH][8];
+  v4f facc[NH][8];  // VF8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
@@ -179,6 +203,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       for (int i = 0; i < 8; ++i) {
         acc[8 * r + i][lane] = 0.0f;
         cacc[r][i] = v4i{0, 0, 0, 0};
+        facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
     ev = 0;
@@ -195,11 +220,17 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       if (!empty) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
-          const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
-          const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-          acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
-          cacc[r][i] = v4i{0, 0, 0, 0};
+          if constexpr (VF8) {
+            const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
+            acc[8 * r + i][lane] = (acc[8 * r + i][lane] + val) * alpha[r];
+            facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          } else {
+            const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
+            const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+            const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+            acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
+            cacc[r][i] = v4i{0, 0, 0, 0};
+          }
         }
       } else {
 #pragma unroll
@@ -301,9 +332,11 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // scale/zero words of tokens 16s + n
-    uint32_t sz[4];
+    uint32_t sz[4] = {0, 0, 0, 0};
+    if constexpr (!VF8) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sz[s] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz);
+      for (int s = 0; s < 4; ++s) sz[s] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz);
+    }
 
     // ---- scores: lane (n, g) gets head 4r + g, token 16s + n ----
     float sc[NH][4];
@@ -347,7 +380,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       move |= tm[r] > mref[r] + (float)kTau;
     }
     smax = row16_max(smax);
-    const bool smove = smax >= sref || ++since_flush >= 8192;
+    // (VF8: the fp32 sums need no fixed-point range)
+    const bool smove = !VF8 && (smax >= sref || ++since_flush >= 8192);
     if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
       float alpha[NH];
 #pragma unroll
@@ -363,6 +397,76 @@ void decode_tq_fp8_kernel(DecodeParams p) {
         ev = 26 - kTau - e;
         sref = exp2i(e + 1);
       }
+    }
+
+    if constexpr (VF8) {
+      // ---- weights in three bf16 parts, to LDS as [part][head][token] ----
+#pragma unroll
+      for (int r = 0; r < NH; ++r) {
+        float ps = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float pr = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+          ps += pr;
+          const uint32_t bh = bf16_bits(pr);
+          const float r1 = pr - u2f(bh << 16);
+          const uint32_t bm = bf16_bits(r1);
+          const uint32_t bl = bf16_bits(r1 - u2f(bm << 16));
+          pbf[wave][r][0][lg][16 * s + ln] = (uint16_t)bh;
+          pbf[wave][r][1][lg][16 * s + ln] = (uint16_t)bm;
+          pbf[wave][r][2][lg][16 * s + ln] = (uint16_t)bl;
+        }
+        l[r] += ps;
+      }
+      empty = false;
+      wave_sync();
+      // ---- value MFMAs, one 32-token half at a time ----
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // A: lane (4h' + part, g) holds part `part` of head h''s weights of
+        // tokens 32h + 8g .. 32h + 8g + 7 (part 3: zero)
+        v8bf16 pa[NH];
+        const int hd = ln >> 2, part = ln & 3;
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          uint4 a4 = make_uint4(0u, 0u, 0u, 0u);
+          if (part < 3) a4 = *reinterpret_cast<const uint4*>(&pbf[wave][r][part][hd][32 * h + 8 * lg]);
+          pa[r] = __builtin_bit_cast(v8bf16, v4u{a4.x, a4.y, a4.z, a4.w});
+        }
+        // ob[t][i]: byte i of value bytes 8n .. 8n+7 of tokens 4t .. 4t+3
+        // of this lane's eight (4x4 byte transposes)
+        uint32_t ob[2][8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t d0 = X.v8[h][4 * t][q], d1 = X.v8[h][4 * t + 1][q];
+            const uint32_t d2 = X.v8[h][4 * t + 2][q], d3 = X.v8[h][4 * t + 3][q];
+            const uint32_t x01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+            const uint32_t x23l = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+            const uint32_t x01h = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+            const uint32_t x23h = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+            ob[t][4 * q + 0] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+            ob[t][4 * q + 1] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+            ob[t][4 * q + 2] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+            ob[t][4 * q + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+          }
+        }
+        // B of MFMA i: column n = value dim 8n + i, rows = the 32 tokens
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const v2bf16 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, false);
+          const v2bf16 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, true);
+          const v2bf16 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[1][i], 1.0f, false);
+          const v2bf16 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[1][i], 1.0f, true);
+          const v8bf16 vb8 = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+          for (int r = 0; r < NH; ++r)
+            facc[r][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[r], vb8, facc[r][i], 0, 0, 0);
+        }
+      }
+      wave_sync();  // the weight parts are rewritten by the next tile
+      return;
     }
 
     // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
@@ -505,7 +609,10 @@ template <int W, int NH>
 hipError_t launch(const DecodeParams& p, hipStream_t st) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH>), dim3(blocks), dim3(64 * W), lds, st, p);
+  if (p.val_fmt == VF_FP8)
+    hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+  else
+    hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -516,7 +623,8 @@ constexpr bool kOneWavePerKvHead = true;
 }  // namespace
 
 hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
-  if (p.d != D || p.key_fmt != KF_FP8 || p.val_fmt != VF_U4 || p.g > 8) return hipErrorNotSupported;
+  if (p.d != D || p.key_fmt != KF_FP8 || (p.val_fmt != VF_U4 && p.val_fmt != VF_FP8) || p.g > 8)
+    return hipErrorNotSupported;
   // slot bytes are addressed with 32-bit buffer offsets (masked: 0xFFFFFF00)
   if (p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31))
     return hipErrorNotSupported;

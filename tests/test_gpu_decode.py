@@ -184,8 +184,9 @@ def test_tq_norm_correction_and_rot_signs(key_fmt):
         assert_close(got, ref, lse, ref_lse, "nc=%d" % nc)
 
 
-@pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3)],
-                         ids=["A_fp8_u4", "B_mse3_u3"])
+@pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3),
+                                 (oracle.KEY_FP8, oracle.VAL_FP8)],
+                         ids=["A_fp8_u4", "B_mse3_u3", "fp8_fp8"])
 def test_tq_full_size_sampled(fmt):
     key_fmt, val_fmt = fmt
     w = W.decode_workload("tq_mixed")
@@ -418,3 +419,49 @@ def test_tq_head_dim_256_shapes(fmt, norm_correction):
                                         int(norm_correction), S, w.sm_scale)
         got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, norm_correction=norm_correction)
         assert_close(got, ref, lse, ref_lse, "fmt %s B=%d" % (fmt, B))
+
+
+# ---------------------------------------------------------------------------
+# FP8 keys + FP8 values (matrix-core path for D = 128, g <= 8)
+
+F8_FMT = (oracle.KEY_FP8, oracle.VAL_FP8)
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_tq_fp8_fp8_shapes(shape, flags):
+    """FP8 keys and FP8 values on the matrix-core kernel (values as exact
+    bf16, weights in three bf16 parts) and on the generic one."""
+    B, hq, hk, d, bs, seq, S = shape
+    w = W.custom_decode_workload(420 + len(seq) * 7 + hq + d, B, hq, hk, d, bs, S, seq, 5, "bf16")
+    cache, cen = tq_case(w, *F8_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *F8_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT, flags=flags)
+    assert_close(got, ref, lse, ref_lse, str(shape))
+
+
+@pytest.mark.parametrize("hq,hk", [(2, 2), (4, 2), (8, 2), (10, 2), (12, 2), (14, 2), (16, 2), (32, 4)],
+                         ids=["g1", "g2", "g4", "g5", "g6", "g7", "g8", "g8x4"])
+def test_tq_fp8_fp8_query_groups(hq, hk):
+    """g = 1 .. 8 (one wave per kv head from g = 5), empty and one-token
+    sequences, sequences over many tiles and splits."""
+    seq = [0, 1, 300, 777, 65, 2000]
+    w = W.custom_decode_workload(430 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    cache, cen = tq_case(w, *F8_FMT)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *F8_FMT)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT)
+    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+
+
+def test_tq_fp8_fp8_split_invariance_and_degenerate_lengths():
+    w = W.custom_decode_workload(440, 3, 8, 2, 128, 16, 4, [37, 1, 100], 2, "bf16")
+    cache, cen = tq_case(w, *F8_FMT)
+    q = W.query(w, bf16_valued=True)
+    seq = np.array([37, 0, 100], np.int32)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *F8_FMT, splits=0, seq_lens=seq)
+    for S in (1, 2, 8, 37, 64, 100, 105, 256):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT, num_splits=S, seq_lens=seq)
+        assert_close(got, ref, lse, ref_lse, "S=%d" % S)
+        assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
