@@ -465,3 +465,20 @@ def test_tq_fp8_fp8_split_invariance_and_degenerate_lengths():
         got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT, num_splits=S, seq_lens=seq)
         assert_close(got, ref, lse, ref_lse, "S=%d" % S)
         assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
+
+
+@pytest.mark.parametrize("hq,hk", [(8, 2), (16, 2)], ids=["g4", "g8"])
+def test_tq_fp8_fp8_random_slot_bytes_wide_scores(hq, hk):
+    """Random slots (no writer): key bytes over every finite E4M3 code, so
+    scores spread over tens of units and the running maximum moves often
+    along a sequence; value codes kept below 2 in magnitude (exponent field
+    at most 7) so the outputs stay O(1). Matrix-core and generic paths."""
+    seq = [0, 1, 300, 2000, 777]
+    w = W.custom_decode_workload(450 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    cache = W.random_tq_cache(w, *F8_FMT, oracle.tq_slot_bytes(128, *F8_FMT))
+    cache[..., 128:256] &= 0xBF
+    q = W.query(w) / 8
+    ref, ref_lse = _oracle_tq(w, q, cache, None, *F8_FMT)
+    for flags in (0, tq.FLAG_GENERIC):
+        got, lse = gpu_tq_decode(w, q, cache, None, *F8_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "wide scores flags=%d" % flags)
