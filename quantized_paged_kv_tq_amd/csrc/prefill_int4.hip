@@ -31,6 +31,7 @@ namespace tqk {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 8.0f;  // headroom of the reference maximum (base-2 units)
 constexpr int kMaxRangePages = 2048;  // block-table entries staged in LDS
 
 template <int D, int G, int U>
@@ -170,15 +171,22 @@ __global__ __launch_bounds__(256) void prefill_int4_kernel(PrefillParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) vd[j] = ((float)((w >> (4 * j)) & 0xFu) - zp) * vsc;
     }
+    // m is a reference maximum: the state moves to a new one only when a
+    // score exceeds it by more than 2^kTau, so the weights stay below
+    // 2^kTau and most tokens take one exponential and no rescaling
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float mn = fmaxf(m[hh], sc[hh]);
-      const float alpha = exp2f(m[hh] - mn);
-      const float pr = exp2f(sc[hh] - mn);
-      l[hh] = l[hh] * alpha + pr;
+      if (sc[hh] > m[hh] + kTau) {
+        const float alpha = exp2f(m[hh] - sc[hh]);  // 0 while m is -inf
+        l[hh] *= alpha;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[hh][j] = acc[hh][j] * alpha + pr * vd[j];
-      m[hh] = mn;
+        for (int j = 0; j < 8; ++j) acc[hh][j] *= alpha;
+        m[hh] = sc[hh];
+      }
+      const float pr = exp2f(sc[hh] - m[hh]);
+      l[hh] += pr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[hh][j] = __builtin_fmaf(pr, vd[j], acc[hh][j]);
     }
   };
 
