@@ -91,3 +91,12 @@ def test_fp8_output_within_one_step(scale):
     lo = grid[np.clip(np.searchsorted(grid, v - tol, side="right") - 1, 0, len(grid) - 1)]
     hi = grid[np.clip(np.searchsorted(grid, v + tol, side="left"), 0, len(grid) - 1)]
     assert np.all((dec >= lo) & (dec <= hi))
+
+
+@pytest.mark.parametrize("window,sinks", [(0, False), (50, True)])
+def test_wide_score_range(window, sinks):
+    """Queries scaled by 40: scores spread over tens of units, so each lane
+    group's reference maximum moves many times along the visible range (and
+    the sink, when present, sits far below or far above it)."""
+    w, c, cu, q = _case(213, 2, 8, 2, 128, 16, ctx=[400, 37], qlen=[60, 9])
+    _check(w, c, cu, q * 40.0, window=window, sinks=W.sink_values(w) if sinks else None)
