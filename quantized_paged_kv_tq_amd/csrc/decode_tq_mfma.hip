@@ -171,15 +171,15 @@ void decode_tq_fp8_kernel(DecodeParams p) {
           B.v8[h][j][1] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 8u * ln + 4u), 0, 0);
         }
       }
-      return;
-    }
-    B.sz = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(slot_of(k, lane) + soff), 0, 0);
+    } else {
+      B.sz = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(slot_of(k, lane) + soff), 0, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
-        B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 4u * ln), 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
+          B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 4u * ln), 0, 0);
+        }
       }
     }
   };
@@ -466,86 +466,86 @@ void decode_tq_fp8_kernel(DecodeParams p) {
         }
       }
       wave_sync();  // the weight parts are rewritten by the next tile
-      return;
-    }
+    } else {
 
-    // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
-    // The encoder's scale16 = (max - min) / levels is positive. A negative
-    // one (any bytes are accepted) takes signed digits: the digits of
-    // p * |scale16|, negated as int8, which the i8 MFMA sums exactly too.
-    const float pscale = exp2i(ev);
-    const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
-                                                     vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
+      // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
+      // The encoder's scale16 = (max - min) / levels is positive. A negative
+      // one (any bytes are accepted) takes signed digits: the digits of
+      // p * |scale16|, negated as int8, which the i8 MFMA sums exactly too.
+      const float pscale = exp2i(ev);
+      const bool any_neg = __builtin_amdgcn_ballot_w64(vsc[0] < 0.0f || vsc[1] < 0.0f ||
+                                                       vsc[2] < 0.0f || vsc[3] < 0.0f) != 0;
 #pragma unroll
-    for (int r = 0; r < NH; ++r) {
-      uint32_t dw[4] = {0, 0, 0, 0};
-      float ps = 0.0f, zs = 0.0f;
-      float pr[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        pr[s] = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
-        ps += pr[s];
-        zs = __builtin_fmaf(pr[s], vz[s], zs);
-      }
-      if (!any_neg) {
+      for (int r = 0; r < NH; ++r) {
+        uint32_t dw[4] = {0, 0, 0, 0};
+        float ps = 0.0f, zs = 0.0f;
+        float pr[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+          pr[s] = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+          ps += pr[s];
+          zs = __builtin_fmaf(pr[s], vz[s], zs);
         }
-      } else {
+        if (!any_neg) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
-          const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], vsc[s] * pscale, 0.5f);
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
-            dw[kk] |= (d & 255u) << (8 * s);
+            for (int kk = 0; kk < 4; ++kk) dw[kk] |= ((pi >> (7 * kk)) & 127u) << (8 * s);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t pi = (uint32_t)__builtin_fmaf(pr[s], fabsf(vsc[s]) * pscale, 0.5f);
+            const uint32_t neg = vsc[s] < 0.0f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const uint32_t d = (((pi >> (7 * kk)) & 127u) ^ neg) - neg;
+              dw[kk] |= (d & 255u) << (8 * s);
+            }
           }
         }
-      }
-      l[r] += ps;
-      zacc[r] += zs;
+        l[r] += ps;
+        zacc[r] += zs;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) p8[wave][r][lg][kk][ln] = dw[kk];
-    }
-    empty = false;
-    wave_sync();
+        for (int kk = 0; kk < 4; ++kk) p8[wave][r][lg][kk][ln] = dw[kk];
+      }
+      empty = false;
+      wave_sync();
 
-    // ---- value MFMAs: B operands by nibble transpose, in two halves ----
-    v4i pa[NH];
+      // ---- value MFMAs: B operands by nibble transpose, in two halves ----
+      v4i pa[NH];
 #pragma unroll
-    for (int r = 0; r < NH; ++r) {
-      const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][r][ln >> 2][ln & 3][4 * lg]);
-      pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t vb[4][4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t w0 = X.vraw[0][kk], w1 = X.vraw[1][kk], w2 = X.vraw[2][kk], w3 = X.vraw[3][kk];
-        const uint32_t sel = h ? 0x07030602u : 0x05010400u;
-        const uint32_t x01 = __builtin_amdgcn_perm(w1, w0, sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(w3, w2, sel);
-        const uint32_t ta = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
-        const uint32_t tb = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
-        vb[0][kk] = ta & 0x0F0F0F0Fu;
-        vb[1][kk] = (ta >> 4) & 0x0F0F0F0Fu;
-        vb[2][kk] = tb & 0x0F0F0F0Fu;
-        vb[3][kk] = (tb >> 4) & 0x0F0F0F0Fu;
+      for (int r = 0; r < NH; ++r) {
+        const uint4 a4 = *reinterpret_cast<const uint4*>(&p8[wave][r][ln >> 2][ln & 3][4 * lg]);
+        pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
+      for (int h = 0; h < 2; ++h) {
+        uint32_t vb[4][4];
 #pragma unroll
-        for (int r = 0; r < NH; ++r)
-          cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t w0 = X.vraw[0][kk], w1 = X.vraw[1][kk], w2 = X.vraw[2][kk], w3 = X.vraw[3][kk];
+          const uint32_t sel = h ? 0x07030602u : 0x05010400u;
+          const uint32_t x01 = __builtin_amdgcn_perm(w1, w0, sel);
+          const uint32_t x23 = __builtin_amdgcn_perm(w3, w2, sel);
+          const uint32_t ta = __builtin_amdgcn_perm(x23, x01, 0x05040100u);
+          const uint32_t tb = __builtin_amdgcn_perm(x23, x01, 0x07060302u);
+          vb[0][kk] = ta & 0x0F0F0F0Fu;
+          vb[1][kk] = (ta >> 4) & 0x0F0F0F0Fu;
+          vb[2][kk] = tb & 0x0F0F0F0Fu;
+          vb[3][kk] = (tb >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
+#pragma unroll
+          for (int r = 0; r < NH; ++r)
+            cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
+        }
       }
+      wave_sync();
     }
-    wave_sync();
   };
 
   Buf ring[2];
