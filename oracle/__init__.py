@@ -11,6 +11,7 @@ The shared object is compiled from source with gcc on first use (or by
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 import subprocess
@@ -30,16 +31,25 @@ VAL_U3, VAL_U4, VAL_FP8 = 1, 2, 3
 DT_F32, DT_F16, DT_BF16 = 0, 1, 2
 
 
+# Compiler flags of the oracle: no contraction, so each fp32 operation in
+# the source rounds exactly once as written.
+CFLAGS = ["-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fPIC", "-shared"]
+
+
+def compile_source(src: str, out: str, extra=()) -> str:
+    """Compile one oracle source file into a shared object at `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = False) -> str:
     """Compile tq_oracle.c into libtq_oracle.so with gcc (no contraction)."""
     if force or not os.path.exists(_LIB_PATH) or (
         os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
     ):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fPIC",
-             "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+        compile_source(_SRC, _LIB_PATH)
     return _LIB_PATH
 
 
@@ -47,66 +57,86 @@ def _p(a, ctype):
     return None if a is None else a.ctypes.data_as(C.POINTER(ctype))
 
 
+def _load(path):
+    """Load an oracle shared object and declare its signatures."""
+    L = C.CDLL(path)
+    i32, i64, f32, f64, u8, u16 = (C.c_int32, C.c_int64, C.c_float,
+                                   C.c_double, C.c_uint8, C.c_uint16)
+    P = C.POINTER
+    L.orc_f32_to_bf16.restype = u16; L.orc_f32_to_bf16.argtypes = [f32]
+    L.orc_bf16_to_f32.restype = f32; L.orc_bf16_to_f32.argtypes = [u16]
+    L.orc_f32_to_f16.restype = u16; L.orc_f32_to_f16.argtypes = [f32]
+    L.orc_f16_to_f32.restype = f32; L.orc_f16_to_f32.argtypes = [u16]
+    L.orc_f32_to_e4m3.restype = u8; L.orc_f32_to_e4m3.argtypes = [f32]
+    L.orc_e4m3_to_f32.restype = f32; L.orc_e4m3_to_f32.argtypes = [u8]
+    L.orc_fwht_f32.argtypes = [P(f32), i32]
+    L.orc_fwht_f64.argtypes = [P(f64), i32]
+    L.orc_int4_quantize_row.argtypes = [P(f32), i32, P(u8), P(f32)]
+    L.orc_int4_dequant_row.argtypes = [P(u8), f32, i32, P(f64)]
+    L.orc_reshape_and_cache_int4.restype = i32
+    L.orc_reshape_and_cache_int4.argtypes = [
+        C.c_void_p, C.c_void_p, i32, i64, i32, i32, P(i64), P(f32),
+        P(u8), P(u8), P(f32), P(f32), i64, i32]
+    L.orc_int4_decode.restype = i32
+    L.orc_int4_decode.argtypes = [
+        P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32),
+        P(f32), i32, i32, i32, i32, i32, i32, f64, P(i32), i32,
+        P(f64), P(f64)]
+    L.orc_int4_prefill.restype = i32
+    L.orc_int4_prefill.argtypes = [
+        P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32), P(i32), i32,
+        P(f32), i32, i32, i32, i32, f64, i32, f64, P(f32), P(f64)]
+    L.orc_tq_full_dequant.restype = i32
+    L.orc_tq_full_dequant.argtypes = [
+        P(u8), P(i32), i32, P(f32), i32, i32, i32, i32, i64, i32, i32, i32, i32, i32,
+        P(u16), P(u16)]
+    L.orc_tq_slot_bytes.restype = i32
+    L.orc_tq_slot_bytes.argtypes = [i32, i32, i32]
+    L.orc_lloyd_max_gaussian.argtypes = [i32, P(f64)]
+    L.orc_tq_encode.restype = i32
+    L.orc_tq_encode.argtypes = [
+        P(f32), P(f32), i64, i32, i32, i32, i32, P(f32), P(f32),
+        P(i64), P(u8), i64, i32, i32]
+    L.orc_tq_decode.restype = i32
+    L.orc_tq_decode.argtypes = [
+        P(f32), P(u8), P(i32), i32, P(i32), P(f32), P(f32), i32, i32,
+        i32, i32, i32, i32, i32, i32, i32, i32, f64, P(i32), i32,
+        P(f64), P(f64)]
+    L.orc_fwht128_quant_fp8.argtypes = [P(u16), i64, P(u8), P(f32)]
+    L.orc_fp8_pow2_scale.restype = f32
+    L.orc_fp8_pow2_scale.argtypes = [f32]
+    L.orc_convert.argtypes = [i32, C.c_void_p, C.c_void_p, i64]
+    L.orc_exp_f32.restype = f32
+    L.orc_exp_f32.argtypes = [f32]
+    L.orc_kpool_compress_and_write.restype = i32
+    L.orc_kpool_compress_and_write.argtypes = [
+        P(u16), C.c_void_p, i32, P(f32), P(i64), P(u8), i64, i32, i32,
+        P(u8), i64, i32, i32, P(u8), P(f32)]
+    return L
+
+
 def lib():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            L = C.CDLL(_LIB_PATH)
-            i32, i64, f32, f64, u8, u16 = (C.c_int32, C.c_int64, C.c_float,
-                                           C.c_double, C.c_uint8, C.c_uint16)
-            P = C.POINTER
-            L.orc_f32_to_bf16.restype = u16; L.orc_f32_to_bf16.argtypes = [f32]
-            L.orc_bf16_to_f32.restype = f32; L.orc_bf16_to_f32.argtypes = [u16]
-            L.orc_f32_to_f16.restype = u16; L.orc_f32_to_f16.argtypes = [f32]
-            L.orc_f16_to_f32.restype = f32; L.orc_f16_to_f32.argtypes = [u16]
-            L.orc_f32_to_e4m3.restype = u8; L.orc_f32_to_e4m3.argtypes = [f32]
-            L.orc_e4m3_to_f32.restype = f32; L.orc_e4m3_to_f32.argtypes = [u8]
-            L.orc_fwht_f32.argtypes = [P(f32), i32]
-            L.orc_fwht_f64.argtypes = [P(f64), i32]
-            L.orc_int4_quantize_row.argtypes = [P(f32), i32, P(u8), P(f32)]
-            L.orc_int4_dequant_row.argtypes = [P(u8), f32, i32, P(f64)]
-            L.orc_reshape_and_cache_int4.restype = i32
-            L.orc_reshape_and_cache_int4.argtypes = [
-                C.c_void_p, C.c_void_p, i32, i64, i32, i32, P(i64), P(f32),
-                P(u8), P(u8), P(f32), P(f32), i64, i32]
-            L.orc_int4_decode.restype = i32
-            L.orc_int4_decode.argtypes = [
-                P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32),
-                P(f32), i32, i32, i32, i32, i32, i32, f64, P(i32), i32,
-                P(f64), P(f64)]
-            L.orc_int4_prefill.restype = i32
-            L.orc_int4_prefill.argtypes = [
-                P(f32), P(u8), P(u8), P(f32), P(f32), P(i32), i32, P(i32), P(i32), i32,
-                P(f32), i32, i32, i32, i32, f64, i32, f64, P(f32), P(f64)]
-            L.orc_tq_full_dequant.restype = i32
-            L.orc_tq_full_dequant.argtypes = [
-                P(u8), P(i32), i32, P(f32), i32, i32, i32, i32, i64, i32, i32, i32, i32, i32,
-                P(u16), P(u16)]
-            L.orc_tq_slot_bytes.restype = i32
-            L.orc_tq_slot_bytes.argtypes = [i32, i32, i32]
-            L.orc_lloyd_max_gaussian.argtypes = [i32, P(f64)]
-            L.orc_tq_encode.restype = i32
-            L.orc_tq_encode.argtypes = [
-                P(f32), P(f32), i64, i32, i32, i32, i32, P(f32), P(f32),
-                P(i64), P(u8), i64, i32, i32]
-            L.orc_tq_decode.restype = i32
-            L.orc_tq_decode.argtypes = [
-                P(f32), P(u8), P(i32), i32, P(i32), P(f32), P(f32), i32, i32,
-                i32, i32, i32, i32, i32, i32, i32, i32, f64, P(i32), i32,
-                P(f64), P(f64)]
-            L.orc_fwht128_quant_fp8.argtypes = [P(u16), i64, P(u8), P(f32)]
-            L.orc_fp8_pow2_scale.restype = f32
-            L.orc_fp8_pow2_scale.argtypes = [f32]
-            L.orc_convert.argtypes = [i32, C.c_void_p, C.c_void_p, i64]
-            L.orc_exp_f32.restype = f32
-            L.orc_exp_f32.argtypes = [f32]
-            L.orc_kpool_compress_and_write.restype = i32
-            L.orc_kpool_compress_and_write.argtypes = [
-                P(u16), C.c_void_p, i32, P(f32), P(i64), P(u8), i64, i32, i32,
-                P(u8), i64, i32, i32, P(u8), P(f32)]
-            _lib = L
+            _lib = _load(build())
     return _lib
+
+
+@contextlib.contextmanager
+def use_library(path):
+    """Route every oracle call through another build of the oracle (a test
+    compiles a copy with one deliberate mistake to show that a pin catches
+    it); the regular library is restored on exit."""
+    global _lib
+    prev = lib()
+    with _lock:
+        _lib = _load(path)
+    try:
+        yield
+    finally:
+        with _lock:
+            _lib = prev
 
 
 # ---------------------------------------------------------------- converters

@@ -568,17 +568,20 @@ static void rotate_f64(const float* x, const float* rot_signs, int d, double* y)
  * fp16, u = Pi k / norm, index = nearest centroid (ties to the lower index;
  * norm 0 gives the centroid nearest 0). Values (b bits): scale =
  * max((max-min)/(2^b-1), 1e-6) and zero = min, both stored fp16; index =
- * clamp(rint((v - zero16) * (1 / scale16)), 0, 2^b-1) (one reciprocal per
- * row); a zero minimum is +0.
+ * clamp(rint((v - zero16) / scale16), 0, 2^b-1), an IEEE division per
+ * element; a zero minimum is +0.
  * Everything is fp32, each operation rounded once, in this order:
  *   ss   = sum of k_i^2, added pairwise with strides 1, 2, ..., d/2 (the
  *          order of the butterflies; see tree_sum_f32);
  *   norm = sqrt(ss) (correctly rounded);
- *   y    = FWHT(k * rot_signs) (strides 1 -> d/2), u_i = y_i * w with
- *          w = r / norm, r = the fp32 rounding of 1/sqrt(d);
+ *   y    = FWHT(k * rot_signs) (strides 1 -> d/2);
+ *   u_i  = (y_i * r) / norm, r = the fp32 rounding of 1/sqrt(d): the rotated
+ *          key Pi k, then divided by its norm, element by element;
  *   index_i = argmin_j |u_i - c_j|.
- * The pages fix none of these roundings; this order is the reading taken,
- * so that an fp32 encoder can reproduce the bytes exactly. */
+ * The pages fix none of these roundings. The two divisions follow the
+ * written forms u = Pi k / ||k|| and (v - zero) / scale; the summation
+ * order of the norm is the reading taken, fixed so that the bytes are a
+ * function of the input alone. */
 static float tree_sum_f32(float* s, int d) {
   for (int h = 1; h < d; h <<= 1)
     for (int i = 0; i < d; i += 2 * h) s[i] = s[i] + s[i + h];
@@ -616,9 +619,8 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
         const float r = (float)(1.0 / sqrt((double)d));
         for (int i = 0; i < d; ++i) y[i] = rot_signs ? k[i] * rot_signs[i] : k[i];
         orc_fwht_f32(y, d);
-        const float wn = nrm > 0.0f ? r / nrm : 0.0f;
         for (int i = 0; i < d; ++i) {
-          const float ui = y[i] * wn;
+          const float ui = nrm > 0.0f ? (y[i] * r) / nrm : 0.0f;
           int best = 0;
           float bd = fabsf(ui - centroids[0]);
           for (int j = 1; j < nc; ++j) {
@@ -652,9 +654,8 @@ int orc_tq_encode(const float* key, const float* value, int64_t num_tokens,
       uint16_t sc16 = orc_f32_to_f16(sc), z16 = orc_f32_to_f16(mn);
       float scr = orc_f16_to_f32(sc16), zr = orc_f16_to_f32(z16);
       uint8_t* vd = s + kps;
-      const float inv = 1.0f / scr;
       for (int i = 0; i < d; ++i) {
-        float idx = nearbyintf((v[i] - zr) * inv);
+        float idx = nearbyintf((v[i] - zr) / scr);
         if (idx < 0.0f) idx = 0.0f;
         if (idx > levels) idx = levels;
         put_bits(vd, i, vb, (unsigned)idx);
