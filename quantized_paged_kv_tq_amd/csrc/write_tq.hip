@@ -3,17 +3,18 @@
 // reads FP8 or Lloyd-Max centroid keys and uniform 3/4-bit values; the pages
 // show no writer). For each (token, kv head) with a valid slot:
 //   FP8 keys       e4m3(clamp(k, +-448)), D bytes;
-//   centroid keys  norm = sqrt(pairwise sum of k^2), u = FWHT(s * k) *
-//                  (fl(1/sqrt(D)) / norm), b-bit index of the nearest
+//   centroid keys  norm = sqrt(pairwise sum of k^2), u = (FWHT(s * k) *
+//                  fl(1/sqrt(D))) / norm, the rotated key divided by its
+//                  norm element by element; b-bit index of the nearest
 //                  centroid (ties to the lower index; norm 0: u = 0), packed
 //                  LSB first, then fp16(norm);
 //   values         scale = max((max - min) / (2^b - 1), 1e-6), zero = min,
-//                  both rounded to fp16; index = clamp(rint((v - zero16) *
-//                  (1 / scale16)), 0, 2^b - 1), packed LSB first; then fp16 scale
+//                  both rounded to fp16; index = clamp(rint((v - zero16) /
+//                  scale16), 0, 2^b - 1), packed LSB first; then fp16 scale
 //                  and zero; the slot's padding bytes are zeroed.
 // All arithmetic is fp32 with one rounding per operation in that order
-// (sums with strides 1 -> D/2, correctly rounded sqrt and division), which
-// is what makes the bytes reproducible.
+// (sums with strides 1 -> D/2, correctly rounded sqrt, IEEE division per
+// element), which is what makes the bytes reproducible.
 //
 // Lane layout as the INT4 writer (write_rows.h): D/16 lanes per row, a lane
 // holds 8 consecutive elements per half, i.e. whole bytes of a 3- or 4-bit
@@ -69,9 +70,20 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
 // [c[j], c[j+1]] for which |u - c[j+1]| < |u - c[j]| in fp32, the same
 // comparison, ties to the lower index, as a full scan. T[j] is found by
 // bisection over the fp32 values of that interval (ordered as integers).
+// The key encoder divides, u = Y / norm with Y = fl(y * fl(1/sqrt(D))), and
+// the index counts the thresholds T with fl(Y / norm) >= T. Since fp32
+// rounding is monotone, fl(x) >= T exactly when x >= mid (T with an even
+// significand, which wins the tie at mid) or x > mid (odd), mid being the
+// midpoint between T and the fp32 number below it. For norm > 0 that is
+// Y >= P or Y > P with P = norm * mid, exact in fp64 (mid has at most 25
+// significant bits, the norm 24). Y is an fp32 number, so the condition is
+// Y >= Yc, with Yc the least fp32 number >= P (> P for odd T): seven fp32
+// bounds per row replace the division of every element. bnd[j] holds mid
+// and odd[j] the parity of T[j].
 template <int NC>
 __device__ __forceinline__ bool centroid_thresholds(const float (&cen)[NC], const float* centroids,
-                                                    float (&thr)[NC - 1]) {
+                                                    float (&thr)[NC - 1], double (&bnd)[NC - 1],
+                                                    bool (&odd)[NC - 1]) {
   bool ok = true;
 #pragma unroll
   for (int j = 0; j < NC; ++j) ok = ok && fabsf(cen[j]) <= 1.0f;
@@ -98,8 +110,26 @@ __device__ __forceinline__ bool centroid_thresholds(const float (&cen)[NC], cons
   }
   const float t = unkey(hi);
 #pragma unroll
-  for (int k = 0; k + 1 < NC; ++k) thr[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), k));
+  for (int k = 0; k + 1 < NC; ++k) {
+    thr[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), k));
+    const float below = unkey(key(thr[k]) - 1u);
+    bnd[k] = ((double)below + (double)thr[k]) * 0.5;  // exact
+    odd[k] = (f2u(thr[k]) & 1u) != 0u;
+  }
   return true;
+}
+
+// The fp32 number just above x (x finite): one step of the bit pattern.
+__device__ __forceinline__ float next_up(float x) {
+  if (x == 0.0f) return u2f(1u);
+  return u2f(x > 0.0f ? f2u(x) + 1u : f2u(x) - 1u);
+}
+
+// The least fp32 number >= p (strict: > p), p an exact fp64 value.
+__device__ __forceinline__ float f32_ceil(double p, bool strict) {
+  const float f = (float)p;  // nearest
+  const double fd = (double)f;
+  return (strict ? fd <= p : fd < p) ? next_up(f) : f;
 }
 
 // Centroid key of one row (D/16 lanes, 16 elements per lane): norm by
@@ -107,7 +137,8 @@ __device__ __forceinline__ bool centroid_thresholds(const float (&cen)[NC], cons
 template <int D, int KB>
 __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* s, int li,
                                                     const float (&cen)[1 << KB], bool fast,
-                                                    const float (&thr)[(1 << KB) - 1],
+                                                    const double (&bnd)[(1 << KB) - 1],
+                                                    const bool (&odd)[(1 << KB) - 1],
                                                     const float* rot_signs, int kps,
                                                     const float sg[4]) {
   constexpr int LPR = D / 16;
@@ -149,21 +180,27 @@ __device__ __forceinline__ void encode_centroid_key(const float v[16], uint8_t* 
   fwht_row<LPR>(y, sg);
   // fp32 1/sqrt(D)
   const float rs = D == 128 ? 0.0883883461356163f : (D == 64 ? 0.125f : 0.0625f);
-  const float wn = nrm > 0.0f ? rs / nrm : 0.0f;
+  const bool pos = nrm > 0.0f;
   uint32_t q[16];
   if (fast) {  // uniform
+    // fl(Y / norm) >= T[c]  <=>  Y >= Yc[c] (see centroid_thresholds); a zero
+    // norm gives u = 0: Y = 0 against the bounds for norm 1 (which are T)
+    const double nd = pos ? (double)nrm : 1.0;
+    float Yc[(1 << KB) - 1];
+#pragma unroll
+    for (int c = 0; c + 1 < (1 << KB); ++c) Yc[c] = f32_ceil(nd * bnd[c], odd[c]);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float u = y[j] * wn;
+      const float Y = pos ? y[j] * rs : 0.0f;
       uint32_t n = 0;
 #pragma unroll
-      for (int c = 0; c + 1 < (1 << KB); ++c) n += u >= thr[c] ? 1u : 0u;
+      for (int c = 0; c + 1 < (1 << KB); ++c) n += Y >= Yc[c] ? 1u : 0u;
       q[j] = n;
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float u = y[j] * wn;
+      const float u = pos ? (y[j] * rs) / nrm : 0.0f;
       uint32_t best = 0;
       float bd = fabsf(u - cen[0]);
 #pragma unroll
@@ -198,9 +235,11 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
   const int it_in = (wave >> 1) * (64 / LPR) + (threadIdx.x & 63) / LPR;
   // key waves of a centroid format: decision thresholds of the table
   float thr[NC > 1 ? NC - 1 : 1];
+  double bnd[NC > 1 ? NC - 1 : 1];
+  bool odd[NC > 1 ? NC - 1 : 1];
   bool fast = false;
   if constexpr (KB != 8) {
-    if (!values) fast = centroid_thresholds<NC>(cen, a.centroids, thr);
+    if (!values) fast = centroid_thresholds<NC>(cen, a.centroids, thr, bnd, odd);
   }
   float sg[4];
 #pragma unroll
@@ -245,7 +284,7 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
         *reinterpret_cast<uint2*>(s + D / 2 + 8 * li) = make_uint2(w[2], w[3]);
         continue;
       } else {
-        encode_centroid_key<D, KB>(v, s, li, cen, fast, thr, a.rot_signs, a.kps, sg);
+        encode_centroid_key<D, KB>(v, s, li, cen, fast, bnd, odd, a.rot_signs, a.kps, sg);
         continue;
       }
     }
@@ -287,11 +326,19 @@ __global__ __launch_bounds__(256) void write_tq_kernel(TqWriteArgs a) {
     const uint16_t sc16 = f16_bits(sc), z16 = f16_bits(mn);
     const float scr = (float)__builtin_bit_cast(_Float16, sc16);
     const float zr = (float)__builtin_bit_cast(_Float16, z16);
+    // index = rint(fl((v - zero16) / scale16)). With t = fl(a * fl(1/scale16))
+    // (a = v - zero16), |t - fl(a / scale16)| < |t| * 2^-22 (three roundings
+    // of at most 2^-24 relative each), so both round to the same integer
+    // unless t lies within |t| * 2^-21 of a half-integer; only then (rarely)
+    // is the quotient itself computed.
     const float inv = 1.0f / scr;
     uint32_t q[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      float idx = __builtin_rintf((v[j] - zr) * inv);
+      const float a = v[j] - zr;
+      const float t = a * inv;
+      float idx = __builtin_rintf(t);
+      if (!(fabsf(t - idx) < __builtin_fmaf(fabsf(t), -0x1p-21f, 0.5f))) idx = __builtin_rintf(a / scr);
       idx = idx < 0.0f ? 0.0f : (idx > levels ? levels : idx);
       q[j] = (uint32_t)idx;
     }

@@ -1,5 +1,7 @@
 """GPU parity of the cache writers against the CPU oracle (bit-exact):
 tq_reshape_and_cache_int4 and fwht128_quant_fp8, through the C ABI."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -252,3 +254,44 @@ def test_tq_encode_head_dim_256(fmt, dtype):
     rs = None if fmt[0] == oracle.KEY_FP8 else W.rht_signs(d, round_idx=5)
     _encode_both(wl["key"], wl["value"], dtype, wl["slot_mapping"], wl["num_blocks"], 16, hk, d,
                  *fmt, rot_signs=rs)
+
+
+def test_tq_encode_rounding_boundaries():
+    """Rows that sit on the encoder's rounding boundaries: the hand-derived
+    slot of golden/rounding_readings.json (a key coordinate 2^-25 above a
+    decision threshold, a value quotient 4.3e-7 above a half-integer), keys
+    whose rotated coordinates cluster at a threshold (four nearly equal
+    entries: u = 1/4 + O(1e-4)), and value rows whose quotients lie within a
+    few ulps of half-integers (both sides of the rounding check)."""
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "rounding_readings.json")))["tq_slot_division_and_norm_order"]
+    d, hk = 64, 1
+    rng = np.random.default_rng(77)
+    T = 2048
+    k = np.zeros((T, hk, d), np.float32)
+    k[:, 0, :4] = (1 + rng.uniform(-1e-3, 1e-3, (T, 4))).astype(np.float32)
+    k[0, 0] = np.array([int(h, 16) for h in g["key_f32_hex"]], np.uint32).view(np.float32)
+    v = np.empty((T, hk, d), np.float32)
+    for t in range(T):
+        s16 = np.float16(rng.uniform(0.05, 3.0))
+        z16 = np.float16(rng.uniform(-4.0, 0.0))
+        s, z = np.float32(s16), np.float32(z16)
+        row = np.empty(d, np.float32)
+        row[0], row[1] = z, np.float32(z + np.float32(15) * s)
+        kk = rng.integers(0, 15, d - 2).astype(np.float32)
+        base = (z + (kk + np.float32(0.5)) * s).astype(np.float32)
+        steps = rng.integers(-3, 4, d - 2)
+        for i in range(d - 2):
+            x = base[i]
+            for _ in range(abs(int(steps[i]))):
+                x = np.nextafter(x, np.float32(np.inf) if steps[i] > 0 else np.float32(-np.inf))
+            row[2 + i] = x
+        v[t, 0] = row
+    v[0, 0] = np.array([int(h, 16) for h in g["value_f32_hex"]], np.uint32).view(np.float32)
+    slots = rng.permutation(T).astype(np.int64)
+    step = np.array(g["centroids"], np.float32)
+    lm = (oracle.lloyd_max_gaussian(8) / np.sqrt(d)).astype(np.float32)
+    for cen in (step, lm):
+        _encode_both(k, v, "f32", slots, T // 16, 16, hk, d, oracle.KEY_MSE3, oracle.VAL_U4, cen=cen)
+    _encode_both(k, v, "f32", slots, T // 16, 16, hk, d, oracle.KEY_MSE3, oracle.VAL_U3, cen=step)
