@@ -31,6 +31,9 @@
  *   - Pointers named "device" are HIP device pointers owned by the caller; the
  *     library never allocates, frees or synchronizes, and keeps no pointer
  *     after the call returns. `stream` is a hipStream_t (NULL: null stream).
+ *     (tq_decode_attention_static, the variant for callers that cannot
+ *     allocate, takes its workspace from a static device array of the
+ *     library instead of the caller's.)
  *   - Tensors are dense and row-major in the shapes given (C order).
  *   - Return value: TQ_OK, or a negative code; nothing is launched unless
  *     TQ_OK is returned (TQ_ELAUNCH: the launch itself failed). The message of
@@ -242,10 +245,43 @@ typedef struct tq_decode_args {
 size_t tq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hk, int32_t D,
                                  int32_t num_kv_splits);
 
-/* Padded combined-slot size for a TurboQuant format, or -1 if invalid. */
+/*
+ * Padded combined-slot size for a TurboQuant format, or -1 if invalid.
+ * triton_turboquant_decode.py passes the slot width (padded_slot) and the key
+ * region size (key_packed_size) in from outside: _get_layout derives only
+ * the index bytes (mse_bytes = ceil(D * bits / 8), val_data_bytes), and
+ * _tq_decode_stage1 reads the fp16 norm right after the key indices and the
+ * fp16 scale and zero right after the value indices. The reading taken:
+ * key region = D bytes (FP8 keys) or mse_bytes + 2 (centroid keys); value
+ * region = val_data_bytes, + 4 for uniform values; the slot is that sum
+ * rounded up to a multiple of 16 bytes.
+ */
 int32_t tq_slot_bytes(int32_t D, int32_t key_fmt, int32_t val_fmt);
 
 int tq_decode_attention(const tq_decode_args* args, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as tq_decode_attention, with the stage-1 workspace taken from a
+ * static device array of TQ_STATIC_WORKSPACE_BYTES inside the library
+ * instead of args->workspace (args->workspace and args->workspace_bytes are
+ * ignored). Each GPU that runs it holds its own copy of the array until the
+ * process ends; the array's device address is looked up on the first call
+ * on each device. The call allocates nothing and frees nothing.
+ *   Limit: tq_decode_workspace_bytes(B, Hq, Hk, D, S) must not exceed
+ *   TQ_STATIC_WORKSPACE_BYTES, else TQ_EINVAL, nothing launched, and
+ *   tq_last_error() names the sizes.
+ *   Contents: nothing in the array needs to start at zero (stage 1 writes
+ *   every value stage 2 reads); it keeps the last call's partials.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls
+ *   that overlap on one GPU (several streams, or several threads) race;
+ *   order them on one stream.
+ * Other arguments, validation, errors and results are those of
+ * tq_decode_attention.
+ */
+#define TQ_STATIC_WORKSPACE_BYTES ((size_t)64 << 20) /* 64 MiB per GPU */
+int tq_decode_attention_static(const tq_decode_args* args, void* stream);
 
 /*
  * Hadamard-128 + power-of-two-scale FP8 (kpool_compress.py,

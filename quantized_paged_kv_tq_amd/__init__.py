@@ -7,6 +7,8 @@ in the library's HIP kernels. torch supplies device memory and streams.
     tq_reshape_and_cache_int4   RHT + INT4 paged-cache write
     tq_encode_and_cache         TurboQuant combined-slot cache write
     tq_decode_attention         split-KV decode (stage 1 + stage 2)
+    tq_decode_attention_static  the same, with the library's static
+                                workspace (for callers that cannot allocate)
     fwht128_quant_fp8           Hadamard-128 + power-of-two-scale FP8
     tq_prefill_attention_int4   multi-query (prefill) attention over the
                                 INT4 cache
@@ -90,6 +92,7 @@ SYMBOLS = {
     "tq_decode_workspace_bytes": (C.c_size_t, [C.c_int32] * 5),
     "tq_slot_bytes": (C.c_int32, [C.c_int32] * 3),
     "tq_decode_attention": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
+    "tq_decode_attention_static": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "tq_prefill_attention_int4": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
     "tq_full_dequant_kv": (C.c_int, [
@@ -254,8 +257,10 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
                    key_cache=None, value_cache=None, k_scale_cache=None, v_scale_cache=None,
                    rht_signs=None, kv_cache=None, key_fmt=KEY_INT4, val_fmt=VAL_INT4,
                    centroids=None, rot_signs=None, norm_correction=False, num_kv_heads=None,
-                   workspace=None, out=None, lse=None, flags=0):
-    """Validate and marshal a tq_decode_attention call; returns (Prepared, out, lse)."""
+                   workspace=None, out=None, lse=None, flags=0, static_workspace=False):
+    """Validate and marshal a tq_decode_attention call; returns (Prepared, out, lse).
+    static_workspace=True marshals tq_decode_attention_static instead, which
+    takes its workspace from the library (no workspace argument)."""
     B, hq, d = query.shape
     _need(query, torch.float32, "query")
     _need(block_table, torch.int32, "block_table")
@@ -284,18 +289,22 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
     if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
         raise ValueError("block_table must be [B, max_blocks], seq_lens [B]")
     dev = query.device
-    if workspace is None:
+    if static_workspace:
+        if workspace is not None:
+            raise ValueError("the static entry point takes no workspace")
+    elif workspace is None:
         nbytes = tq_decode_workspace_bytes(B, hq, hk, d, num_kv_splits)
         workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=dev)
     if out is None:
         out = torch.empty(B, hq, d, dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(B, hq, dtype=torch.float32, device=dev)
-    _need(workspace, torch.float32, "workspace")
+    if not static_workspace:
+        _need(workspace, torch.float32, "workspace")
+        if workspace.numel() * 4 < tq_decode_workspace_bytes(B, hq, hk, d, num_kv_splits):
+            raise ValueError("workspace too small")
     _need(out, torch.float32, "out")
     _need(lse, torch.float32, "lse")
-    if workspace.numel() * 4 < tq_decode_workspace_bytes(B, hq, hk, d, num_kv_splits):
-        raise ValueError("workspace too small")
     a = DecodeArgs()
     a.struct_size = C.sizeof(DecodeArgs)
     a.flags = flags
@@ -311,10 +320,11 @@ def prepare_decode(query, block_table, seq_lens, *, num_kv_splits, sm_scale=None
     a.kv_cache, a.slot_bytes = _ptr(kv_cache), slot_bytes
     a.centroids, a.rot_signs = _ptr(centroids), _ptr(rot_signs)
     a.workspace, a.out, a.lse = _ptr(workspace), _ptr(out), _ptr(lse)
-    a.workspace_bytes = workspace.numel() * 4
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * 4
     keep = [query, block_table, seq_lens, key_cache, value_cache, k_scale_cache, v_scale_cache,
             rht_signs, kv_cache, centroids, rot_signs, workspace, out, lse]
-    return Prepared(lib().tq_decode_attention, (C.byref(a),), keep + [a]), out, lse
+    fn = lib().tq_decode_attention_static if static_workspace else lib().tq_decode_attention
+    return Prepared(fn, (C.byref(a),), keep + [a]), out, lse
 
 
 def tq_decode_attention(query, block_table, seq_lens, *, stream=None, **kw):
@@ -326,6 +336,15 @@ def tq_decode_attention(query, block_table, seq_lens, *, stream=None, **kw):
     workspace/out/lse may be passed pre-allocated (no allocation then).
     """
     call, out, lse = prepare_decode(query, block_table, seq_lens, **kw)
+    call.run(stream, query.device)
+    return out, lse
+
+
+def tq_decode_attention_static(query, block_table, seq_lens, *, stream=None, **kw):
+    """tq_decode_attention through the library's static workspace (the C
+    entry point allocates nothing; see include/tq.h). Calls that overlap on
+    one GPU share that workspace and race."""
+    call, out, lse = prepare_decode(query, block_table, seq_lens, static_workspace=True, **kw)
     call.run(stream, query.device)
     return out, lse
 

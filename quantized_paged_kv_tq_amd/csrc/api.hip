@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "tq.h"
 #include "balance.h"
@@ -337,7 +338,14 @@ int tq_full_dequant_kv(const uint8_t* kv_cache, const int32_t* block_table, int3
                   "tq_full_dequant_kv");
 }
 
-int tq_decode_attention(const tq_decode_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// tq_decode_attention with the stage-1 workspace `ws` of `ws_bytes` bytes
+// (the caller's, or the library's static one); `name` labels the errors.
+int decode_impl(const tq_decode_args* a, float* ws, int64_t ws_bytes, const char* name,
+                void* stream) {
   if (!a) return fail(TQ_EINVAL, "null args");
   if (a->struct_size < sizeof(tq_decode_args))
     return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size, sizeof(tq_decode_args));
@@ -362,7 +370,7 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
     g_err[0] = '\0';
     return TQ_OK;
   }
-  if (!a->query || !a->block_table || !a->seq_lens || !a->workspace || !a->out)
+  if (!a->query || !a->block_table || !a->seq_lens || !ws || !a->out)
     return fail(TQ_EINVAL, "null pointer argument");
   tqk::DecodeParams p{};
   if (int4) {
@@ -383,12 +391,12 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
     p.kps = key_region_bytes(a->D, a->key_fmt);
     p.vdb = value_index_bytes(a->D, a->val_fmt);
   }
-  if (!aligned(a->query, 16) || !aligned(a->workspace, 16) || !aligned(a->out, 16))
+  if (!aligned(a->query, 16) || !aligned(ws, 16) || !aligned(a->out, 16))
     return fail(TQ_EINVAL, "query / workspace / out must be 16-byte aligned");
   {
     const size_t need = tq_decode_workspace_bytes(a->B, a->Hq, a->Hk, a->D, a->num_kv_splits);
-    if (a->workspace_bytes < 0 || (size_t)a->workspace_bytes < need)
-      return fail(TQ_EINVAL, "workspace_bytes %lld < %zu", (long long)a->workspace_bytes, need);
+    if (ws_bytes < 0 || (size_t)ws_bytes < need)
+      return fail(TQ_EINVAL, "%s: workspace_bytes %lld < %zu", name, (long long)ws_bytes, need);
   }
   p.B = a->B; p.hq = a->Hq; p.hk = a->Hk; p.d = a->D; p.g = a->Hq / a->Hk;
   p.block_size = a->block_size; p.max_blocks = a->max_blocks; p.splits = a->num_kv_splits;
@@ -398,9 +406,9 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
   p.kc = a->key_cache; p.vc = a->value_cache; p.ks = a->k_scale_cache; p.vs = a->v_scale_cache;
   p.rht_signs = a->rht_signs; p.kv = a->kv_cache; p.slot_bytes = a->slot_bytes;
   p.centroids = a->centroids; p.rot_signs = a->rot_signs;
-  p.ws = a->workspace; p.out = a->out; p.lse = a->lse;
+  p.ws = ws; p.out = a->out; p.lse = a->lse;
   p.nw = 0; p.wgh = 1;
-  p.wsp = a->workspace + (int64_t)a->B * a->Hq * a->num_kv_splits * (a->D + 1);
+  p.wsp = ws + (int64_t)a->B * a->Hq * a->num_kv_splits * (a->D + 1);
   {
     const int g = a->Hq / a->Hk;
     p.wsx = reinterpret_cast<int*>(
@@ -415,8 +423,67 @@ int tq_decode_attention(const tq_decode_args* a, void* stream) {
     else e = tqk::launch_decode_tqb_mfma(p, st);
   }
   if (e == hipErrorNotSupported) e = tqk::launch_decode_generic(p, st);
-  if (e != hipSuccess) return launched(e, "tq_decode_attention stage 1");
-  return launched(tqk::launch_merge(p, st), "tq_decode_attention stage 2");
+  char what[96];
+  snprintf(what, sizeof(what), "%s stage 1", name);
+  if (e != hipSuccess) return launched(e, what);
+  snprintf(what, sizeof(what), "%s stage 2", name);
+  return launched(tqk::launch_merge(p, st), what);
+}
+
+// Workspace of tq_decode_attention_static: a file-scope device array. Every
+// GPU that loads the library holds its own copy, at its own address, until
+// the process ends. In host code `scratch` names a host-side stand-in, so
+// the kernels receive the device address that hipGetSymbolAddress returns,
+// looked up once per device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[TQ_STATIC_WORKSPACE_BYTES / sizeof(float)];
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+int scratch_address(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TQ_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TQ_ENOTSUP, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(TQ_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_decode_attention(const tq_decode_args* a, void* stream) {
+  if (!a) return fail(TQ_EINVAL, "null args");
+  return decode_impl(a, a->workspace, a->workspace_bytes, "tq_decode_attention", stream);
+}
+
+int tq_decode_attention_static(const tq_decode_args* a, void* stream) {
+  if (!a) return fail(TQ_EINVAL, "null args");
+  if (a->struct_size >= sizeof(tq_decode_args) && a->B > 0 && a->Hq > 0 && a->Hk > 0 &&
+      a->D > 0 && a->num_kv_splits > 0) {
+    const size_t need = tq_decode_workspace_bytes(a->B, a->Hq, a->Hk, a->D, a->num_kv_splits);
+    if (need > (size_t)TQ_STATIC_WORKSPACE_BYTES)
+      return fail(TQ_EINVAL,
+                  "tq_decode_attention_static: B=%d Hq=%d D=%d S=%d needs %zu workspace bytes, "
+                  "above the static maximum of %zu; use tq_decode_attention with a workspace",
+                  a->B, a->Hq, a->D, a->num_kv_splits, need, (size_t)TQ_STATIC_WORKSPACE_BYTES);
+  }
+  float* ws = nullptr;
+  if (a->B > 0) {
+    const int r = scratch_address(&ws);
+    if (r != TQ_OK) return r;
+  }
+  return decode_impl(a, ws, TQ_STATIC_WORKSPACE_BYTES, "tq_decode_attention_static", stream);
 }
 
 }  // extern "C"

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert set(names) == {"tq_last_error", "tq_version", "tq_reshape_and_cache_int4",
                           "tq_encode_and_cache", "tq_decode_workspace_bytes", "tq_slot_bytes",
-                          "tq_decode_attention", "fwht128_quant_fp8",
+                          "tq_decode_attention", "tq_decode_attention_static",
+                          "fwht128_quant_fp8",
                           "tq_kpool_compress_and_write_cache", "tq_prefill_attention_int4",
                           "tq_full_dequant_kv"}
     raw = C.CDLL(tq.LIB_PATH)
@@ -284,3 +285,16 @@ def test_full_dequant_validation(L):
     assert call(kf=tq.KEY_MSE3, vf=tq.VAL_U3, sb=112, cen=None) == tq.TQ_EINVAL
     assert call(kv=None) == tq.TQ_EINVAL
     assert call(k=8) == tq.TQ_EINVAL             # misaligned output
+
+
+def test_static_decode_size_limit_and_empty_batch(L):
+    """The static-workspace entry point rejects a call whose workspace would
+    exceed its fixed maximum (before touching any GPU) and returns TQ_OK for
+    an empty batch."""
+    B, hq, hk, d, S = 4096, 64, 8, 128, 64
+    assert tq.tq_decode_workspace_bytes(B, hq, hk, d, S) > 64 << 20
+    a = _args(B=B, Hq=hq, Hk=hk, D=d, num_kv_splits=S)
+    assert L.tq_decode_attention_static(C.byref(a), None) == tq.TQ_EINVAL
+    assert "static maximum" in tq.last_error()
+    assert L.tq_decode_attention_static(None, None) == tq.TQ_EINVAL
+    assert L.tq_decode_attention_static(C.byref(_args(B=0)), None) == tq.TQ_OK
