@@ -14,7 +14,10 @@ Printed: one JSON line (rank 0). `value` is the step's algorithmic HBM
 bytes / step time in TB/s. `roofline` covers the decode call (stage 1 +
 stage 2 kernels), timed with HIP events on the stream it runs on.
 `cpu_baseline` times the CPU oracle (tests' reference implementation) on a
-bounded sample of the same step on the host cores.
+bounded sample of the same step on the host cores, single-threaded and on
+all the cores this process may use (at most 16), with the core count and
+CPU model. `copy_calibration_TBps` is a 512 MiB device copy timed in the
+same run. Every GPU time is the median of 5 event-timed runs.
 
 Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
 tq_mixed_b, tq_fp8_values (the tq_mixed shape with FP8 keys and values),
@@ -64,6 +67,54 @@ class Events:
         b.record(self.stream)
         b.synchronize()
         return a.elapsed_time(b) / n * 1e-3  # seconds per call
+
+    def median(self, fn, n, reps=5):
+        """Median over `reps` event-timed runs of n back-to-back calls (the
+        call index keeps counting across runs, so cache copies keep
+        rotating); returns (median, min, max) seconds per call."""
+        ts = []
+        for r in range(reps):
+            ts.append(self.time(lambda i: fn(r * n + i), n))
+        ts.sort()
+        return ts[len(ts) // 2], ts[0], ts[-1]
+
+
+def copy_calibration(torch, stream, warmup=3, n=20):
+    """Device-to-device copy of 512 MiB on the same stream: the streaming
+    rate this machine's HBM reaches with a plain copy (read + write bytes)."""
+    dev = torch.device("cuda:0")
+    nbytes = 512 * 2 ** 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(warmup):
+        b.copy_(a)
+    t, _, _ = Events(torch, stream).median(lambda i: b.copy_(a), n)
+    del a, b
+    return 2 * nbytes / t
+
+
+def host_cpu():
+    """Host CPU facts for the CPU baseline: logical CPUs, the ones this
+    process may run on, and the model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count() or 1
+    return dict(nproc=os.cpu_count() or 1, allowed=allowed, model=model)
+
+
+# Worker threads of the CPU baselines: the host cores this process may use,
+# at most 16 (the CPU share of one GPU on the measurement boxes).
+CPU_THREAD_CAP = 16
 
 
 def decode_bytes(w, splits_nonempty):
@@ -177,61 +228,124 @@ def run_int4(args, torch, tq, W, name):
         step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    # decode call alone, HIP events on its stream
-    t_dec = ev.time(decode, max(args.steps, 20))
+    # decode call alone, HIP events on its stream: median of 5 runs
+    t_dec, t_min, t_max = ev.median(decode, max(args.steps, 20))
     b = decode_bytes(w, nonempty_splits(w.seq_lens, S))
     wb = w.B * w.hk * (2 * w.d * 2 + (w.d + 8)) + w.B * 8
     step_bytes = b["total"] + wb
-    res = dict(w=w, wall=wall, t_dec=t_dec, bytes=b, step_bytes=step_bytes, sets=sets, q=q,
-               signs=signs)
+    res = dict(w=w, wall=wall, t_dec=t_dec, t_dec_range=(t_min, t_max), bytes=b,
+               step_bytes=step_bytes, sets=sets, q=q, signs=signs)
     return res
 
 
-def cpu_baseline_int4(res, W, budget_s):
-    """Time the oracle on a bounded sample of the step: the decode of whole
-    sequences (all query heads) until about budget_s of CPU work, on a
-    thread pool (ctypes releases the GIL); scaled to TB/s of the same
-    algorithmic bytes."""
+def _cpu_rate(work, units, budget_s, threads):
+    """Run work(i) over units 0, 1, ... (cycling) on `threads` threads until
+    about budget_s seconds have passed; work returns the algorithmic bytes
+    of its item. Returns (items, bytes, seconds). Each work item is one
+    oracle call (ctypes releases the GIL)."""
     import concurrent.futures as cf
+    done, nbytes, t0 = 0, 0, time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        while time.perf_counter() - t0 < budget_s:
+            batch = [(done + k) % units for k in range(threads)]
+            nbytes += sum(pool.map(work, batch))
+            done += len(batch)
+    return done, nbytes, time.perf_counter() - t0
 
+
+def cpu_baseline(work, units, budget_s, what):
+    """The oracle on a bounded sample of the workload: single-thread, then
+    on all the host cores this process may use (at most CPU_THREAD_CAP),
+    each for about half of budget_s. Rates are algorithmic bytes per second
+    (the same byte count as the GPU line), `value` the all-core one."""
+    cpu = host_cpu()
+    threads = max(1, min(CPU_THREAD_CAP, cpu["allowed"]))
+    n1, b1, t1 = _cpu_rate(work, units, budget_s / 2, 1)
+    nn, bn, tn = _cpu_rate(work, units, budget_s / 2, threads)
+    r1 = b1 / t1
+    rn = bn / tn
+    return dict(value=rn / 1e12, unit="TB/s", cores=threads, kind="oracle",
+                single_thread=r1 / 1e12, all_core=rn / 1e12, nproc=cpu["nproc"],
+                cpus_allowed=cpu["allowed"], cpu_model=cpu["model"],
+                sample="%s: %d items in %.1f s on 1 thread, %d items in %.1f s on %d threads "
+                       "(the host's CPU share, at most %d)" % (
+                           what, n1, t1, nn, tn, threads, CPU_THREAD_CAP))
+
+
+def cpu_baseline_int4(res, W, budget_s):
+    """The fp64 oracle decode of single (sequence, kv head) units -- all the
+    query heads of one kv head of one sequence -- cycling over the batch,
+    scaled to TB/s of the same KV bytes the GPU line counts."""
     import oracle
-    import torch
     w = res["w"]
     kc, vc, ks, vs = (t.cpu().numpy() for t in res["sets"][0])
     q = res["q"].cpu().numpy()
     signs = res["signs"].cpu().numpy()
-    threads = min(16, os.cpu_count() or 1)
-    order = np.argsort(w.seq_lens)  # start from short sequences
-    done_bytes, t_used, used_seqs, passes = 0, 0.0, 0, 0
-    pool = cf.ThreadPoolExecutor(max_workers=threads)
-    # whole sequences (all query heads), cycling over the batch until the
-    # time budget is spent
-    while t_used < budget_s:
-        for b in order:
-            rows = np.arange(b * w.hq, (b + 1) * w.hq, dtype=np.int32)
-            chunks = np.array_split(rows, min(threads, len(rows)))
-            t0 = time.perf_counter()
-            list(pool.map(lambda r: oracle.int4_decode(q, kc, vc, ks, vs, w.block_table,
-                                                       w.seq_lens, signs, w.num_splits,
-                                                       w.sm_scale, r), chunks))
-            t_used += time.perf_counter() - t0
-            done_bytes += int(w.seq_lens[b]) * w.hk * (w.d + 8)
-            used_seqs += 1
-            if t_used >= budget_s:
-                break
-        passes += 1
-    pool.shutdown()
-    return dict(value=done_bytes / t_used / 1e12, unit="TB/s", cores=threads, kind="oracle",
-                sample="fp64 oracle decode of %d sequence-passes over the %d sequences "
-                       "(all %d query heads each; %d pass(es) over the batch), KV bytes only, "
-                       "%.1f s on %d threads" % (used_seqs, w.B, w.hq, passes, t_used, threads))
+    g = w.hq // w.hk
+    units = [(b, h) for b in range(w.B) for h in range(w.hk)]
+    kv_bytes = [int(w.seq_lens[b]) * (w.d + 8) for b, h in units]
+
+    def work(i):
+        b, h = units[i]
+        rows = np.arange(b * w.hq + h * g, b * w.hq + (h + 1) * g, dtype=np.int32)
+        oracle.int4_decode(q, kc, vc, ks, vs, w.block_table, w.seq_lens, signs, w.num_splits,
+                           w.sm_scale, rows)
+        return kv_bytes[i]
+
+    return cpu_baseline(work, len(units), budget_s,
+                        "fp64 oracle decode of (sequence, kv head) units of the %s batch "
+                        "(%d query heads each), KV bytes" % (w.name, g))
+
+
+def cpu_baseline_write(wl, W, budget_s):
+    """The oracle INT4 cache writer on chunks of 512 tokens of the write
+    workload (each into its own small cache), scaled to TB/s of the same
+    algorithmic bytes as the GPU line (source rows read, codes and scale
+    words written, slot indices read)."""
+    import oracle
+    T, hk, d = wl["key"].shape
+    chunk = 512
+    units = T // chunk
+    signs = W.rht_signs(d)
+    slots = wl["slot_mapping"]
+
+    def work(i):
+        sl = slots[i * chunk:(i + 1) * chunk]
+        local = np.where(sl >= 0, np.arange(chunk, dtype=np.int64), -1)
+        kc = np.zeros((chunk // 16, 16, hk, d // 2), np.uint8)
+        vc = np.zeros_like(kc)
+        ks = np.zeros((chunk // 16, 16, hk), np.float32)
+        vs = np.zeros_like(ks)
+        oracle.reshape_and_cache_int4(wl["key"][i * chunk:(i + 1) * chunk],
+                                      wl["value"][i * chunk:(i + 1) * chunk], oracle.DT_BF16,
+                                      local, signs, kc, vc, ks, vs)
+        return int((sl >= 0).sum()) * hk * (2 * d * 2 + (d + 8)) + chunk * 8
+
+    return cpu_baseline(work, units, budget_s,
+                        "oracle reshape_and_cache_int4 of 512-token chunks of the 65536 x 8 x 128 "
+                        "bf16 rows (5% skipped)")
+
+
+def cpu_baseline_fwht(bits, budget_s):
+    """The oracle fwht128_quant_fp8 on chunks of 4096 rows of the 1M-row
+    input, scaled to TB/s of the same algorithmic bytes as the GPU line."""
+    import oracle
+    chunk = 4096
+    units = bits.shape[0] // chunk
+
+    def work(i):
+        oracle.fwht128_quant_fp8(bits[i * chunk:(i + 1) * chunk])
+        return chunk * (256 + 128 + 4)
+
+    return cpu_baseline(work, units, budget_s,
+                        "oracle fwht128_quant_fp8 of 4096-row chunks of the 1048576 x 128 bf16 rows")
 
 
 def _time_loop(torch, stream, fn, warmup, steps):
+    """Median of 5 event-timed runs of `steps` calls, after warmup."""
     for i in range(warmup):
         fn(i)
-    ev = Events(torch, stream)
-    return ev.time(fn, steps)
+    return Events(torch, stream).median(fn, steps)[0]
 
 
 def run_other(args, torch, tq, W):
@@ -265,6 +379,8 @@ def run_other(args, torch, tq, W):
         line = dict(workload="write: tq_reshape_and_cache_int4 65536 tokens x 8 heads x 128 bf16, "
                              "5% slots skipped", us=t * 1e6, algorithmic_bytes=nbytes,
                     TBps=nbytes / t / 1e12, pct_peak=100 * nbytes / t / PEAK_HBM)
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline_write(wl, W, args.cpu_budget)
     elif name in ("tq_write_a", "tq_write_b"):
         wl = W.write_workload()
         T, hk, d = wl["key"].shape
@@ -310,6 +426,8 @@ def run_other(args, torch, tq, W):
         line = dict(workload="fwht: fwht128_quant_fp8 1048576 rows x 128 bf16", us=t * 1e6,
                     algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline_fwht(bits, args.cpu_budget)
     elif name == "kpool":
         wl = W.kpool_workload()
         n, P, hd = wl["slot_k"].shape
@@ -500,6 +618,9 @@ def main():
                                        int(w.seq_lens.sum()), w.num_splits),
                        "global_batch": w.B, "seq_len": int(w.seq_lens.max()), "parallelism": "1 GPU"},
             "decode_us": round(res["t_dec"] * 1e6, 2),
+            "decode_us_min_max": [round(res["t_dec_range"][0] * 1e6, 2),
+                                  round(res["t_dec_range"][1] * 1e6, 2)],
+            "timing": "decode_us: median of 5 HIP-event runs of %d back-to-back calls" % max(args.steps, 20),
             "decode_TBps": round(achieved / 1e12, 4),
             "decode_pct_peak": round(100 * achieved / PEAK_HBM, 2),
             "kv_only_TBps": round(b["kv"] / res["t_dec"] / 1e12, 4),
@@ -509,6 +630,7 @@ def main():
                          "traffic": profiled_traffic("decode_int4_" + w.name),
                          "algorithmic_bytes": b},
         }
+        line["copy_calibration_TBps"] = round(copy_calibration(torch, torch.cuda.current_stream()) / 1e12, 4)
         if not args.no_cpu:
             log("[bench] cpu baseline")
             line["cpu_baseline"] = cpu_baseline_int4(res, W, args.cpu_budget)

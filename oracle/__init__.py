@@ -119,7 +119,10 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            _lib = _load(build())
+            # TQ_ORACLE_LIB names another build of this source (the
+            # sanitizer test runs the pins against an ASan/UBSan build)
+            alt = os.environ.get("TQ_ORACLE_LIB")
+            _lib = _load(alt if alt else build())
     return _lib
 
 

@@ -98,3 +98,22 @@ def gpu_tq_decode(w, q, cache, cen, key_fmt, val_fmt, rot_signs=None, norm_corre
         norm_correction=norm_correction)
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(-1, w.d).astype(np.float64), lse.cpu().numpy().ravel()
+
+
+def oracle_rows(fn, n_rows, threads=None):
+    """Run an oracle decode fn(rows) -> (out [R, D], lse [R]) over all rows
+    0..n_rows-1 on a thread pool (the oracle releases the GIL), in chunks;
+    returns the concatenated (out, lse)."""
+    import concurrent.futures as cf
+    import os
+    if threads is None:
+        try:
+            threads = len(os.sched_getaffinity(0))
+        except AttributeError:
+            threads = os.cpu_count() or 1
+        threads = max(1, min(16, threads))
+    rows = np.arange(n_rows, dtype=np.int32)
+    chunks = [c for c in np.array_split(rows, max(1, min(n_rows, 4 * threads))) if c.size]
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        parts = list(pool.map(fn, chunks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])

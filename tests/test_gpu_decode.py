@@ -11,7 +11,8 @@ import oracle
 import quantized_paged_kv_tq_amd as tq
 from quantized_paged_kv_tq_amd import workloads as W
 
-from gpu_cases import assert_close, gpu_int4_decode, gpu_tq_decode, int4_caches, tq_case
+from gpu_cases import (assert_close, gpu_int4_decode, gpu_tq_decode, int4_caches, oracle_rows,
+                       tq_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,21 +136,16 @@ def test_int4_balanced_chunked_range():
     assert np.all(np.isfinite(got))
 
 
-def _sampled_rows(w, n, seed):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(w.B * w.hq, size=min(n, w.B * w.hq), replace=False)).astype(np.int32)
-
-
 @pytest.mark.parametrize("name", ["llama8b_int4", "long_int4"])
-def test_int4_full_size_sampled(name):
+def test_int4_full_size_all_rows(name):
+    """Every (batch, query head) row of the full-size workloads, in the
+    launch configuration the benchmark times, against the fp64 oracle."""
     w = W.decode_workload(name)
     c = int4_caches(w)
     q = W.query(w)
     got, lse = gpu_int4_decode(w, q, c)
-    rows = _sampled_rows(w, 48, 7)
-    ref, ref_lse = _oracle_int4(w, q, c, rows=rows)
-    assert_close(got[rows], ref, lse[rows], ref_lse, name)
-    assert np.all(np.isfinite(got)) and np.all(np.isfinite(lse))
+    ref, ref_lse = oracle_rows(lambda r: _oracle_int4(w, q, c, rows=r), w.B * w.hq)
+    assert_close(got, ref, lse, ref_lse, name)
 
 
 TQ_FORMATS = [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3),
@@ -187,16 +183,18 @@ def test_tq_norm_correction_and_rot_signs(key_fmt):
 @pytest.mark.parametrize("fmt", [(oracle.KEY_FP8, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U3),
                                  (oracle.KEY_FP8, oracle.VAL_FP8)],
                          ids=["A_fp8_u4", "B_mse3_u3", "fp8_fp8"])
-def test_tq_full_size_sampled(fmt):
+def test_tq_full_size_all_rows(fmt):
+    """Every row of the full tq_mixed shape (B = 16, Hq = 32, 16384 tokens,
+    S = 32) against the fp64 oracle."""
     key_fmt, val_fmt = fmt
     w = W.decode_workload("tq_mixed")
     cache, cen = tq_case(w, key_fmt, val_fmt)
     q = W.query(w, bf16_valued=True)
     got, lse = gpu_tq_decode(w, q, cache, cen, key_fmt, val_fmt)
-    rows = _sampled_rows(w, 24, 8)
-    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, key_fmt,
-                                    val_fmt, 0, w.num_splits, w.sm_scale, rows)
-    assert_close(got[rows], ref, lse[rows], ref_lse, "tq_mixed %s" % (fmt,))
+    ref, ref_lse = oracle_rows(
+        lambda r: oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, key_fmt,
+                                   val_fmt, 0, w.num_splits, w.sm_scale, r), w.B * w.hq)
+    assert_close(got, ref, lse, ref_lse, "tq_mixed %s" % (fmt,))
 
 
 def _oracle_tq(w, q, cache, cen, key_fmt, val_fmt, splits=None, rows=None, seq_lens=None):
