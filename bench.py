@@ -210,7 +210,8 @@ def run_int4(args, torch, tq, W, name):
                                          v_scale_cache=vs, rht_signs=signs))
         decodes.append(tq.prepare_decode(q, bt, sl, num_kv_splits=S, key_cache=kc, value_cache=vc,
                                          k_scale_cache=ks, v_scale_cache=vs, rht_signs=signs,
-                                         workspace=ws, out=out, lse=lse)[0])
+                                         workspace=ws, out=out, lse=lse,
+                                         flags=tq.FLAG_WIDE if args.wide else 0)[0])
 
     def decode(i):
         decodes[i % ncopies].run(sp)
@@ -544,7 +545,8 @@ def run_other(args, torch, tq, W):
                          dtype=torch.float32, device=dev)
         calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
                                    key_fmt=fmt[0], val_fmt=fmt[1], centroids=cen,
-                                   workspace=ws)[0] for c in caches]
+                                   workspace=ws, flags=tq.FLAG_WIDE if args.wide else 0)[0]
+                 for c in caches]
         t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
         slot_used = kps + vdb + (0 if fmt[1] == tq.VAL_FP8 else 4)  # padding not counted
         kv = int(w.seq_lens.sum()) * w.hk * slot_used
@@ -580,6 +582,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="override num_kv_splits (sweeps)")
+    ap.add_argument("--wide", action="store_true",
+                    help="decode through the 64-bit addressing variant (the one caches of "
+                         "2 GiB and more take) whatever the cache size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU "
@@ -615,7 +620,8 @@ def main():
                                    "(sum %d) num_kv_splits=%d, INT4 K/V" % (
                                        w.name, w.B, w.hq, w.hk, w.d, w.block_size,
                                        "U[1024,8192]" if w.name == "llama8b_int4" else str(int(w.seq_lens[0])),
-                                       int(w.seq_lens.sum()), w.num_splits),
+                                       int(w.seq_lens.sum()), w.num_splits)
+                                   + (", 64-bit addressing variant" if args.wide else ""),
                        "global_batch": w.B, "seq_len": int(w.seq_lens.max()), "parallelism": "1 GPU"},
             "decode_us": round(res["t_dec"] * 1e6, 2),
             "decode_us_min_max": [round(res["t_dec_range"][0] * 1e6, 2),

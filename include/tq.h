@@ -75,6 +75,9 @@ extern "C" {
 
 /* tq_decode_args.flags */
 #define TQ_FLAG_GENERIC 1u /* force the format-generic vector kernel         */
+#define TQ_FLAG_WIDE 2u    /* force the 64-bit addressing variant of the    */
+                           /* matrix-core kernels (taken by itself for     */
+                           /* caches of 2 GiB and more); for tests          */
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* tq_last_error(void);

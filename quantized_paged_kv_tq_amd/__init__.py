@@ -36,6 +36,7 @@ DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
 KEY_INT4, KEY_FP8, KEY_MSE3, KEY_MSE4 = 0, 1, 2, 3
 VAL_INT4, VAL_U3, VAL_U4, VAL_FP8 = 0, 1, 2, 3
 FLAG_GENERIC = 1
+FLAG_WIDE = 2
 
 
 class TQError(RuntimeError):

@@ -408,6 +408,7 @@ int decode_impl(const tq_decode_args* a, float* ws, int64_t ws_bytes, const char
   p.centroids = a->centroids; p.rot_signs = a->rot_signs;
   p.ws = ws; p.out = a->out; p.lse = a->lse;
   p.nw = 0; p.wgh = 1;
+  p.force_wide = (a->flags & TQ_FLAG_WIDE) ? 1 : 0;
   p.wsp = ws + (int64_t)a->B * a->Hq * a->num_kv_splits * (a->D + 1);
   {
     const int g = a->Hq / a->Hk;

@@ -91,7 +91,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-constexpr uint32_t kMasked = 0x03FFFFFFu;  // row index whose bytes lie past any buffer
+// Narrow addressing (caches below 2 GiB): the tile table holds the byte
+// offset of each token's head-0 key row, (page * bs + offset) * Hk * D/2,
+// and a masked token holds kMaskedByte, past every buffer the kernel reads:
+// the kv head's offset (kvh * D/2 bytes, or 4 * kvh for the scale words,
+// whose offset is the row offset / 16) rides in the loads' scalar offset
+// and still lands beyond the buffer end, so masked rows read 0 without a
+// branch or a select.
+constexpr uint32_t kMaskedByte = 0x80000000u;
 // Headroom of the value-weight fixed point: weights are taken relative to a
 // reference maximum that is raised only when a tile exceeds it by more than
 // 2^kTau, so p = 2^(s - m_ref) <= 2^kTau.
@@ -107,7 +114,14 @@ constexpr int kLastOfSplit = 2;
 // DEPTH = 2 with two waves per SIMD: one wave per SIMD with NH = 2 (all of
 // a kv head's query heads) and rings of 3 or 4 measured slower, the second
 // wave on a SIMD hiding the first one's MFMA, LDS and DPP latencies.
-template <int W, int NH, int DEPTH>
+//
+// WIDE: 64-bit addressing for caches of 2 GiB and more (buffer offsets are
+// 32-bit). The tile table then holds the head-0 row index (page * bs +
+// offset) * Hk, a masked token row 0 (a valid address), and a per-tile mask
+// of live tokens decides what a masked token's bytes may do: its score is
+// -inf (weight 0, so its value nibbles add 0) and its value scale word is
+// taken as 0.
+template <int W, int NH, int DEPTH, bool WIDE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DEPTH == 2 ? 2 : 1)))
 void decode_int4_mfma_kernel(DecodeParams p) {
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
@@ -115,10 +129,12 @@ void decode_int4_mfma_kernel(DecodeParams p) {
   // per wave: MFMA A-operand image of its queries (query set-up), then the
   // per-tile weight digit planes
   __shared__ __attribute__((aligned(16))) uint32_t wbuf[W][NH][2][64][4];
-  // (page * bs + offset) * Hk of each token of the chunk's tiles; the
-  // DEPTH - 1 rows after the chunk's last tile are all masked (the prefetch
-  // past the end)
+  // each token of the chunk's tiles: the byte offset of its head-0 key row
+  // (WIDE: the row index); the DEPTH - 1 rows after the chunk's last tile
+  // are all masked (the prefetch past the end)
   __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + DEPTH - 1][64];
+  // WIDE: live tokens of each tile (bit j: token j)
+  __shared__ uint64_t tlive[WIDE ? kChunk + DEPTH - 1 : 1];
   __shared__ int4 tinfo[kChunk];  // (b, s, flags, -) per tile of the chunk
   __shared__ int scan[W];
   // fp32 accumulators of the wave's heads, lane-major (touched only when
@@ -154,10 +170,18 @@ void decode_int4_mfma_kernel(DecodeParams p) {
   const bool bs_pow2 = (bs & (bs - 1u)) == 0u;
   const int bs_shift = __builtin_ctz(bs);
   const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
-  const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(p.kc, nrows * (uint32_t)(D / 2));
-  const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(p.vc, nrows * (uint32_t)(D / 2));
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ks, nrows * 4u);
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(p.vs, nrows * 4u);
+  const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(p.kc, WIDE ? 0u : nrows * (uint32_t)(D / 2));
+  const __amdgpu_buffer_rsrc_t rv_ = make_rsrc(p.vc, WIDE ? 0u : nrows * (uint32_t)(D / 2));
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(p.ks, WIDE ? 0u : nrows * 4u);
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(p.vs, WIDE ? 0u : nrows * 4u);
+  // the kv head's byte offsets (wave-uniform)
+  const int kvo = __builtin_amdgcn_readfirstlane(kvh * (D / 2));
+  const int kvs = __builtin_amdgcn_readfirstlane(kvh * 4);
+  // WIDE: per-lane 64-bit bases (kv head and lane parts folded in)
+  const uint8_t* kbase = p.kc + (int64_t)kvh * (D / 2) + 16 * lg;
+  const uint8_t* vbase = p.vc + (int64_t)kvh * (D / 2) + 4 * ln;
+  const float* ksbase = p.ks + kvh;
+  const float* vsbase = p.vs + kvh;
 
   // ---- registers of one tile ----
   // key bytes and both scale words of tokens 16s+n; value dword n of tokens
@@ -168,29 +192,49 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     uint32_t live;
     uint32_t vraw[4][4];
   };
-  auto row_of = [&](int k, int j) -> uint32_t {
-    const uint32_t r = tok_rows[k][j];
-    return r == kMasked ? kMasked : r + (uint32_t)kvh;
-  };
   auto issue = [&](Buf& B, int k) {  // k < K + DEPTH - 1: rows from K on are masked
     B.live = 0;
+    if constexpr (!WIDE) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t r = row_of(k, 16 * s + ln);
-      B.live |= (r != kMasked ? 1u : 0u) << s;
-      B.kraw[s] = __builtin_amdgcn_raw_buffer_load_b128(rk_, (int)((r << 6) | (16u * lg)), 0, 0);
-    }
-    {
-      const uint32_t r = row_of(k, lane);
-      B.ksw = __builtin_amdgcn_raw_buffer_load_b32(rks, (int)(r << 2), 0, 0);
-      B.vsw = __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)(r << 2), 0, 0);
-    }
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t o = tok_rows[k][16 * s + ln];
+        B.live |= (o < kMaskedByte ? 1u : 0u) << s;
+        B.kraw[s] = __builtin_amdgcn_raw_buffer_load_b128(rk_, (int)(o | (16u * lg)), kvo, 0);
+      }
+      {
+        const uint32_t o = tok_rows[k][lane] >> 4;  // row * 4
+        B.ksw = __builtin_amdgcn_raw_buffer_load_b32(rks, (int)o, kvs, 0);
+        B.vsw = __builtin_amdgcn_raw_buffer_load_b32(rvs, (int)o, kvs, 0);
+      }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t r = row_of(k, 16 * s + 4 * lg + kk);
-        B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rv_, (int)((r << 6) | (4u * ln)), 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t o = tok_rows[k][16 * s + 4 * lg + kk];
+          B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rv_, (int)(o | (4u * ln)), kvo, 0);
+        }
+      }
+    } else {
+      const uint64_t lv = tlive[k];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint64_t r = tok_rows[k][16 * s + ln];
+        B.live |= (uint32_t)((lv >> (16 * s + ln)) & 1u) << s;
+        B.kraw[s] = *reinterpret_cast<const v4u*>(kbase + r * (D / 2));
+      }
+      {
+        const uint64_t r = tok_rows[k][lane];
+        B.ksw = __float_as_uint(ksbase[r]);
+        // a masked token's value scale word counts as 0 (its row is row 0)
+        B.vsw = ((lv >> lane) & 1u) ? __float_as_uint(vsbase[r]) : 0u;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint64_t r = tok_rows[k][16 * s + 4 * lg + kk];
+          B.vraw[s][kk] = *reinterpret_cast<const uint32_t*>(vbase + r * (D / 2));
+        }
       }
     }
   };
@@ -539,7 +583,8 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     for (int e = tid; e < (K + DEPTH - 1) * 64; e += NT) {
       const int k = e >> 6, j = e & 63;  // k is the same across a wave
       if (k >= K) {
-        tok_rows[k][j] = kMasked;
+        tok_rows[k][j] = WIDE ? 0u : kMaskedByte;
+        if (WIDE && j == 0) tlive[k] = 0;
         continue;
       }
       const int x = c0 + k;
@@ -561,15 +606,23 @@ void decode_int4_mfma_kernel(DecodeParams p) {
       if (end > q.seq) end = q.seq;
       if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
       const int tok = tok0 + j;
-      uint32_t row = kMasked;
+      uint32_t row = WIDE ? 0u : kMaskedByte;
+      bool live = false;
       if (tok < end) {
         const uint32_t t32 = (uint32_t)tok;
         const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
         const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
-        if (page >= 0 && page < p.num_blocks)
-          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
+        if (page >= 0 && page < p.num_blocks) {
+          const uint32_t r = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
+          row = WIDE ? r : r * (uint32_t)(D / 2);
+          live = true;
+        }
       }
       tok_rows[k][j] = row;
+      if constexpr (WIDE) {
+        const uint64_t m = __ballot(live);  // k is the same across the wave
+        if (j == 0) tlive[k] = m;
+      }
       if (j == 0) {
         const int nt = (s == q.n - 1) ? q.TLast : q.TL;
         tinfo[k] = make_int4(b, s, (t == 0 ? kFirstOfSplit : 0) | (t == nt - 1 ? kLastOfSplit : 0), 0);
@@ -592,10 +645,13 @@ void decode_int4_mfma_kernel(DecodeParams p) {
 }
 
 template <int W, int NH, int DEPTH>
-hipError_t launch(const DecodeParams& p, hipStream_t st) {
+hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH>), dim3(blocks), dim3(64 * W), lds, st, p);
+  if (wide)
+    hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+  else
+    hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -603,8 +659,11 @@ hipError_t launch(const DecodeParams& p, hipStream_t st) {
 
 hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
   if (p.d != D || p.key_fmt != KF_INT4 || p.g > 8) return hipErrorNotSupported;
-  // cache bytes are addressed with 32-bit buffer offsets
-  if (p.num_blocks * (int64_t)p.block_size * p.hk * (D / 2) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  // cache bytes below 2 GiB take 32-bit buffer offsets; larger caches the
+  // 64-bit addressing variant, whose tile table holds 32-bit row indices
+  const int64_t rows = p.num_blocks * (int64_t)p.block_size * p.hk;
+  if (rows >= ((int64_t)1 << 32)) return hipErrorNotSupported;
+  const bool wide = p.force_wide || rows * (D / 2) >= ((int64_t)1 << 31);
   // token and tile indices are 32-bit; the per-sequence tile prefix sums
   // live in LDS
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
@@ -617,10 +676,10 @@ hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1, 1, 2>(p, st);
-    case 2: return launch<2, 1, 2>(p, st);
-    case 4: return launch<4, 1, 2>(p, st);
-    default: return launch<8, 1, 2>(p, st);
+    case 1: return launch<1, 1, 2>(p, st, wide);
+    case 2: return launch<2, 1, 2>(p, st, wide);
+    case 4: return launch<4, 1, 2>(p, st, wide);
+    default: return launch<8, 1, 2>(p, st, wide);
   }
 }
 

@@ -25,6 +25,8 @@
 // per kv head instead of by two waves, and each wave's loads are its own
 // (two waves of a kv head fetched the same lines). That wave needs more
 // than 256 registers and runs alone on its SIMD.
+#include <type_traits>
+
 #include "balance.h"
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -35,6 +37,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
@@ -48,6 +51,14 @@ constexpr int kTau = 4;     // headroom of the value-weight fixed point
 // buffer (cache sizes stay below 2^31 bytes), so its loads read zeros even
 // after a kv head's offset and a field offset are added.
 constexpr uint32_t kMaskedByte = 0x80000000u;
+// Caches of 2 GiB and more take the 64-bit addressing variant (WIDE): the
+// tile table holds 64-bit byte offsets from the wave's kv-head base, and a
+// masked token the offset of a static page of zeros (never written), so a
+// masked token reads zeros there as the narrow variant reads zeros past the
+// buffer end. The zero page covers every kv head's slot (Hk * slot bytes up
+// to kZeroBytes).
+constexpr int kZeroBytes = 65536;
+__device__ __attribute__((aligned(256))) uint8_t g_zero_page[kZeroBytes];
 constexpr int kFirstOfSplit = 1;
 constexpr int kLastOfSplit = 2;
 
@@ -94,7 +105,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // head h) and B = 32 tokens x 16 value dims, dims 8n + i for MFMA i (lane n
 // loads value bytes 8n .. 8n + 7 of its tokens, and a 4x4 byte transpose
 // gives byte i of 4 tokens per register).
-template <int W, int NH, bool VF8>
+template <int W, int NH, bool VF8, bool WIDE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_tq_fp8_kernel(DecodeParams p) {
   constexpr int NT = 64 * W;
@@ -104,7 +115,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t pbf[VF8 ? W : 1][NH][3][4][64];
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
-  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
+  using Off = typename std::conditional<WIDE, int64_t, uint32_t>::type;
+  __shared__ __attribute__((aligned(16))) Off tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
   __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
@@ -137,7 +149,27 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   const int bs_shift = __builtin_ctz(bs);
   const uint32_t sb = (uint32_t)p.slot_bytes;
   const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, nrows * sb);
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, WIDE ? 0u : nrows * sb);
+  // WIDE: the wave's kv-head base and the offset of the zero page from it
+  const uint8_t* kvb = p.kv + (int64_t)kvh * sb;
+  const int64_t zoff = (int64_t)(g_zero_page - p.kv);
+  auto ld32 = [&](Off o) -> uint32_t {
+    if constexpr (WIDE) return *reinterpret_cast<const uint32_t*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)o, 0, 0);
+  };
+  auto ld64 = [&](Off o) -> v2u {
+    if constexpr (WIDE) return *reinterpret_cast<const v2u*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b64(rkv, (int)o, 0, 0);
+  };
+  auto ld128 = [&](Off o) -> v4u {
+    if constexpr (WIDE) return *reinterpret_cast<const v4u*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)o, 0, 0);
+  };
+  // a token's slot is masked (it reads zeros)
+  auto masked = [&](Off o) -> bool {
+    if constexpr (WIDE) return o == (Off)zoff;
+    else return o >= kMaskedByte;
+  };
   const uint32_t voff = (uint32_t)p.kps;            // value indices
   const uint32_t soff = (uint32_t)(p.kps + p.vdb);  // fp16 scale, fp16 zero
 
@@ -151,34 +183,34 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     uint32_t v8[2][8][2];  // VF8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
-  auto slot_of = [&](int k, int j) -> uint32_t { return tok_rows[k][j] + kvh_off; };
+  auto slot_of = [&](int k, int j) -> Off { return WIDE ? tok_rows[k][j] : tok_rows[k][j] + kvh_off; };
   auto issue = [&](Buf& B, int k) {
     B.live = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t o = slot_of(k, 16 * s + ln);
-      B.live |= (o < kMaskedByte ? 1u : 0u) << s;
-      B.kraw[s][0] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg), 0, 0);
-      B.kraw[s][1] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)(o + 32u * lg + 16u), 0, 0);
+      const Off o = slot_of(k, 16 * s + ln);
+      B.live |= (masked(o) ? 0u : 1u) << s;
+      B.kraw[s][0] = ld128(o + 32u * lg);
+      B.kraw[s][1] = ld128(o + 32u * lg + 16u);
     }
     if constexpr (VF8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t o = slot_of(k, 32 * h + 8 * lg + j);
-          B.v8[h][j][0] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 8u * ln), 0, 0);
-          B.v8[h][j][1] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 8u * ln + 4u), 0, 0);
+          const Off o = slot_of(k, 32 * h + 8 * lg + j);
+          B.v8[h][j][0] = ld32(o + voff + 8u * ln);
+          B.v8[h][j][1] = ld32(o + voff + 8u * ln + 4u);
         }
       }
     } else {
-      B.sz = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(slot_of(k, lane) + soff), 0, 0);
+      B.sz = ld32(slot_of(k, lane) + soff);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
-          B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + voff + 4u * ln), 0, 0);
+          const Off o = slot_of(k, 16 * s + 4 * lg + kk);
+          B.vraw[s][kk] = ld32(o + voff + 4u * ln);
         }
       }
     }
@@ -555,7 +587,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     for (int e = tid; e < (K + 1) * 64; e += NT) {
       const int k = e >> 6, j = e & 63;
       if (k == K) {
-        tok_rows[k][j] = kMaskedByte;
+        tok_rows[k][j] = WIDE ? (Off)zoff : (Off)kMaskedByte;
         continue;
       }
       const int x = c0 + k;
@@ -576,13 +608,17 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       if (end > q.seq) end = q.seq;
       if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
       const int tok = tok0 + j;
-      uint32_t row = kMaskedByte;
+      Off row = WIDE ? (Off)zoff : (Off)kMaskedByte;
       if (tok < end) {
         const uint32_t t32 = (uint32_t)tok;
         const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
         const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
-        if (page >= 0 && page < p.num_blocks)
-          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk * sb;
+        if (page >= 0 && page < p.num_blocks) {
+          if constexpr (WIDE)
+            row = ((int64_t)page * bs + (t32 - pi * bs)) * p.hk * (int64_t)sb;
+          else
+            row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk * sb;
+        }
       }
       tok_rows[k][j] = row;
       if (j == 0) {
@@ -606,13 +642,20 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 }
 
 template <int W, int NH>
-hipError_t launch(const DecodeParams& p, hipStream_t st) {
+hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  if (p.val_fmt == VF_FP8)
-    hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
-  else
-    hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+  if (p.val_fmt == VF_FP8) {
+    if (wide)
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+    else
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+    else
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+  }
   return hipGetLastError();
 }
 
@@ -625,9 +668,11 @@ constexpr bool kOneWavePerKvHead = true;
 hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
   if (p.d != D || p.key_fmt != KF_FP8 || (p.val_fmt != VF_U4 && p.val_fmt != VF_FP8) || p.g > 8)
     return hipErrorNotSupported;
-  // slot bytes are addressed with 32-bit buffer offsets (masked: 0xFFFFFF00)
-  if (p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31))
-    return hipErrorNotSupported;
+  // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
+  // 64-bit variant (whose zero page must cover every kv head's slot)
+  const bool wide = p.force_wide ||
+      p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31);
+  if (wide && (int64_t)p.hk * p.slot_bytes > kZeroBytes) return hipErrorNotSupported;
   if ((p.kps + p.vdb) % 4 != 0 || p.kps % 4 != 0 || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
@@ -641,9 +686,9 @@ hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
     const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
     p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
     switch (p.wgh) {
-      case 1: return launch<1, 2>(p, st);
-      case 2: return launch<2, 2>(p, st);
-      default: return launch<4, 2>(p, st);
+      case 1: return launch<1, 2>(p, st, wide);
+      case 2: return launch<2, 2>(p, st, wide);
+      default: return launch<4, 2>(p, st, wide);
     }
   }
   const int qs = (p.g + 3) / 4;
@@ -651,10 +696,10 @@ hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1, 1>(p, st);
-    case 2: return launch<2, 1>(p, st);
-    case 4: return launch<4, 1>(p, st);
-    default: return launch<8, 1>(p, st);
+    case 1: return launch<1, 1>(p, st, wide);
+    case 2: return launch<2, 1>(p, st, wide);
+    case 4: return launch<4, 1>(p, st, wide);
+    default: return launch<8, 1>(p, st, wide);
   }
 }
 

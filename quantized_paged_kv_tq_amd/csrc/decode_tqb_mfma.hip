@@ -44,6 +44,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -54,6 +55,14 @@ constexpr int kTau = 4;     // headroom of the value-weight fixed point
 // buffer (cache sizes stay below 2^31 bytes), so its loads read zeros even
 // after a kv head's offset and a field offset are added.
 constexpr uint32_t kMaskedByte = 0x80000000u;
+// Caches of 2 GiB and more take the 64-bit addressing variant (WIDE): the
+// tile table holds 64-bit byte offsets from the wave's kv-head base, and a
+// masked token the offset of a static page of zeros (never written), so a
+// masked token reads zeros there as the narrow variant reads zeros past the
+// buffer end. The zero page covers every kv head's slot (Hk * slot bytes up
+// to kZeroBytes).
+constexpr int kZeroBytes = 65536;
+__device__ __attribute__((aligned(256))) uint8_t g_zero_page[kZeroBytes];
 constexpr int kFirstOfSplit = 1;
 constexpr int kLastOfSplit = 2;
 // slot offsets
@@ -101,7 +110,7 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
 // operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH>
+template <int W, int NH, bool WIDE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
   constexpr int NT = 64 * W;
@@ -110,7 +119,8 @@ void decode_tqb_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2][64][4];  // query digit image
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
-  __shared__ __attribute__((aligned(16))) uint32_t tok_rows[kChunk + 1][64];
+  using Off = typename std::conditional<WIDE, int64_t, uint32_t>::type;
+  __shared__ __attribute__((aligned(16))) Off tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
   __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
@@ -173,7 +183,27 @@ void decode_tqb_kernel(DecodeParams p) {
   const int bs_shift = __builtin_ctz(bs);
   const uint32_t sb = (uint32_t)p.slot_bytes;
   const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, nrows * sb);
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(p.kv, WIDE ? 0u : nrows * sb);
+  // WIDE: the wave's kv-head base and the offset of the zero page from it
+  const uint8_t* kvb = p.kv + (int64_t)kvh * sb;
+  const int64_t zoff = (int64_t)(g_zero_page - p.kv);
+  auto ld32 = [&](Off o) -> uint32_t {
+    if constexpr (WIDE) return *reinterpret_cast<const uint32_t*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)o, 0, 0);
+  };
+  auto ld64 = [&](Off o) -> v2u {
+    if constexpr (WIDE) return *reinterpret_cast<const v2u*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b64(rkv, (int)o, 0, 0);
+  };
+  auto ld128 = [&](Off o) -> v4u {
+    if constexpr (WIDE) return *reinterpret_cast<const v4u*>(kvb + o);
+    else return __builtin_amdgcn_raw_buffer_load_b128(rkv, (int)o, 0, 0);
+  };
+  // a token's slot is masked (it reads zeros)
+  auto masked = [&](Off o) -> bool {
+    if constexpr (WIDE) return o == (Off)zoff;
+    else return o >= kMaskedByte;
+  };
   // this lane's 3 value bytes (dims 8n .. 8n+7) start at byte kValOff + 3n;
   // one dword load from that byte offset (buffer loads take byte offsets,
   // dword loads need not be 4-byte aligned)
@@ -189,7 +219,7 @@ void decode_tqb_kernel(DecodeParams p) {
     uint32_t vraw[4][4];
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
-  auto slot_of = [&](int k, int j) -> uint32_t { return tok_rows[k][j] + kvh_off; };
+  auto slot_of = [&](int k, int j) -> Off { return WIDE ? tok_rows[k][j] : tok_rows[k][j] + kvh_off; };
   // keys and per-token words first; the value windows after the current
   // tile's scores (issue_v), which keeps both tiles' values from being live
   // through the score computation
@@ -198,8 +228,8 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t o = slot_of(k, 16 * s + 4 * lg + kk);
-        B.vraw[s][kk] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + vbyte), 0, 0);
+        const Off o = slot_of(k, 16 * s + 4 * lg + kk);
+        B.vraw[s][kk] = ld32(o + vbyte);
       }
     }
   };
@@ -207,16 +237,16 @@ void decode_tqb_kernel(DecodeParams p) {
     B.live = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t o = slot_of(k, 16 * s + ln);
-      B.live |= (o < kMaskedByte ? 1u : 0u) << s;
+      const Off o = slot_of(k, 16 * s + ln);
+      B.live |= (masked(o) ? 0u : 1u) << s;
 #pragma unroll
       for (int i = 0; i < 3; ++i)
-        B.kraw[s][i] = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + 12u * lg + 4u * i), 0, 0);
+        B.kraw[s][i] = ld32(o + 12u * lg + 4u * i);
     }
     {
-      const uint32_t o = slot_of(k, lane);
-      B.nw = __builtin_amdgcn_raw_buffer_load_b32(rkv, (int)(o + kNormOff), 0, 0);
-      const v2u w = __builtin_amdgcn_raw_buffer_load_b64(rkv, (int)(o + kScaleOff), 0, 0);
+      const Off o = slot_of(k, lane);
+      B.nw = ld32(o + kNormOff);
+      const v2u w = ld64(o + kScaleOff);
       B.sz0 = w.x;
       B.sz1 = w.y;
     }
@@ -602,7 +632,7 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int e = tid; e < (K + 1) * 64; e += NT) {
       const int k = e >> 6, j = e & 63;
       if (k == K) {
-        tok_rows[k][j] = kMaskedByte;
+        tok_rows[k][j] = WIDE ? (Off)zoff : (Off)kMaskedByte;
         continue;
       }
       const int x = c0 + k;
@@ -623,13 +653,17 @@ void decode_tqb_kernel(DecodeParams p) {
       if (end > q.seq) end = q.seq;
       if (end > tok0 + kTileTokens) end = tok0 + kTileTokens;
       const int tok = tok0 + j;
-      uint32_t row = kMaskedByte;
+      Off row = WIDE ? (Off)zoff : (Off)kMaskedByte;
       if (tok < end) {
         const uint32_t t32 = (uint32_t)tok;
         const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
         const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
-        if (page >= 0 && page < p.num_blocks)
-          row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk * sb;
+        if (page >= 0 && page < p.num_blocks) {
+          if constexpr (WIDE)
+            row = ((int64_t)page * bs + (t32 - pi * bs)) * p.hk * (int64_t)sb;
+          else
+            row = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk * sb;
+        }
       }
       tok_rows[k][j] = row;
       if (j == 0) {
@@ -654,10 +688,13 @@ void decode_tqb_kernel(DecodeParams p) {
 }
 
 template <int W, int NH>
-hipError_t launch(const DecodeParams& p, hipStream_t st) {
+hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  hipLaunchKernelGGL((decode_tqb_kernel<W, NH>), dim3(blocks), dim3(64 * W), lds, st, p);
+  if (wide)
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+  else
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -671,9 +708,11 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   if (p.d != D || p.key_fmt != KF_MSE3 || p.val_fmt != VF_U3 || p.g > 8 || p.norm_correction)
     return hipErrorNotSupported;
   if (p.kps != (int)kValOff || p.vdb != 48 || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
-  // slot bytes are addressed with 32-bit buffer offsets (masked: 0xFFFFFF00)
-  if (p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31))
-    return hipErrorNotSupported;
+  // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
+  // 64-bit variant (whose zero page must cover every kv head's slot)
+  const bool wide = p.force_wide ||
+      p.num_blocks * (int64_t)p.block_size * p.hk * p.slot_bytes >= ((int64_t)1 << 31);
+  if (wide && (int64_t)p.hk * p.slot_bytes > kZeroBytes) return hipErrorNotSupported;
   const int64_t cap = (int64_t)p.max_blocks * p.block_size;
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
   const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
@@ -686,9 +725,9 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
     const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
     p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
     switch (p.wgh) {
-      case 1: return launch<1, 2>(p, st);
-      case 2: return launch<2, 2>(p, st);
-      default: return launch<4, 2>(p, st);
+      case 1: return launch<1, 2>(p, st, wide);
+      case 2: return launch<2, 2>(p, st, wide);
+      default: return launch<4, 2>(p, st, wide);
     }
   }
   const int qs = (p.g + 3) / 4;
@@ -696,10 +735,10 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   const int64_t nw = balance_max_wgs(p.hk, p.g);
   p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
   switch (p.wgh * qs) {
-    case 1: return launch<1, 1>(p, st);
-    case 2: return launch<2, 1>(p, st);
-    case 4: return launch<4, 1>(p, st);
-    default: return launch<8, 1>(p, st);
+    case 1: return launch<1, 1>(p, st, wide);
+    case 2: return launch<2, 1>(p, st, wide);
+    case 4: return launch<4, 1>(p, st, wide);
+    default: return launch<8, 1>(p, st, wide);
   }
 }
 

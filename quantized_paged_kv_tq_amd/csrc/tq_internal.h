@@ -70,6 +70,7 @@ struct DecodeParams {
   // Balanced partition of the INT4 decode (balance.h), set by its launcher:
   // nw workgroups per group of wgh kv heads; 0 = one partial per split only.
   int nw, wgh;
+  int force_wide;  // take the 64-bit addressing variant whatever the cache size
   float* wsp;    // piece slots [Hk / wgh][nw][2][wgh * g][D+1], after ws
   int* wsx;      // [B + 1] tile-list prefix sums (stage 1 writes, stage 2 reads)
 };

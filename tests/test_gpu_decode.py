@@ -48,7 +48,8 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
 def test_int4_shapes(shape, flags):
     B, hq, hk, d, bs, seq, S = shape
@@ -88,7 +89,7 @@ def test_int4_random_cache_bytes():
     c = dict(kc=kc, vc=vc, ks=ks, vs=vs, signs=W.rht_signs(128))
     q = W.query(w)
     ref, ref_lse = _oracle_int4(w, q, c)
-    for flags in (0, tq.FLAG_GENERIC):
+    for flags in (0, tq.FLAG_GENERIC, tq.FLAG_WIDE):
         got, lse = gpu_int4_decode(w, q, c, flags=flags)
         assert_close(got, ref, lse, ref_lse, "random bytes")
 
@@ -206,7 +207,8 @@ def _oracle_tq(w, q, cache, cen, key_fmt, val_fmt, splits=None, rows=None, seq_l
 A_FMT = (oracle.KEY_FP8, oracle.VAL_U4)
 
 
-@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
 def test_tq_fp8_u4_shapes(shape, flags):
     """FP8 keys / 4-bit values on the matrix-core kernel (D = 128, up to
@@ -240,7 +242,7 @@ def test_tq_fp8_u4_random_slot_bytes():
     cache = W.random_tq_fp8_u4_cache(w, oracle.tq_slot_bytes(128, *A_FMT))
     q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
     ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
-    for flags in (0, tq.FLAG_GENERIC):
+    for flags in (0, tq.FLAG_GENERIC, tq.FLAG_WIDE):
         got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT, flags=flags)
         assert_close(got, ref, lse, ref_lse, "random slots flags=%d" % flags)
 
@@ -274,7 +276,8 @@ def test_tq_fp8_u4_balanced_few_tiles(seq, S):
 B_FMT = (oracle.KEY_MSE3, oracle.VAL_U3)
 
 
-@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
 def test_tq_mse3_u3_shapes(shape, flags):
     B, hq, hk, d, bs, seq, S = shape
@@ -321,7 +324,7 @@ def test_tq_mse3_u3_random_slot_bytes_and_table(antisymmetric):
     assert np.array_equal(cen[::-1] == -cen, np.full(8, antisymmetric))
     q = W.query(w) / 4
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
-    for flags in (0, tq.FLAG_GENERIC):
+    for flags in (0, tq.FLAG_GENERIC, tq.FLAG_WIDE):
         got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT, flags=flags)
         assert_close(got, ref, lse, ref_lse, "random slots flags=%d" % flags)
 
@@ -361,8 +364,9 @@ def test_tq_mse3_u3_query_groups_of_five_to_eight(hq, hk, antisymmetric):
     cen = _random_centroids(350 + hq, antisymmetric)
     q = W.query(w) / 4
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *B_FMT)
-    got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT)
-    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+    for flags in (0, tq.FLAG_WIDE):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *B_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
 
 
 @pytest.mark.parametrize("hq,hk", [(10, 2), (12, 2), (14, 2), (16, 2), (32, 4)],
@@ -375,8 +379,9 @@ def test_tq_fp8_u4_query_groups_of_five_to_eight(hq, hk):
     cache = W.random_tq_fp8_u4_cache(w, oracle.tq_slot_bytes(128, *A_FMT))
     q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
     ref, ref_lse = _oracle_tq(w, q, cache, None, *A_FMT)
-    got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT)
-    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+    for flags in (0, tq.FLAG_WIDE):
+        got, lse = gpu_tq_decode(w, q, cache, None, *A_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
 
 
 
@@ -425,7 +430,8 @@ def test_tq_head_dim_256_shapes(fmt, norm_correction):
 F8_FMT = (oracle.KEY_FP8, oracle.VAL_FP8)
 
 
-@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC])
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
 def test_tq_fp8_fp8_shapes(shape, flags):
     """FP8 keys and FP8 values on the matrix-core kernel (values as exact
@@ -449,8 +455,9 @@ def test_tq_fp8_fp8_query_groups(hq, hk):
     cache, cen = tq_case(w, *F8_FMT)
     q = W.query(w, bf16_valued=True)
     ref, ref_lse = _oracle_tq(w, q, cache, cen, *F8_FMT)
-    got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT)
-    assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+    for flags in (0, tq.FLAG_WIDE):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *F8_FMT, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
 
 
 def test_tq_fp8_fp8_split_invariance_and_degenerate_lengths():
@@ -477,6 +484,6 @@ def test_tq_fp8_fp8_random_slot_bytes_wide_scores(hq, hk):
     cache[..., 128:256] &= 0xBF
     q = W.query(w) / 8
     ref, ref_lse = _oracle_tq(w, q, cache, None, *F8_FMT)
-    for flags in (0, tq.FLAG_GENERIC):
+    for flags in (0, tq.FLAG_GENERIC, tq.FLAG_WIDE):
         got, lse = gpu_tq_decode(w, q, cache, None, *F8_FMT, flags=flags)
         assert_close(got, ref, lse, ref_lse, "wide scores flags=%d" % flags)
