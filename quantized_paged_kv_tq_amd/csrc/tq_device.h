@@ -20,6 +20,22 @@ __device__ __forceinline__ float round_to_bf16(float x) {
 
 // IEEE binary16 <-> fp32 through the hardware converts (round to nearest
 // even, fp16 denormals kept: the gfx9 default mode).
+// Float -> u32 with the hardware convert, which truncates and saturates:
+// every negative argument gives 0 (a C++ cast of a negative float would be
+// undefined).
+__device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// (v << s) | w as one v_lshl_or_b32 (a chain of these packs nibbles with
+// one instruction each; left to itself the compiler regroups such a chain
+// into separate shifts and three-input ORs).
+__device__ __forceinline__ uint32_t lshl_or(uint32_t v, int s, uint32_t w) {
+  uint32_t r;
+  asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "i"(s), "v"(w));
+  return r;
+}
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
 }

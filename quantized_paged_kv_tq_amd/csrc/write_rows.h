@@ -69,18 +69,13 @@ __device__ __forceinline__ void fwht_row(float x[16], const float sg[4]) {
 }
 
 // ---------------------------------------------------------------------------
-// Pair layout: a row of D elements over two adjacent lanes. Lane q = lane & 1
-// holds the 8-element chunks c = 2m + q (m = 0 .. D/16 - 1) as
-// x[8m + j] = element 8c + j, so element e = 16m + 8q + j: FWHT strides 1, 2,
-// 4 pair elements inside a chunk, stride 8 pairs the two lanes, and strides
-// 16 .. D/2 pair chunks m and m ^ (stride / 16) inside the lane. The two
-// lanes of a row read its 32-byte spans together (bf16), and a row costs one
-// lane exchange per element instead of three.
+// Two lanes per row (quarter layout, write_int4.hip): the cross-lane
+// butterfly is a DPP fused multiply-add with the partner lane.
 
 // x[i] += (x[i] of lane ^ 1) * s for eight values: one v_fmac_f32 with a DPP
-// operand each. With s = +1 in lane 0 and -1 in lane 1 this is the stride-8
-// butterfly, except that lane 1 receives the negated difference x1 - x0
-// (exact: sign flips commute with rounding). Every lane of the wave must be
+// operand each. With s = +1 in lane 0 and -1 in lane 1 this is the
+// cross-lane butterfly, except that lane 1 receives the negated difference
+// x1 - x0 (exact: sign flips commute with rounding). Every lane of the wave must be
 // active. The s_nop covers the wait states a DPP read needs after a VALU
 // write of its operand or of EXEC.
 __device__ __forceinline__ void fmac_partner8(float* x, float s) {
@@ -97,20 +92,23 @@ __device__ __forceinline__ void fmac_partner8(float* x, float s) {
       : "v"(s));
 }
 
-// In-place butterfly (a, b) -> (a + b, a - b).
+// In-place butterfly (a, b) -> (a + b, a - b), the two instructions kept
+// together so that a butterfly holds one extra register while it runs (the
+// scheduler would otherwise issue many sums ahead of their differences and
+// hold all the pairs live).
 __device__ __forceinline__ void bfly(float& a, float& b) {
-  const float u = a + b, v = a - b;
+  float u;
+  asm("v_add_f32 %0, %2, %3\n\tv_sub_f32 %1, %2, %3" : "=&v"(u), "=v"(b) : "v"(a), "v"(b));
   a = u;
-  b = v;
 }
 
-// FWHT over the pair layout from the state after stride 1 (the writers fuse
-// that stage with unpacking). On return lane 0 holds FWHT(row) at its
-// elements and lane 1 holds -FWHT(row) at its elements (sigma = +1 / -1),
-// except for the sign of exact zeros: a zero difference is +0 whichever way
-// round it is taken, so a consumer must not depend on the sign of a zero.
+// FWHT over the quarter layout (lane q holds chunks (m mod M/2) + q M/2 +
+// M (m div M/2), M = D/16) from the state after stride 1: strides 2, 4 in
+// a chunk, 8 .. D/8 across lane-local chunks m ^ 1 .., D/4 across the lane
+// pair (DPP, leaving lane 1 negated), D/2 across m ^ M/2 in the lane (on
+// lane 1's negated values, which stays exact).
 template <int D>
-__device__ __forceinline__ void fwht_pair_from_stride2(float (&x)[D / 2], int q) {
+__device__ __forceinline__ void fwht_quarters_from_stride2(float (&x)[D / 2], int q) {
   constexpr int M = D / 16;
 #pragma unroll
   for (int h = 2; h < 8; h <<= 1)
@@ -119,27 +117,31 @@ __device__ __forceinline__ void fwht_pair_from_stride2(float (&x)[D / 2], int q)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if ((j & h) == 0) bfly(x[8 * m + j], x[8 * m + j + h]);
-  const float s = q ? -1.0f : 1.0f;
 #pragma unroll
-  for (int m = 0; m < M; ++m) fmac_partner8(x + 8 * m, s);
-#pragma unroll
-  for (int hm = 1; hm < M; hm <<= 1)
+  for (int hm = 1; hm < M / 2; hm <<= 1)
 #pragma unroll
     for (int m = 0; m < M; ++m)
       if ((m & hm) == 0)
 #pragma unroll
         for (int j = 0; j < 8; ++j) bfly(x[8 * m + j], x[8 * (m + hm) + j]);
+  const float s = q ? -1.0f : 1.0f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) fmac_partner8(x + 8 * m, s);
+#pragma unroll
+  for (int m = 0; m < M / 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bfly(x[8 * m + j], x[8 * (m + M / 2) + j]);
 }
 
-// Round a pair of fp32 values to bfloat16 (nearest even) and back, with one
-// packed convert.
-__device__ __forceinline__ void round2_bf16(float& a, float& b) {
+// Round one fp32 value to bfloat16 (nearest even) and back with a single
+// packed convert whose other half is the constant 0: the converted value
+// lands in the upper 16 bits over a zero lower half, which is its fp32
+// encoding.
+__device__ __forceinline__ float round1_bf16(float a) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = {a, b};
-  const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  a = u2f(u << 16);
-  b = u2f(u & 0xFFFF0000u);
+  const f32x2 v = {0.0f, a};
+  return u2f(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2)));
 }
 
 }  // namespace tqk

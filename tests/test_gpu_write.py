@@ -59,6 +59,19 @@ def test_write_scaled_and_outlier_rows():
     k[2] *= 1e-6
     k[3] *= 1e4
     k[4, :, 7] = 500.0
+    # rows whose rotated values are one-signed (every code above 15 before
+    # the clamp, or below 0): the source is the inverse rotation of a
+    # chosen row, x = signs * H y / d (H the Sylvester Hadamard matrix)
+    sg = W.rht_signs(d).astype(np.float64)
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    for r, y in ((5, 5.0 + 0.1 * rng.standard_normal(d)),
+                 (6, -5.0 + 0.1 * rng.standard_normal(d)),
+                 (7, np.full(d, 2.5)),
+                 (8, 1e3 + rng.standard_normal(d)),
+                 (9, np.where(np.arange(d) % 3 == 0, 7.0, 0.0) + 0.01 * rng.standard_normal(d))):
+        k[r] = (sg * (h @ y) / d).astype(np.float32)
     v = np.flip(k, 0).copy()
     slots = np.arange(T, dtype=np.int64)[::-1].copy()
     for dtype in ("bf16", "f16", "f32"):
