@@ -342,11 +342,23 @@ def cpu_baseline_fwht(bits, budget_s):
                         "oracle fwht128_quant_fp8 of 4096-row chunks of the 1048576 x 128 bf16 rows")
 
 
+# Secondary workloads time at least this many back-to-back calls per run: a
+# run of a few milliseconds still sees the GPU's clocks ramping up after an
+# idle spell (tens of milliseconds of load), which inflates per-call times
+# by several percent.
+MIN_TIMED_CALLS = 400
+
+
+def _timed_calls(steps):
+    return max(steps, MIN_TIMED_CALLS)
+
+
 def _time_loop(torch, stream, fn, warmup, steps):
-    """Median of 5 event-timed runs of `steps` calls, after warmup."""
+    """Median of 5 event-timed runs of max(steps, MIN_TIMED_CALLS) calls,
+    after warmup."""
     for i in range(warmup):
         fn(i)
-    return Events(torch, stream).median(fn, steps)[0]
+    return Events(torch, stream).median(fn, _timed_calls(steps))[0]
 
 
 def run_other(args, torch, tq, W):
@@ -558,7 +570,8 @@ def run_other(args, torch, tq, W):
                     pct_peak=100 * nbytes / t / PEAK_HBM)
     else:
         raise SystemExit("unknown workload %s" % name)
-    line.update(steps=args.steps, warmup=args.warmup)
+    line.update(steps=args.steps, warmup=args.warmup,
+                timing="us: median of 5 HIP-event runs of %d back-to-back calls" % _timed_calls(args.steps))
     print(json.dumps(line), flush=True)
 
 
