@@ -484,12 +484,24 @@ def run_other(args, torch, tq, W):
             k_scale_cache=ks, v_scale_cache=vs,
             rht_signs=torch.from_numpy(W.rht_signs(w.d)).to(dev), sm_scale=w.sm_scale)
         t = _time_loop(torch, stream, lambda i: call.run(sp), args.warmup, args.steps)
+        # the vector-ALU kernel (the path without a workspace), fewer calls
+        vcall, _ = tq.prepare_prefill(
+            torch.from_numpy(q).to(dev), kc, vc, torch.from_numpy(w.block_table).to(dev),
+            torch.from_numpy(cu).to(dev), torch.from_numpy(w.seq_lens).to(dev),
+            k_scale_cache=ks, v_scale_cache=vs,
+            rht_signs=torch.from_numpy(W.rht_signs(w.d)).to(dev), sm_scale=w.sm_scale,
+            workspace=None)
+        for i in range(2):
+            vcall.run(sp)
+        tv = Events(torch, stream).median(lambda i: vcall.run(sp), 20)[0]
         pairs = int(sum(int(c) * int(n) + int(n) * (int(n) + 1) // 2 for c, n in zip(ctx, ql)))
         flops = 4 * pairs * w.hq * w.d
         line = dict(workload="prefill_int4: tq_prefill_attention_int4, 4 sequences x (1024 "
-                             "context + 1024 query tokens), Hq=32 Hk=8 D=128 bs=16, INT4 K/V",
+                             "context + 1024 query tokens), Hq=32 Hk=8 D=128 bs=16, INT4 K/V, "
+                             "matrix-core path (query tokens as decode entries)",
                     us=t * 1e6, query_tokens_per_s=float(ql.sum()) / t,
-                    visible_pairs=pairs, attention_TFLOPs=flops / t / 1e12)
+                    visible_pairs=pairs, attention_TFLOPs=flops / t / 1e12,
+                    vector_path_us=tv * 1e6, vector_path_TFLOPs=flops / tv / 1e12)
     elif name == "tq_dequant":
         # bulk dequant of the tq_mixed cache (B=16 Hk=4 D=128, 16384 tokens each,
         # FP8 keys + 4-bit values, 208-B slots) to fp16 K/V

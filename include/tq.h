@@ -328,6 +328,19 @@ int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
  *                 output_scale is set
  * D = 64 or 128 (TQ_ENOTSUP otherwise). num_tokens == 0 returns TQ_OK
  * without launching.
+ *
+ * Paths. With a workspace of at least tq_prefill_workspace_bytes(...) bytes
+ * (16-byte aligned, as are query, f32 out and both caches), D = 128 and
+ * Hq / Hk <= 8, the
+ * call runs on the matrix cores: each query token becomes one entry of the
+ * split-KV INT4 decode (its visible keys [t0, t1) read from its sequence's
+ * block-table row), in chunks of at most 4096 tokens that reuse the
+ * workspace in stream order. Otherwise (no workspace, or a shape the
+ * matrix-core decode does not take) a vector-ALU kernel computes the same
+ * result. The workspace is scratch owned by the caller; calls that share
+ * one must not overlap. Callers built against the layout without the
+ * workspace fields pass struct_size = offsetof(tq_prefill_args, workspace)
+ * and get the vector path.
  */
 typedef struct {
   uint32_t struct_size; /* sizeof(tq_prefill_args) */
@@ -348,9 +361,20 @@ typedef struct {
   const float* sinks;
   const float* output_scale;
   void* out;
+  void* workspace;          /* device scratch, or NULL (vector path) */
+  int64_t workspace_bytes;
 } tq_prefill_args;
 
 int tq_prefill_attention_int4(const tq_prefill_args* args, void* stream);
+
+/*
+ * Workspace bytes that put tq_prefill_attention_int4 on the matrix cores
+ * for num_tokens query tokens (0 when that path does not apply: D != 128,
+ * Hq / Hk > 8, or no tokens): three int32 per token of a chunk of up to 4096
+ * tokens, then the split-KV decode workspace of one chunk
+ * (tq_decode_workspace_bytes with one split).
+ */
+size_t tq_prefill_workspace_bytes(int64_t num_tokens, int32_t Hq, int32_t Hk, int32_t D);
 
 /*
  * Bulk dequantization of the TurboQuant combined-slot cache to fp16 rows

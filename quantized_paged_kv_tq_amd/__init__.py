@@ -55,6 +55,7 @@ class PrefillArgs(C.Structure):
         ("block_table", C.c_void_p), ("key_cache", C.c_void_p), ("value_cache", C.c_void_p),
         ("k_scale_cache", C.c_void_p), ("v_scale_cache", C.c_void_p), ("rht_signs", C.c_void_p),
         ("sinks", C.c_void_p), ("output_scale", C.c_void_p), ("out", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_int64),
     ]
 
 
@@ -96,6 +97,7 @@ SYMBOLS = {
     "tq_decode_attention_static": (C.c_int, [C.POINTER(DecodeArgs), C.c_void_p]),
     "fwht128_quant_fp8": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "tq_prefill_attention_int4": (C.c_int, [C.POINTER(PrefillArgs), C.c_void_p]),
+    "tq_prefill_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
     "tq_full_dequant_kv": (C.c_int, [
         C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
         C.c_int32, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
@@ -432,11 +434,19 @@ def tq_kpool_compress_and_write_cache(kv_cache, slot_k, slot_score, ape, loc, *,
     return (ck, cs) if return_compressed else None
 
 
+def tq_prefill_workspace_bytes(num_tokens, Hq, Hk, D):
+    """Workspace bytes that put tq_prefill_attention_int4 on the matrix cores
+    (0 when that path does not apply)."""
+    return lib().tq_prefill_workspace_bytes(num_tokens, Hq, Hk, D)
+
+
 def prepare_prefill(query, key_cache, value_cache, block_table, cu_seqlens_q, seq_lens, *,
                     k_scale_cache, v_scale_cache, rht_signs, sm_scale=None, window=0,
-                    softcap=0.0, sinks=None, output_scale=None, out=None):
+                    softcap=0.0, sinks=None, output_scale=None, out=None, workspace="auto"):
     """Validate and marshal a tq_prefill_attention_int4 call; returns (Prepared, out).
-    out is [T, Hq, D] f32, or float8_e4m3fn when output_scale ([1] f32) is given."""
+    out is [T, Hq, D] f32, or float8_e4m3fn when output_scale ([1] f32) is given.
+    workspace: "auto" allocates what the matrix-core path needs (none when it
+    does not apply), None takes the vector path, or a device tensor."""
     T, hq, d = query.shape
     _need(query, torch.float32, "query")
     for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
@@ -483,6 +493,18 @@ def prepare_prefill(query, key_cache, value_cache, block_table, cu_seqlens_q, se
     a.k_scale_cache, a.v_scale_cache, a.rht_signs = (_ptr(k_scale_cache), _ptr(v_scale_cache),
                                                      _ptr(rht_signs))
     a.sinks, a.output_scale, a.out = _ptr(sinks), _ptr(output_scale), _ptr(out)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        nbytes = tq_prefill_workspace_bytes(T, hq, hk, d)
+        workspace = (torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=query.device)
+                     if nbytes > 0 else None)
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        keep.append(workspace)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     keep.append(a)
     return Prepared(lib().tq_prefill_attention_int4, (C.byref(a),), keep), out
 

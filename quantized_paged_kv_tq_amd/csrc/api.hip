@@ -46,6 +46,13 @@ int key_region_bytes(int d, int key_fmt) {
 }
 int value_index_bytes(int d, int val_fmt) { return (d * val_bits(val_fmt) + 7) / 8; }
 
+// The matrix-core prefill runs query tokens as decode entries, at most the
+// decode's per-call entry count at a time; its plan (three int32 per entry)
+// heads the workspace.
+constexpr int64_t kPrefillChunk = 4096;
+size_t prefill_plan_bytes(int64_t chunk) { return ((size_t)chunk * 3 * sizeof(int32_t) + 255) / 256 * 256; }
+int prefill_on_matrix_cores(const tqk::PrefillParams& pp, void* ws, hipStream_t st);
+
 }  // namespace
 
 extern "C" {
@@ -229,10 +236,20 @@ int tq_kpool_compress_and_write_cache(const void* slot_k, const void* slot_score
                   "tq_kpool_compress_and_write_cache");
 }
 
+size_t tq_prefill_workspace_bytes(int64_t num_tokens, int32_t Hq, int32_t Hk, int32_t D) {
+  if (num_tokens <= 0 || D != 128 || Hk <= 0 || Hq < Hk || Hq % Hk != 0 || Hq / Hk > 8) return 0;
+  const int64_t chunk = num_tokens < kPrefillChunk ? num_tokens : kPrefillChunk;
+  return prefill_plan_bytes(chunk) + tq_decode_workspace_bytes((int32_t)chunk, Hq, Hk, D, 1);
+}
+
 int tq_prefill_attention_int4(const tq_prefill_args* a, void* stream) {
   if (!a) return fail(TQ_EINVAL, "null args");
-  if (a->struct_size < sizeof(tq_prefill_args))
-    return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size, sizeof(tq_prefill_args));
+  if (a->struct_size < offsetof(tq_prefill_args, workspace))
+    return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size,
+                offsetof(tq_prefill_args, workspace));
+  // the workspace fields exist only in the current layout
+  void* const pws = a->struct_size >= sizeof(tq_prefill_args) ? a->workspace : nullptr;
+  const int64_t pws_bytes = a->struct_size >= sizeof(tq_prefill_args) ? a->workspace_bytes : 0;
   if (a->num_tokens < 0 || a->num_seqs < 0) return fail(TQ_EINVAL, "negative num_tokens or num_seqs");
   if (a->D != 64 && a->D != 128) return fail(TQ_ENOTSUP, "D=%d (INT4 prefill supports 64, 128)", a->D);
   if (a->Hk < 1 || a->Hq < a->Hk || a->Hq % a->Hk != 0)
@@ -285,8 +302,15 @@ int tq_prefill_attention_int4(const tq_prefill_args* a, void* stream) {
   p.window = a->window;
   p.sm_scale = a->sm_scale;
   p.softcap = a->softcap;
-  return launched(tqk::launch_prefill_int4(p, static_cast<hipStream_t>(stream)),
-                  "tq_prefill_attention_int4");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t need = tq_prefill_workspace_bytes(a->num_tokens, a->Hq, a->Hk, a->D);
+  if (pws && need > 0 && pws_bytes >= 0 && (size_t)pws_bytes >= need && aligned(pws, 16) &&
+      aligned(a->query, 16) && (a->output_scale || aligned(a->out, 16)) &&
+      aligned(a->key_cache, 16) && aligned(a->value_cache, 16)) {
+    const int r = prefill_on_matrix_cores(p, pws, st);
+    if (r != TQ_ENOTSUP) return r;
+  }
+  return launched(tqk::launch_prefill_int4(p, st), "tq_prefill_attention_int4");
 }
 
 int tq_full_dequant_kv(const uint8_t* kv_cache, const int32_t* block_table, int32_t max_blocks,
@@ -429,6 +453,55 @@ int decode_impl(const tq_decode_args* a, float* ws, int64_t ws_bytes, const char
   if (e != hipSuccess) return launched(e, what);
   snprintf(what, sizeof(what), "%s stage 2", name);
   return launched(tqk::launch_merge(p, st), what);
+}
+
+// Multi-query (prefill) attention on the matrix cores: each query token is
+// one entry of the split-KV INT4 decode (one split per entry), planned on
+// the GPU into the workspace's head, in chunks of kPrefillChunk tokens (the
+// decode's per-call entry limit). TQ_ENOTSUP when the decode declines the
+// shape before anything ran; the caller then takes the vector kernel.
+int prefill_on_matrix_cores(const tqk::PrefillParams& pp, void* ws, hipStream_t st) {
+  const int64_t T = pp.num_tokens;
+  const int64_t chunk = T < kPrefillChunk ? T : kPrefillChunk;
+  int32_t* lens = static_cast<int32_t*>(ws);
+  int32_t* rows = lens + chunk;
+  int32_t* offs = rows + chunk;
+  float* dws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + prefill_plan_bytes(chunk));
+  for (int64_t begin = 0; begin < T; begin += chunk) {
+    const int n = (int)(T - begin < chunk ? T - begin : chunk);
+    hipError_t e = tqk::launch_prefill_plan(pp, begin, n, lens, rows, offs, st);
+    if (e != hipSuccess) return launched(e, "tq_prefill_attention_int4 plan");
+    tqk::DecodeParams p;
+    p.B = n; p.hq = pp.hq; p.hk = pp.hk; p.d = pp.d; p.g = pp.g;
+    p.block_size = pp.block_size; p.max_blocks = pp.max_blocks; p.splits = 1;
+    p.key_fmt = TQ_KEY_INT4; p.val_fmt = TQ_VAL_INT4; p.norm_correction = 0;
+    p.sm_scale = pp.sm_scale; p.num_blocks = pp.num_blocks;
+    p.q = pp.q + begin * pp.hq * pp.d;
+    p.block_table = pp.block_table; p.seq_lens = lens;
+    p.kc = pp.kc; p.vc = pp.vc; p.ks = pp.ks; p.vs = pp.vs;
+    p.rht_signs = pp.rht_signs; p.kv = nullptr; p.slot_bytes = 0;
+    p.centroids = nullptr; p.rot_signs = nullptr;
+    p.ws = dws;
+    p.out = pp.out ? pp.out + begin * pp.hq * pp.d : nullptr;
+    p.lse = nullptr;
+    p.nw = 0; p.wgh = 1; p.force_wide = 0;
+    p.wsp = dws + (int64_t)n * pp.hq * (pp.d + 1);
+    p.wsx = reinterpret_cast<int*>(p.wsp + (int64_t)2 * tqk::balance_max_wgs(pp.hk, pp.g) * pp.hq *
+                                               (pp.d + 1));
+    p.bt_row = rows;
+    p.tok_off = offs;
+    p.softcap = pp.softcap;
+    p.sinks = pp.sinks;
+    p.output_scale = pp.output_scale;
+    p.out_fp8 = pp.out_fp8 ? pp.out_fp8 + begin * pp.hq * pp.d : nullptr;
+    e = tqk::launch_decode_int4_mfma(p, st);
+    if (e == hipErrorNotSupported && begin == 0) return TQ_ENOTSUP;
+    if (e != hipSuccess) return launched(e, "tq_prefill_attention_int4 stage 1");
+    e = tqk::launch_merge(p, st);
+    if (e != hipSuccess) return launched(e, "tq_prefill_attention_int4 stage 2");
+  }
+  g_err[0] = '\0';
+  return TQ_OK;
 }
 
 // Workspace of tq_decode_attention_static: a file-scope device array. Every

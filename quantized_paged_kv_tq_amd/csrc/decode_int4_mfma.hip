@@ -121,7 +121,11 @@ constexpr int kLastOfSplit = 2;
 // of live tokens decides what a masked token's bytes may do: its score is
 // -inf (weight 0, so its value nibbles add 0) and its value scale word is
 // taken as 0.
-template <int W, int NH, int DEPTH, bool WIDE>
+//
+// MQ: multi-query entries (prefill): entry b reads block-table row
+// p.bt_row[b] from token p.tok_off[b] on, and scores may be softcapped. The
+// plain decode instantiation carries none of it.
+template <int W, int NH, int DEPTH, bool WIDE, bool MQ>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DEPTH == 2 ? 2 : 1)))
 void decode_int4_mfma_kernel(DecodeParams p) {
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
@@ -168,6 +172,9 @@ void decode_int4_mfma_kernel(DecodeParams p) {
 
   const uint32_t bs = (uint32_t)p.block_size;
   const bool bs_pow2 = (bs & (bs - 1u)) == 0u;
+  const bool capped = MQ && p.softcap > 0.0f;
+  const float cap_in = kLn2 / (capped ? p.softcap : 1.0f);  // base-2 score -> y = s / c
+  const float cap_out = p.softcap * kLog2e;                 // tanh -> base-2 score
   const int bs_shift = __builtin_ctz(bs);
   const uint32_t nrows = (uint32_t)(p.num_blocks * bs * p.hk);
   const __amdgpu_buffer_rsrc_t rk_ = make_rsrc(p.kc, WIDE ? 0u : nrows * (uint32_t)(D / 2));
@@ -439,7 +446,7 @@ void decode_int4_mfma_kernel(DecodeParams p) {
       vsw[s] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.vsw);
     }
     // ---- scores on the matrix cores ----
-    float sc[NH][4];
+    float sc[NH][4], smask[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const v4u w4 = X.kraw[s];
@@ -467,9 +474,27 @@ void decode_int4_mfma_kernel(DecodeParams p) {
         const float d2 = __builtin_fmaf(-zpk, qsum[r][2], (float)c.z);
         const float d3 = __builtin_fmaf(-zpk, qsum[r][3], (float)c.w);
         const float dot = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(d3, 128.0f, d2), 128.0f, d1), 128.0f, d0);
-        sc[r][s] = fminf(dot * (qf[r] * ksc), mask);
+        sc[r][s] = dot * (qf[r] * ksc);
       }
+      smask[s] = mask;
     }
+    // softcap on natural-unit scores (sc is in base-2 units):
+    // c tanh(x ln2 / c) log2e, tanh(y) = sign(y) (1 - 2 / (e^{2|y|} + 1))
+    if (MQ && capped) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          const float y = sc[r][s] * cap_in;
+          const float e = __builtin_amdgcn_exp2f(fabsf(y) * 2.8853900817779268f);  // e^{2|y|}
+          const float t = 1.0f - 2.0f / (e + 1.0f);
+          sc[r][s] = __builtin_copysignf(t, y) * cap_out;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int r = 0; r < NH; ++r) sc[r][s] = fminf(sc[r][s], smask[s]);
     float vsc[4];
     uint32_t zp4 = 0;
     float smax = 0.0f;
@@ -609,9 +634,11 @@ void decode_int4_mfma_kernel(DecodeParams p) {
       uint32_t row = WIDE ? 0u : kMaskedByte;
       bool live = false;
       if (tok < end) {
-        const uint32_t t32 = (uint32_t)tok;
+        // multi-query entries read their sequence's row from an offset
+        const uint32_t t32 = (uint32_t)tok + (MQ ? (uint32_t)p.tok_off[b] : 0u);
+        const int64_t brow = MQ ? (int64_t)p.bt_row[b] : (int64_t)b;
         const uint32_t pi = bs_pow2 ? (t32 >> bs_shift) : (t32 / bs);
-        const int64_t page = p.block_table[(int64_t)b * p.max_blocks + pi];
+        const int64_t page = p.block_table[brow * p.max_blocks + pi];
         if (page >= 0 && page < p.num_blocks) {
           const uint32_t r = ((uint32_t)page * bs + (t32 - pi * bs)) * (uint32_t)p.hk;
           row = WIDE ? r : r * (uint32_t)(D / 2);
@@ -648,10 +675,15 @@ template <int W, int NH, int DEPTH>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  if (wide)
-    hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
-  else
-    hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+  const bool mq = p.bt_row != nullptr;
+#define TQ_I4(WD, M) \
+  hipLaunchKernelGGL((decode_int4_mfma_kernel<W, NH, DEPTH, WD, M>), dim3(blocks), dim3(64 * W), lds, st, p)
+  if (mq) {
+    if (wide) TQ_I4(true, true); else TQ_I4(false, true);
+  } else {
+    if (wide) TQ_I4(true, false); else TQ_I4(false, false);
+  }
+#undef TQ_I4
   return hipGetLastError();
 }
 
@@ -659,6 +691,9 @@ hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
 
 hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
   if (p.d != D || p.key_fmt != KF_INT4 || p.g > 8) return hipErrorNotSupported;
+  // multi-query entries come with both maps; a softcap only with them
+  if ((p.bt_row == nullptr) != (p.tok_off == nullptr) || (p.softcap > 0.0f && !p.bt_row))
+    return hipErrorInvalidValue;
   // cache bytes below 2 GiB take 32-bit buffer offsets; larger caches the
   // 64-bit addressing variant, whose tile table holds 32-bit row indices
   const int64_t rows = p.num_blocks * (int64_t)p.block_size * p.hk;

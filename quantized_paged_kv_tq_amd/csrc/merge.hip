@@ -7,7 +7,10 @@
 //   M = max lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
 //   lse = M + ln(sum w_s).
 // For the INT4 format the output is rotated back (int4_per_token_head.py,
-// unified_attention_int4): out = rht_signs * FWHT(o) / D.
+// unified_attention_int4): out = rht_signs * FWHT(o) / D. Used for the
+// multi-query (prefill) attention, a sink term joins the denominator and the
+// output may be stored as E4M3 codes (int4_per_token_head.py, _attn_packed:
+// sinks, output scale).
 // One workgroup per (batch, query head), one lane per output dimension.
 #include "balance.h"
 #include "tq_device.h"
@@ -168,6 +171,9 @@ __global__ __launch_bounds__(D * PG) void merge_kernel(DecodeParams p) {
   // the first group (threads < D) stores the row; the others only take
   // part in the barriers below
   if (wsum > 0.0f) o /= wsum;
+  // a sink joins the denominator: sum_s e^{lse_s} o_s / (sum_s e^{lse_s} +
+  // e^{sink}); a row with no visible key stays 0
+  if (p.sinks && wsum > 0.0f) o *= wsum / (wsum + __expf(p.sinks[h] - M));
   if constexpr (ROTATE) {
     // inverse RHT: FWHT over D (strides 1 .. 32 inside the wave, 64 through
     // LDS), then signs and 1/D
@@ -187,7 +193,13 @@ __global__ __launch_bounds__(D * PG) void merge_kernel(DecodeParams p) {
     o = o * sgn * (1.0f / (float)D);
   }
   if (tid < D) {
-    p.out[(int64_t)bh * D + d] = o;
+    if (p.out_fp8) {
+      // E4M3 codes of clamp(out * fl(1 / output_scale), +-448), nearest even
+      const float v = fminf(fmaxf(o * (1.0f / p.output_scale[0]), -448.0f), 448.0f);
+      p.out_fp8[(int64_t)bh * D + d] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu);
+    } else {
+      p.out[(int64_t)bh * D + d] = o;
+    }
     if (p.lse && d == 0) p.lse[bh] = (wsum > 0.0f) ? M + __logf(wsum) : -INFINITY;
   }
 }

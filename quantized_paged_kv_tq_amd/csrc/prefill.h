@@ -27,6 +27,10 @@ struct PrefillParams {
   float sm_scale, softcap;
 };
 hipError_t launch_prefill_int4(const PrefillParams& p, hipStream_t st);
+// Query tokens [begin, begin + n) as decode entries (matrix-core path): per
+// entry the visible key count, the block-table row and the first key.
+hipError_t launch_prefill_plan(const PrefillParams& p, int64_t begin, int n, int32_t* lens,
+                               int32_t* rows, int32_t* offs, hipStream_t st);
 
 struct DequantParams {
   const uint8_t* kv;          // [num_blocks, bs, hk, slot_bytes]

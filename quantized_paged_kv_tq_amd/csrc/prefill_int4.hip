@@ -283,6 +283,40 @@ __global__ __launch_bounds__(256) void prefill_int4_kernel(PrefillParams p) {
   }
 }
 
+// Multi-query attention as one decode entry per query token: token tq of
+// sequence b at position pos sees keys [t0, t1) (t1 = min(pos + 1, seq), t0
+// = pos - W + 1 under a window), so entry i = tq - begin is a decode of
+// t1 - t0 keys read from block-table row b from token t0 on. Tokens with no
+// visible key (or outside every sequence) get length 0 (their output is 0).
+__global__ __launch_bounds__(256) void prefill_plan_kernel(PrefillParams p, int64_t begin, int n,
+                                                           int32_t* lens, int32_t* rows,
+                                                           int32_t* offs) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t tq = begin + i;
+  int lo_b = 0, hi_b = p.num_seqs;  // largest b with cu[b] <= tq
+  while (hi_b - lo_b > 1) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (p.cu_seqlens[mid] <= tq) lo_b = mid;
+    else hi_b = mid;
+  }
+  const int b = lo_b;
+  const int64_t q0 = p.cu_seqlens[b], q1 = p.cu_seqlens[b + 1];
+  int64_t seq = p.seq_lens[b];
+  const int64_t cap = (int64_t)p.max_blocks * p.block_size;
+  seq = seq < 0 ? 0 : (seq > cap ? cap : seq);
+  int64_t t0 = 0, t1 = 0;
+  if (tq >= q0 && tq < q1) {
+    const int64_t pos = seq - (q1 - q0) + (tq - q0);
+    t1 = pos + 1 < seq ? pos + 1 : seq;
+    if (p.window > 0 && pos - p.window + 1 > 0) t0 = pos - p.window + 1;
+  }
+  const bool any = t1 > t0;
+  lens[i] = any ? (int32_t)(t1 - t0) : 0;
+  rows[i] = b;
+  offs[i] = any ? (int32_t)t0 : 0;
+}
+
 template <int D>
 hipError_t launch_d(const PrefillParams& p, hipStream_t st) {
   const int G = p.g <= 1 ? 1 : (p.g <= 2 ? 2 : (p.g <= 4 ? 4 : 8));
@@ -298,6 +332,13 @@ hipError_t launch_d(const PrefillParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_prefill_plan(const PrefillParams& p, int64_t begin, int n, int32_t* lens,
+                               int32_t* rows, int32_t* offs, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p,
+                     begin, n, lens, rows, offs);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_int4(const PrefillParams& p, hipStream_t st) {
   if (p.d == 128) return launch_d<128>(p, st);

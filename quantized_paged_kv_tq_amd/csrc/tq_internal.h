@@ -73,6 +73,15 @@ struct DecodeParams {
   int force_wide;  // take the 64-bit addressing variant whatever the cache size
   float* wsp;    // piece slots [Hk / wgh][nw][2][wgh * g][D+1], after ws
   int* wsx;      // [B + 1] tile-list prefix sums (stage 1 writes, stage 2 reads)
+  // Multi-query use (prefill as one decode entry per query token; INT4
+  // matrix-core stage 1 and stage 2 only). Entry b reads the block table
+  // row bt_row[b] from token tok_off[b] on (null: row b, from token 0).
+  const int32_t* bt_row = nullptr;
+  const int32_t* tok_off = nullptr;
+  float softcap = 0.0f;            // > 0: score <- softcap * tanh(score / softcap)
+  const float* sinks = nullptr;    // [Hq]: e^sink joins each softmax denominator
+  const float* output_scale = nullptr;  // [1]: stage 2 writes E4M3 codes to out_fp8
+  uint8_t* out_fp8 = nullptr;      // [B, Hq, D]
 };
 
 // Format-generic vector stage 1 (every key/value format).

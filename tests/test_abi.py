@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
                           "tq_decode_attention", "tq_decode_attention_static",
                           "fwht128_quant_fp8",
                           "tq_kpool_compress_and_write_cache", "tq_prefill_attention_int4",
-                          "tq_full_dequant_kv"}
+                          "tq_prefill_workspace_bytes", "tq_full_dequant_kv"}
     raw = C.CDLL(tq.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -263,6 +263,27 @@ def test_prefill_empty_and_null(L):
     assert L.tq_prefill_attention_int4(None, None) == tq.TQ_EINVAL
     assert L.tq_prefill_attention_int4(C.byref(_pargs(num_tokens=0)), None) == tq.TQ_OK
     assert tq.last_error() == ""
+    # the layout before the workspace fields is still accepted
+    old = C.sizeof(tq.PrefillArgs) - 16
+    assert tq.PrefillArgs.workspace.offset == old
+    assert L.tq_prefill_attention_int4(C.byref(_pargs(num_tokens=0, struct_size=old)), None) == tq.TQ_OK
+    assert L.tq_prefill_attention_int4(C.byref(_pargs(struct_size=old - 8)), None) == tq.TQ_EINVAL
+
+
+def test_prefill_workspace_bytes(L):
+    # a plan of three int32 per token of a chunk (256-byte aligned), then the
+    # decode workspace of one chunk with one split per entry
+    def plan(n):
+        return (n * 12 + 255) // 256 * 256
+    assert tq.tq_prefill_workspace_bytes(10, 32, 8, 128) == \
+        plan(10) + tq.tq_decode_workspace_bytes(10, 32, 8, 128, 1)
+    # chunks of at most 4096 tokens
+    assert tq.tq_prefill_workspace_bytes(10000, 8, 2, 128) == \
+        plan(4096) + tq.tq_decode_workspace_bytes(4096, 8, 2, 128, 1)
+    # no matrix-core path: D != 128, g > 8, no tokens
+    assert tq.tq_prefill_workspace_bytes(10, 8, 2, 64) == 0
+    assert tq.tq_prefill_workspace_bytes(10, 18, 2, 128) == 0
+    assert tq.tq_prefill_workspace_bytes(0, 8, 2, 128) == 0
 
 
 def test_full_dequant_validation(L):
