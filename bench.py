@@ -353,6 +353,12 @@ def _timed_calls(steps):
     return max(steps, MIN_TIMED_CALLS)
 
 
+def set_min_timed_calls(n):
+    """Counter-collection runs (one record per dispatch) time fewer calls."""
+    global MIN_TIMED_CALLS
+    MIN_TIMED_CALLS = max(1, int(n))
+
+
 def _time_loop(torch, stream, fn, warmup, steps):
     """Median of 5 event-timed runs of max(steps, MIN_TIMED_CALLS) calls,
     after warmup."""
@@ -606,11 +612,14 @@ def main():
     ap.add_argument("--workload", default="llama8b_int4")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--min-calls", type=int, default=MIN_TIMED_CALLS,
+                    help="secondary workloads: least calls per timed run (fewer for counter runs)")
     ap.add_argument("--splits", type=int, default=0, help="override num_kv_splits (sweeps)")
     ap.add_argument("--wide", action="store_true",
                     help="decode through the 64-bit addressing variant (the one caches of "
                          "2 GiB and more take) whatever the cache size")
     args = ap.parse_args()
+    set_min_timed_calls(args.min_calls)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU "
               "component in this build (run with --gpus 1)", file=sys.stderr)

@@ -11,6 +11,7 @@
 #include "balance.h"
 #include "tq_internal.h"
 #include "kpool.h"
+#include "merge_one.h"
 #include "prefill.h"
 
 namespace {
@@ -497,7 +498,7 @@ int prefill_on_matrix_cores(const tqk::PrefillParams& pp, void* ws, hipStream_t 
     e = tqk::launch_decode_int4_mfma(p, st);
     if (e == hipErrorNotSupported && begin == 0) return TQ_ENOTSUP;
     if (e != hipSuccess) return launched(e, "tq_prefill_attention_int4 stage 1");
-    e = tqk::launch_merge(p, st);
+    e = tqk::launch_merge_one_split(p, st);
     if (e != hipSuccess) return launched(e, "tq_prefill_attention_int4 stage 2");
   }
   g_err[0] = '\0';
