@@ -199,7 +199,7 @@ int tq_encode_and_cache(const void* key, const void* value, int32_t kv_dtype,
  * result for that sequence is then unspecified); seq_len is clamped to
  * max_blocks * block_size; seq_len == 0 gives out = 0 and lse = -inf.
  * Supported: D in {64, 128} (and 256 for the TQ formats); Hq % Hk == 0 and
- * Hq / Hk <= 16;
+ * Hq / Hk <= 64;
  * 1 <= num_kv_splits <= 256; block_size >= 1.
  */
 typedef struct tq_decode_args {
@@ -331,7 +331,7 @@ int fwht128_quant_fp8(const void* x_bf16, int64_t rows, uint8_t* y_e4m3,
  *
  * Paths. With a workspace of at least tq_prefill_workspace_bytes(...) bytes
  * (16-byte aligned, as are query, f32 out and both caches), D = 128 and
- * Hq / Hk <= 8, the
+ * Hq / Hk <= 32, the
  * call runs on the matrix cores: each query token becomes one entry of the
  * split-KV INT4 decode (its visible keys [t0, t1) read from its sequence's
  * block-table row), in chunks of at most 4096 tokens that reuse the
@@ -370,7 +370,7 @@ int tq_prefill_attention_int4(const tq_prefill_args* args, void* stream);
 /*
  * Workspace bytes that put tq_prefill_attention_int4 on the matrix cores
  * for num_tokens query tokens (0 when that path does not apply: D != 128,
- * Hq / Hk > 8, or no tokens): three int32 per token of a chunk of up to 4096
+ * Hq / Hk > 32, or no tokens): three int32 per token of a chunk of up to 4096
  * tokens, then the split-KV decode workspace of one chunk
  * (tq_decode_workspace_bytes with one split).
  */

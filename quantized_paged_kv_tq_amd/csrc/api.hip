@@ -238,7 +238,7 @@ int tq_kpool_compress_and_write_cache(const void* slot_k, const void* slot_score
 }
 
 size_t tq_prefill_workspace_bytes(int64_t num_tokens, int32_t Hq, int32_t Hk, int32_t D) {
-  if (num_tokens <= 0 || D != 128 || Hk <= 0 || Hq < Hk || Hq % Hk != 0 || Hq / Hk > 8) return 0;
+  if (num_tokens <= 0 || D != 128 || Hk <= 0 || Hq < Hk || Hq % Hk != 0 || Hq / Hk > 32) return 0;
   const int64_t chunk = num_tokens < kPrefillChunk ? num_tokens : kPrefillChunk;
   return prefill_plan_bytes(chunk) + tq_decode_workspace_bytes((int32_t)chunk, Hq, Hk, D, 1);
 }
@@ -376,7 +376,7 @@ int decode_impl(const tq_decode_args* a, float* ws, int64_t ws_bytes, const char
     return fail(TQ_EINVAL, "args.struct_size %u < %zu", a->struct_size, sizeof(tq_decode_args));
   if (a->B < 0 || a->Hq <= 0 || a->Hk <= 0) return fail(TQ_EINVAL, "bad B / Hq / Hk");
   if (a->Hq % a->Hk != 0) return fail(TQ_EINVAL, "Hq %% Hk != 0");
-  if (a->Hq / a->Hk > 16) return fail(TQ_ENOTSUP, "Hq / Hk > 16");
+  if (a->Hq / a->Hk > 64) return fail(TQ_ENOTSUP, "Hq / Hk > 64");
   if (a->D <= 0 || a->D % 2 != 0 || (a->D & (a->D - 1)) != 0)
     return fail(TQ_EINVAL, "D must be an even power of two (got %d)", a->D);
   if (a->D != 64 && a->D != 128 && !(a->D == 256 && a->key_fmt != TQ_KEY_INT4))

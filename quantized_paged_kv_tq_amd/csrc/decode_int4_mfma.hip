@@ -690,7 +690,9 @@ hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
 }  // namespace
 
 hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
-  if (p.d != D || p.key_fmt != KF_INT4 || p.g > 8) return hipErrorNotSupported;
+  // up to 32 query heads per kv head: ceil(g / 4) waves of four heads each,
+  // at most 8 waves per workgroup
+  if (p.d != D || p.key_fmt != KF_INT4 || p.g > 32) return hipErrorNotSupported;
   // multi-query entries come with both maps; a softcap only with them
   if ((p.bt_row == nullptr) != (p.tok_off == nullptr) || (p.softcap > 0.0f && !p.bt_row))
     return hipErrorInvalidValue;
@@ -713,8 +715,13 @@ hipError_t launch_decode_int4_mfma(DecodeParams& p, hipStream_t st) {
   switch (p.wgh * qs) {
     case 1: return launch<1, 1, 2>(p, st, wide);
     case 2: return launch<2, 1, 2>(p, st, wide);
+    case 3: return launch<3, 1, 2>(p, st, wide);
     case 4: return launch<4, 1, 2>(p, st, wide);
-    default: return launch<8, 1, 2>(p, st, wide);
+    case 5: return launch<5, 1, 2>(p, st, wide);
+    case 6: return launch<6, 1, 2>(p, st, wide);
+    case 7: return launch<7, 1, 2>(p, st, wide);
+    case 8: return launch<8, 1, 2>(p, st, wide);
+    default: return hipErrorNotSupported;
   }
 }
 

@@ -89,7 +89,7 @@ def _args(**kw):
     (dict(D=96), tq.TQ_EINVAL),
     (dict(D=256), tq.TQ_ENOTSUP),
     (dict(Hq=6, Hk=4), tq.TQ_EINVAL),
-    (dict(Hq=34, Hk=2), tq.TQ_ENOTSUP),
+    (dict(Hq=130, Hk=2), tq.TQ_ENOTSUP),
     (dict(num_kv_splits=0), tq.TQ_EINVAL),
     (dict(num_kv_splits=257), tq.TQ_EINVAL),
     (dict(block_size=0), tq.TQ_EINVAL),
@@ -280,9 +280,10 @@ def test_prefill_workspace_bytes(L):
     # chunks of at most 4096 tokens
     assert tq.tq_prefill_workspace_bytes(10000, 8, 2, 128) == \
         plan(4096) + tq.tq_decode_workspace_bytes(4096, 8, 2, 128, 1)
-    # no matrix-core path: D != 128, g > 8, no tokens
+    # no matrix-core path: D != 128, g > 32, no tokens
     assert tq.tq_prefill_workspace_bytes(10, 8, 2, 64) == 0
-    assert tq.tq_prefill_workspace_bytes(10, 18, 2, 128) == 0
+    assert tq.tq_prefill_workspace_bytes(10, 66, 2, 128) == 0
+    assert tq.tq_prefill_workspace_bytes(10, 18, 2, 128) > 0
     assert tq.tq_prefill_workspace_bytes(0, 8, 2, 128) == 0
 
 

@@ -61,6 +61,22 @@ def test_int4_shapes(shape, flags):
     assert_close(got, ref, lse, ref_lse, str(shape))
 
 
+@pytest.mark.parametrize("hq,hk", [(24, 2), (32, 2), (40, 2), (56, 2), (64, 2), (96, 2)],
+                         ids=["g12", "g16", "g20", "g28", "g32", "g48"])
+def test_int4_query_groups_above_eight(hq, hk):
+    """g = 9 .. 32 on the matrix-core path: ceil(g / 4) waves of four query
+    heads per kv head (workgroups of 3 .. 8 waves, the last wave padded);
+    g = 48 goes to the generic kernel. Empty, one-token and long sequences."""
+    seq = [0, 1, 300, 777, 65, 2000]
+    w = W.custom_decode_workload(330 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    c = int4_caches(w)
+    q = W.query(w)
+    ref, ref_lse = _oracle_int4(w, q, c)
+    for flags in (0, tq.FLAG_WIDE):
+        got, lse = gpu_int4_decode(w, q, c, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d flags=%d" % (hq, hk, flags))
+
+
 def test_int4_split_invariance_and_empty_splits():
     w = W.custom_decode_workload(140, 2, 8, 2, 128, 16, 4, [37, 100], 2, "bf16")
     c = int4_caches(w)

@@ -65,7 +65,7 @@ def test_tiny_features(window, softcap, sinks, d, path):
            sinks=W.sink_values(w) if sinks else None)
 
 
-@pytest.mark.parametrize("hq,hk", [(32, 8), (16, 2), (8, 8), (12, 2), (6, 3)])
+@pytest.mark.parametrize("hq,hk", [(32, 8), (16, 2), (8, 8), (12, 2), (6, 3), (32, 2), (40, 2)])
 @PATHS
 def test_gqa_d128(hq, hk, path):
     w, c, cu, q = _case(202 + hq + hk, 3, hq, hk, 128, 16, ctx=[100, 0, 300], qlen=[40, 70, 3])
