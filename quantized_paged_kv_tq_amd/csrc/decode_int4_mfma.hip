@@ -437,6 +437,13 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     }
     seg_to_end = (info.z & kLastOfSplit) != 0;
     issue(Y, k + DEPTH - 1);
+    // Hold the workgroup's waves on one tile: the two waves of a SIMD
+    // otherwise drift apart (the younger one falls behind) and a long range
+    // ends with the younger waves alone. Every wave of the workgroup walks
+    // the same tiles, so each reaches the barrier equally often. (The
+    // multi-query entries are bound by ALU work, where the drift costs
+    // nothing and the barrier does.)
+    if constexpr (!MQ) __builtin_amdgcn_s_barrier();
 
     // scale words of tokens 16s+n from lane 16s+n
     uint32_t ksw[4], vsw[4];
