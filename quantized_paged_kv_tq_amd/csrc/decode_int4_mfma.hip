@@ -319,8 +319,9 @@ void decode_int4_mfma_kernel(DecodeParams p) {
   // 32g + 16c + 8(j/2) + 2b + (j%2) -- the order of the K unpack.
   v4i qa[NH][2];
   float qsum[NH][4], qf[NH];
-  auto load_query = [&](int b) {
-    float qx[NHEAD][2];
+  // the wave's query rows of sequence b times the RHT signs (lane: dims
+  // lane and lane + 64)
+  auto query_rows = [&](int b, float (&qx)[NHEAD][2]) {
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
       const bool ok = hh < gw;
@@ -328,6 +329,9 @@ void decode_int4_mfma_kernel(DecodeParams p) {
       qx[hh][0] = ok ? qrow[lane] * p.rht_signs[lane] : 0.0f;
       qx[hh][1] = ok ? qrow[lane + 64] * p.rht_signs[lane + 64] : 0.0f;
     }
+  };
+  // rotate, scale and split the rows into the MFMA A-operand image
+  auto query_image = [&](const float (&qx)[NHEAD][2]) {
     uint8_t* img = reinterpret_cast<uint8_t*>(&wbuf[wave][0][0][0][0]);
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
@@ -383,6 +387,11 @@ void decode_int4_mfma_kernel(DecodeParams p) {
       }
     wave_sync();  // the image region is reused for the weight digit planes
   };
+  auto load_query = [&](int b) {
+    float qx[NHEAD][2];
+    query_rows(b, qx);
+    query_image(qx);
+  };
   uint32_t(*p8)[4][4][16] = reinterpret_cast<uint32_t(*)[4][4][16]>(&wbuf[wave][0][0][0][0]);
 
   // ---------------- segment bookkeeping ----------------
@@ -427,8 +436,9 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     const int4 info = tinfo[k];
     if (gk == lo || (info.z & kFirstOfSplit)) {
       // a new segment begins with this tile
+      // (the range's first query is set up before its first tile)
       if (gk != lo) emit();
-      if (gk == lo || info.x != seg_b) load_query(info.x);
+      if (gk != lo && info.x != seg_b) load_query(info.x);
       reset();
       seg_b = info.x;
       seg_s = info.y;
@@ -607,6 +617,20 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     wave_sync();  // the digit planes are rewritten by the next tile
   };
 
+  // The range's first query rows are requested now: their loads overlap
+  // the tile table's, so the first tiles can be issued back to back once
+  // the table is built (tile 0 would otherwise wait for the query).
+  float q0[NHEAD][2];
+  {
+    int bl = 0, bh = p.B - 1;  // the sequence of tile lo, as the table finds it
+    while (bl < bh) {
+      const int m = (bl + bh + 1) >> 1;
+      if (prefix[m] <= lo) bl = m;
+      else bh = m - 1;
+    }
+    query_rows(bl, q0);
+  }
+
   Buf ring[DEPTH];
   for (int c0 = lo; c0 < hi; c0 += kChunk) {
     const int K = hi - c0 < kChunk ? hi - c0 : kChunk;  // tiles of this chunk
@@ -664,7 +688,7 @@ void decode_int4_mfma_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    // the first tiles' loads overlap the query set-up
+    if (c0 == lo) query_image(q0);
 #pragma unroll
     for (int u = 0; u < DEPTH - 1; ++u) issue(ring[u], u);
     for (int k = 0; k < K; k += DEPTH) {
