@@ -108,6 +108,10 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 template <int W, int NH, bool VF8, bool WIDE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_tq_fp8_kernel(DecodeParams p) {
+  // the range's first query is requested before the tile table is built
+  // (not where holding it through the table build costs registers in the
+  // tile loop: the 64-bit, FP8-value and two-row-set variants)
+  constexpr bool kEarlyQuery = !WIDE && !VF8 && NH == 1;
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
   __shared__ __attribute__((aligned(16))) uint32_t p8[VF8 ? 1 : W][NH][4][4][16];  // weight digit planes
@@ -279,16 +283,29 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   // 32g + 8kb .. 32g + 8kb + 7 (part 3: zero)
   v8bf16 qa[NH][4];
   float qf;
-  auto load_query = [&](int b) {
+  // the query dims of lane (m = 4h + part, g) for sequence b: 32g + 8kb ..
+  // 32g + 8kb + 7 of head h, in two float4
+  auto query_rows = [&](int b, float4 (&raw)[NH][4][2]) {
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+      const int hq = 4 * r + (ln >> 2);
+      const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        raw[r][kb][0] = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
+        raw[r][kb][1] = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
+      }
+    }
+  };
+  auto query_image = [&](const float4 (&raw)[NH][4][2]) {
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       const int hq = 4 * r + (ln >> 2), part = ln & 3;
       const bool ok = hq < gw && part < 3;
-      const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
-        const float4 c = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
+        const float4 a = raw[r][kb][0];
+        const float4 c = raw[r][kb][1];
         const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
         uint32_t w[4];
 #pragma unroll
@@ -311,6 +328,11 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       }
     }
     qf = p.sm_scale * kLog2e;
+  };
+  auto load_query = [&](int b) {
+    float4 raw[NH][4][2];
+    query_rows(b, raw);
+    query_image(raw);
   };
 
   // ---------------- segment bookkeeping ----------------
@@ -350,8 +372,10 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     const int gk = c0 + k;
     const int4 info = tinfo[k];
     if (gk == lo || (info.z & kFirstOfSplit)) {
+      // (with kEarlyQuery the range's first query is set up before its
+      // first tile)
       if (gk != lo) emit();
-      if (gk == lo || info.x != seg_b) load_query(info.x);
+      if ((!kEarlyQuery || gk != lo) && (gk == lo || info.x != seg_b)) load_query(info.x);
       reset();
       seg_b = info.x;
       seg_s = info.y;
@@ -580,6 +604,19 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     }
   };
 
+  // The range's first query rows are requested now: their loads overlap
+  // the tile table's, so tile 0 does not wait behind the query set-up.
+  float4 q0[NH][4][2];
+  if constexpr (kEarlyQuery) {
+    int bl = 0, bh = p.B - 1;  // the sequence of tile lo, as the table finds it
+    while (bl < bh) {
+      const int m = (bl + bh + 1) >> 1;
+      if (prefix[m] <= lo) bl = m;
+      else bh = m - 1;
+    }
+    query_rows(bl, q0);
+  }
+
   Buf ring[2];
   for (int c0 = lo; c0 < hi; c0 += kChunk) {
     const int K = hi - c0 < kChunk ? hi - c0 : kChunk;
@@ -627,6 +664,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       }
     }
     __syncthreads();
+    if (kEarlyQuery && c0 == lo) query_image(q0);
     issue(ring[0], 0);
     // the two register sets as a ring indexed by the unrolled position (the
     // compiler keeps them apart without copies or spills)

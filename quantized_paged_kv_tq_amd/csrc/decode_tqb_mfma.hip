@@ -309,8 +309,9 @@ void decode_tqb_kernel(DecodeParams p) {
   // digit of dim 32g + 16kc + 4j + bb -- the byte order of the bit planes.
   v4i qa[NH][2];
   float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
-  auto load_query = [&](int b) {
-    float qx[NHEAD][2];
+  // the wave's query rows of sequence b times the rotation signs (lane:
+  // dims lane and lane + 64)
+  auto query_rows = [&](int b, float (&qx)[NHEAD][2]) {
     const float s0 = p.rot_signs ? p.rot_signs[lane] : 1.0f;
     const float s1 = p.rot_signs ? p.rot_signs[lane + 64] : 1.0f;
 #pragma unroll
@@ -320,6 +321,9 @@ void decode_tqb_kernel(DecodeParams p) {
       qx[hh][0] = ok ? qrow[lane] * s0 : 0.0f;
       qx[hh][1] = ok ? qrow[lane + 64] * s1 : 0.0f;
     }
+  };
+  // rotate, scale and split the rows into the MFMA A-operand image
+  auto query_image = [&](const float (&qx)[NHEAD][2]) {
     uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0][0]);
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
@@ -374,6 +378,11 @@ void decode_tqb_kernel(DecodeParams p) {
         qa[r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
       }
   };
+  auto load_query = [&](int b) {
+    float qx[NHEAD][2];
+    query_rows(b, qx);
+    query_image(qx);
+  };
 
   // ---------------- segment bookkeeping ----------------
   int seg_b = -1, seg_s = 0;
@@ -412,8 +421,9 @@ void decode_tqb_kernel(DecodeParams p) {
     const int gk = c0 + k;
     const int4 info = tinfo[k];
     if (gk == lo || (info.z & kFirstOfSplit)) {
+      // (the range's first query is set up before its first tile)
       if (gk != lo) emit();
-      if (gk == lo || info.x != seg_b) load_query(info.x);
+      if (gk != lo && info.x != seg_b) load_query(info.x);
       reset();
       seg_b = info.x;
       seg_s = info.y;
@@ -625,6 +635,19 @@ void decode_tqb_kernel(DecodeParams p) {
     wave_sync();
   };
 
+  // The range's first query rows are requested now: their loads overlap
+  // the tile table's, so tile 0 does not wait behind the query set-up.
+  float q0[NHEAD][2];
+  {
+    int bl = 0, bh = p.B - 1;  // the sequence of tile lo, as the table finds it
+    while (bl < bh) {
+      const int m = (bl + bh + 1) >> 1;
+      if (prefix[m] <= lo) bl = m;
+      else bh = m - 1;
+    }
+    query_rows(bl, q0);
+  }
+
   Buf ring[2];
   for (int c0 = lo; c0 < hi; c0 += kChunk) {
     const int K = hi - c0 < kChunk ? hi - c0 : kChunk;
@@ -672,6 +695,7 @@ void decode_tqb_kernel(DecodeParams p) {
       }
     }
     __syncthreads();
+    if (c0 == lo) query_image(q0);
     issue(ring[0], 0);
     issue_v(ring[0], 0);
     // the two register sets as a ring indexed by the unrolled position (the
