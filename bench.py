@@ -21,7 +21,8 @@ same run. Every GPU time is the median of 5 event-timed runs.
 
 Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
 tq_mixed_b, tq_fp8_values (the tq_mixed shape with FP8 keys and values),
-tq_mixed_b_d256 (3-bit centroid keys and values at D=256), write (65536
+tq_mixed_b_d256 (3-bit centroid keys and values at D=256), tq_mse4_u4 (the
+tq_mixed shape with 4-bit centroid keys and 4-bit values), write (65536
 tokens x 8 heads x 128 bf16), tq_write_a / tq_write_b (the TurboQuant slot
 writer on the same rows), fwht (1,048,576 rows), kpool (pooled-softmax key
 compression: 262144 pools of 4 tokens), prefill_int4 (multi-query INT4
@@ -211,7 +212,8 @@ def run_int4(args, torch, tq, W, name):
         decodes.append(tq.prepare_decode(q, bt, sl, num_kv_splits=S, key_cache=kc, value_cache=vc,
                                          k_scale_cache=ks, v_scale_cache=vs, rht_signs=signs,
                                          workspace=ws, out=out, lse=lse,
-                                         flags=tq.FLAG_WIDE if args.wide else 0)[0])
+                                         flags=(tq.FLAG_WIDE if args.wide else 0) |
+                                         (tq.FLAG_GENERIC if args.generic else 0))[0])
 
     def decode(i):
         decodes[i % ncopies].run(sp)
@@ -570,20 +572,25 @@ def run_other(args, torch, tq, W):
         q = torch.from_numpy(W.query(w, bf16_valued=True)).to(dev)
         bt = torch.from_numpy(w.block_table).to(dev)
         sl = torch.from_numpy(w.seq_lens).to(dev)
-        cen = torch.linspace(-0.2, 0.2, 1 << kb, device=dev) if fmt[0] != tq.KEY_FP8 else None
+        # an evenly spaced table, c[n - 1 - j] = -c[j] exactly (as in every
+        # Lloyd-Max table), made on the host
+        cen = torch.linspace(-0.2, 0.2, 1 << kb).to(dev) if fmt[0] != tq.KEY_FP8 else None
         ws = torch.empty(tq.tq_decode_workspace_bytes(w.B, w.hq, w.hk, w.d, w.num_splits) // 4,
                          dtype=torch.float32, device=dev)
         calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
                                    key_fmt=fmt[0], val_fmt=fmt[1], centroids=cen,
-                                   workspace=ws, flags=tq.FLAG_WIDE if args.wide else 0)[0]
+                                   workspace=ws,
+                                   flags=(tq.FLAG_WIDE if args.wide else 0) |
+                                   (tq.FLAG_GENERIC if args.generic else 0))[0]
                  for c in caches]
         t = _time_loop(torch, stream, lambda i: calls[i % ncopies].run(sp), args.warmup, args.steps)
         slot_used = kps + vdb + (0 if fmt[1] == tq.VAL_FP8 else 4)  # padding not counted
         kv = int(w.seq_lens.sum()) * w.hk * slot_used
         parts = w.B * w.hq * w.num_splits * (w.d + 1) * 8
         nbytes = kv + parts + w.B * w.hq * (8 * w.d + 4)
-        line = dict(workload="%s: B=16 Hq=32 Hk=4 D=%d seq 16384 S=32, %s keys + %s values" % (
-                        name, w.d, TQ_KEY_NAMES[fmt[0]], TQ_VAL_NAMES[fmt[1]]), us=t * 1e6,
+        line = dict(workload="%s: B=16 Hq=32 Hk=4 D=%d seq 16384 S=32, %s keys + %s values%s" % (
+                        name, w.d, TQ_KEY_NAMES[fmt[0]], TQ_VAL_NAMES[fmt[1]],
+                        ", generic kernel" if args.generic else ""), us=t * 1e6,
                     algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
     else:
@@ -599,6 +606,7 @@ TQ_DECODES = {
     "tq_mixed_b": (("KEY_MSE3", "VAL_U3"), 128),
     "tq_fp8_values": (("KEY_FP8", "VAL_FP8"), 128),
     "tq_mixed_b_d256": (("KEY_MSE3", "VAL_U3"), 256),
+    "tq_mse4_u4": (("KEY_MSE4", "VAL_U4"), 128),
 }
 TQ_KEY_NAMES = {1: "FP8", 2: "3-bit centroid", 3: "4-bit centroid"}
 TQ_VAL_NAMES = {1: "3-bit uniform", 2: "4-bit uniform", 3: "FP8"}
@@ -615,6 +623,8 @@ def main():
     ap.add_argument("--min-calls", type=int, default=MIN_TIMED_CALLS,
                     help="secondary workloads: least calls per timed run (fewer for counter runs)")
     ap.add_argument("--splits", type=int, default=0, help="override num_kv_splits (sweeps)")
+    ap.add_argument("--generic", action="store_true",
+                    help="decode workloads: force the generic (vector) kernel, for comparison")
     ap.add_argument("--wide", action="store_true",
                     help="decode through the 64-bit addressing variant (the one caches of "
                          "2 GiB and more take) whatever the cache size")
@@ -655,7 +665,8 @@ def main():
                                        w.name, w.B, w.hq, w.hk, w.d, w.block_size,
                                        "U[1024,8192]" if w.name == "llama8b_int4" else str(int(w.seq_lens[0])),
                                        int(w.seq_lens.sum()), w.num_splits)
-                                   + (", 64-bit addressing variant" if args.wide else ""),
+                                   + (", 64-bit addressing variant" if args.wide else "")
+                                   + (", generic kernel" if args.generic else ""),
                        "global_batch": w.B, "seq_len": int(w.seq_lens.max()), "parallelism": "1 GPU"},
             "decode_us": round(res["t_dec"] * 1e6, 2),
             "decode_us_min_max": [round(res["t_dec_range"][0] * 1e6, 2),

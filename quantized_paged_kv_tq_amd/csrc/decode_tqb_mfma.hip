@@ -1,15 +1,15 @@
 // TurboQuant split-KV decode, stage 1, on the CDNA4 matrix cores, for
-// 3-bit Lloyd-Max centroid keys with 3-bit uniform values
+// 3- or 4-bit Lloyd-Max centroid keys with 3- or 4-bit uniform values
 // (triton_turboquant_decode.py, _tq_decode_stage1: score = sm_scale *
 // norm16 * (q_rot . c[idx]); v = idx * scale16 + zero16; online softmax;
 // partials acc / l and m + ln l).
 //
-// Scores. A key's 3-bit index idx = b0 + 2 b1 + 4 b2 picks c[idx]; as a
-// function of its bits, c is the multilinear polynomial
+// Scores. A key's KB-bit index idx = b0 + 2 b1 + 4 b2 (+ 8 b3) picks c[idx];
+// as a function of its bits, c is the multilinear polynomial
 //   c(b) = sum over S of alpha_S * prod_{i in S} b_i   (S a subset of bits),
 // alpha the Moebius transform of the table. So
 //   q_rot . c[idx] = alpha_0 * sum(q_rot) + sum_{S != 0} alpha_S * (q_rot . P_S)
-// with P_S the 0/1 vector of the product of the bits in S. The seven dot
+// with P_S the 0/1 vector of the product of the bits in S. The 2^KB - 1 dot
 // products with 0/1 vectors run as v_mfma_i32_16x16x64_i8 on exact
 // integers: the rotated query is scaled by 2^E to integers below 2^27 and
 // split into four balanced base-128 digits (the A operand, as in the INT4
@@ -29,9 +29,16 @@
 // is done once per kv head instead of by two waves; that wave needs more
 // than 256 registers and runs alone on its SIMD.
 //
-// Slot layout (D = 128): bytes [0, 48) key indices (LSB-first 3-bit
-// stream), [48, 50) fp16 norm, [50, 98) value indices, [98, 100) fp16
-// scale, [100, 102) fp16 zero.
+// A table with c[2^KB - 1 - j] = -c[j] (Lloyd-Max tables are) has only odd
+// Walsh terms: 4 bit planes for KB = 3 (b0, b1, b2, b0^b1^b2), 8 for KB = 4
+// (the four bits and the four parities of three of them).
+//
+// Slot layout (D = 128): bytes [0, 16 KB) key indices (LSB-first KB-bit
+// stream), then the fp16 norm, 16 VB bytes of value indices (LSB-first),
+// the fp16 scale and the fp16 zero. A lane's 4-bit keys stay packed: its
+// bit planes are read from the nibbles of each byte, even dimensions from
+// the low nibbles and odd ones from the high nibbles, and the query image
+// takes the same dimension order.
 #include <type_traits>
 
 #include "balance.h"
@@ -65,8 +72,15 @@ constexpr int kZeroBytes = 65536;
 __device__ __attribute__((aligned(256))) uint8_t g_zero_page[kZeroBytes];
 constexpr int kFirstOfSplit = 1;
 constexpr int kLastOfSplit = 2;
-// slot offsets
-constexpr uint32_t kNormOff = 48, kValOff = 50, kScaleOff = 96;  // scale word pair at 96
+// slot offsets for KB-bit keys and VB-bit values: norm, value indices,
+// and the 8-byte word pair at kScaleOff whose bytes 2..3 are the scale and
+// 4..5 the zero
+template <int KB, int VB>
+struct SlotLayout {
+  static constexpr uint32_t kNormOff = 16 * KB;
+  static constexpr uint32_t kValOff = 16 * KB + 2;
+  static constexpr uint32_t kScaleOff = 16 * (KB + VB);
+};
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -99,6 +113,11 @@ __device__ __forceinline__ uint32_t unpack3x4(uint32_t x) {
   const uint32_t y = ((x & 0xFC0u) << 10) | (x & 0x3Fu);  // fields 2, 3 to bits 16..21
   return (y | (y << 5)) & 0x07070707u;                      // fields 1, 3 to bytes 1, 3
 }
+// nibbles 4h .. 4h+3 of x -> four bytes
+__device__ __forceinline__ uint32_t unpack4x4(uint32_t x, int h) {
+  const uint32_t t = __builtin_amdgcn_perm(x, x, h ? 0x03030202u : 0x01010000u);
+  return ((t >> 4) & 0x0F000F00u) | (t & 0x000F000Fu);
+}
 // bits [bit, bit + 12) of the 96-bit little-endian value w
 __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
   const int word = bit >> 5, sh = bit & 31;
@@ -110,9 +129,12 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
 // operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH, bool WIDE>
+template <int W, int NH, bool WIDE, int KB, int VB>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
+  using L = SlotLayout<KB, VB>;
+  constexpr uint32_t kNormOff = L::kNormOff, kValOff = L::kValOff, kScaleOff = L::kScaleOff;
+  constexpr int NC = 1 << KB;  // centroids
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
   __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
@@ -143,32 +165,32 @@ void decode_tqb_kernel(DecodeParams p) {
   const int h0 = kvh * g + hq0;
 
   // Coefficients of the centroid table (uniform), for the index bits
-  // b = (b0, b1, b2) as the subset mask S in 0..7:
+  // b = (b0, .., b_{KB-1}) as the subset mask S in 0..NC-1:
   //   al: multilinear (Moebius) form c(b) = sum_S al_S prod_{i in S} b_i;
   //   ga: Walsh form c(b) = sum_S ga_S (-1)^{popcount(b & S)}.
-  // A table with c[7 - j] = -c[j] (Lloyd-Max tables are) has ga_S = 0 for
-  // every even |S|; then only the planes b0, b1, b2 and b0^b1^b2 are needed:
+  // A table with c[NC - 1 - j] = -c[j] (Lloyd-Max tables are) has ga_S = 0
+  // for every even |S|; then only the planes of odd |S| are needed:
   //   q . c[idx] = sum_S ga_S (sum q - 2 q . [popcount(b & S) odd]).
-  float al[8], ga[8];
+  float al[NC], ga[NC];
   bool anti = true;
   {
-    float c[8];
+    float c[NC];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = p.centroids[j];
+    for (int j = 0; j < NC; ++j) c[j] = p.centroids[j];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) anti = anti && (c[7 - j] == -c[j]);
+    for (int j = 0; j < NC; ++j) anti = anti && (c[NC - 1 - j] == -c[j]);
 #pragma unroll
-    for (int S = 0; S < 8; ++S) {
+    for (int S = 0; S < NC; ++S) {
       float a = 0.0f, w = 0.0f;
 #pragma unroll
-      for (int T = 0; T < 8; ++T) {
+      for (int T = 0; T < NC; ++T) {
         w = (__builtin_popcount(T & S) & 1) ? w - c[T] : w + c[T];
         if ((T & S) != T) continue;
         const int sign = __builtin_popcount(S ^ T) & 1;
         a = sign ? a - c[T] : a + c[T];
       }
       al[S] = a;
-      ga[S] = w * 0.125f;
+      ga[S] = w * (1.0f / NC);
     }
   }
 
@@ -204,17 +226,17 @@ void decode_tqb_kernel(DecodeParams p) {
     if constexpr (WIDE) return o == (Off)zoff;
     else return o >= kMaskedByte;
   };
-  // this lane's 3 value bytes (dims 8n .. 8n+7) start at byte kValOff + 3n;
-  // one dword load from that byte offset (buffer loads take byte offsets,
-  // dword loads need not be 4-byte aligned)
-  const uint32_t vbyte = kValOff + 3u * (uint32_t)ln;
+  // this lane's VB value bytes (dims 8n .. 8n+7) start at byte kValOff +
+  // VB n; one dword load from that byte offset (buffer loads take byte
+  // offsets, dword loads need not be 4-byte aligned)
+  const uint32_t vbyte = kValOff + (uint32_t)VB * (uint32_t)ln;
 
   // ---- registers of one tile ----
-  // key bytes [12g, 12g + 12) of tokens 16s + n (dims 32g .. 32g+31); the
-  // norm word and scale/zero words of token `lane`; the dword starting at
-  // value byte 3n of tokens 16s + 4g + k
+  // key bytes [4 KB g, 4 KB (g + 1)) of tokens 16s + n (dims 32g ..
+  // 32g+31); the norm word and scale/zero words of token `lane`; the dword
+  // starting at value byte VB n of tokens 16s + 4g + k
   struct Buf {
-    uint32_t kraw[4][3];
+    uint32_t kraw[4][KB];
     uint32_t nw, sz0, sz1, live;
     uint32_t vraw[4][4];
   };
@@ -239,9 +261,17 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int s = 0; s < 4; ++s) {
       const Off o = slot_of(k, 16 * s + ln);
       B.live |= (masked(o) ? 0u : 1u) << s;
+      if constexpr (KB == 4) {
+        const v4u kw = ld128(o + 16u * lg);
+        B.kraw[s][0] = kw.x;
+        B.kraw[s][1] = kw.y;
+        B.kraw[s][2] = kw.z;
+        B.kraw[s][3] = kw.w;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 3; ++i)
-        B.kraw[s][i] = ld32(o + 12u * lg + 4u * i);
+        for (int i = 0; i < 3; ++i)
+          B.kraw[s][i] = ld32(o + 12u * lg + 4u * i);
+      }
     }
     {
       const Off o = slot_of(k, lane);
@@ -306,7 +336,9 @@ void decode_tqb_kernel(DecodeParams p) {
   // q' = FWHT(rot_signs * q) (two dims per lane), scaled by 2^E to integers
   // below 2^27 and split into four balanced base-128 digits; the image for
   // MFMA chunk kc: lane (m = 4h' + piece, g), dword j, byte bb holds the
-  // digit of dim 32g + 16kc + 4j + bb -- the byte order of the bit planes.
+  // digit of dim 32g + 16kc + 4j + bb (KB = 3), or of dim 32g + 16kc +
+  // 8(j/2) + 2bb + (j%2) (KB = 4: low, then high nibbles of each dword) --
+  // the byte order of the bit planes.
   v4i qa[NH][2];
   float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
   // the wave's query rows of sequence b times the rotation signs (lane:
@@ -350,7 +382,9 @@ void decode_tqb_kernel(DecodeParams p) {
         const int dim = lane + 64 * e;
         int v = (int)__builtin_rintf((e ? x1 : x0) * sc);
         const int gg = dim >> 5, o = dim & 31;
-        const int kc = o >> 4, j = (o & 15) >> 2, bb = o & 3;
+        const int kc = o >> 4;
+        const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
+        const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
 #pragma unroll
         for (int pc = 0; pc < 4; ++pc) {
           const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
@@ -440,15 +474,21 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
-      // index bytes of dims 32g + 4i .. +3
-      uint32_t ix[8];
+      // KB = 3: index bytes of dims 32g + 4i .. +3 (KB = 4 reads the planes
+      // from the packed nibbles)
+      uint32_t ix[KB == 3 ? 8 : 1];
+      if constexpr (KB == 3) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
+        for (int i = 0; i < 8; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
+      }
       // one bit plane at a time: two MFMAs (dims 32g + 16kc + ...), then its
       // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
       // digit planes of head g, token 16s+n
       auto plane_dot = [&](auto sel, float (&out)[NH]) {
-        constexpr int S = decltype(sel)::value;  // 1..7: product; 8 + S: parity
+        // the subset S of index bits (low bits); + 32: parity, else product
+        constexpr int SS = decltype(sel)::value;
+        constexpr bool PAR = SS >= 32;
+        constexpr int S = SS & 31;
         v4i c[NH];
 #pragma unroll
         for (int r = 0; r < NH; ++r) c[r] = v4i{0, 0, 0, 0};
@@ -457,21 +497,19 @@ void decode_tqb_kernel(DecodeParams p) {
           uint32_t pl[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t x = ix[4 * kc + j];
-            uint32_t m;
-            if constexpr (S < 8) {
-              m = 0x01010101u;
-              if (S & 1) m &= x;
-              if (S & 2) m &= x >> 1;
-              if (S & 4) m &= x >> 2;
-            } else {
-              m = 0;
-              if (S & 1) m ^= x;
-              if (S & 2) m ^= x >> 1;
-              if (S & 4) m ^= x >> 2;
-              m &= 0x01010101u;
+            // bit k of each byte (KB = 3) or of each nibble (KB = 4) of x
+            // is index bit k of one dimension
+            uint32_t x;
+            if constexpr (KB == 4) x = X.kraw[s][2 * kc + (j >> 1)];
+            else x = ix[4 * kc + j];
+            uint32_t m = PAR ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+              if (!((S >> k) & 1)) continue;
+              if constexpr (PAR) m ^= x >> k;
+              else m &= x >> k;
             }
-            pl[j] = m;
+            pl[j] = ((KB == 4 && (j & 1)) ? m >> 4 : m) & 0x01010101u;
           }
           const v4i bpl = v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
 #pragma unroll
@@ -483,26 +521,38 @@ void decode_tqb_kernel(DecodeParams p) {
                                                  (float)c[r].y), 128.0f, (float)c[r].x);
       };
       float dot[NH];
+      float t[NH];
       if (anti) {
-        // odd Walsh terms: planes b0, b1, b2, b0^b1^b2
-        float t1[NH], t2[NH], t4[NH], t7[NH];
-        plane_dot(std::integral_constant<int, 9>{}, t1);
-        plane_dot(std::integral_constant<int, 10>{}, t2);
-        plane_dot(std::integral_constant<int, 12>{}, t4);
-        plane_dot(std::integral_constant<int, 15>{}, t7);
+        // odd Walsh terms: the single bits and (KB = 3) b0^b1^b2 or (KB = 4)
+        // the four parities of three bits
+        float tw[NH];
+        float gs = 0.0f;
 #pragma unroll
-        for (int r = 0; r < NH; ++r) {
-          const float t = t1[r] * ga[1] + t2[r] * ga[2] + t4[r] * ga[4] + t7[r] * ga[7];
-          dot[r] = __builtin_fmaf(ga[1] + ga[2] + ga[4] + ga[7], qsum[r], -2.0f * t);
+        for (int r = 0; r < NH; ++r) tw[r] = 0.0f;
+#define TQK_WALSH(S)                                                               \
+        plane_dot(std::integral_constant<int, 32 + S>{}, t);                       \
+        gs += ga[S];                                                               \
+        for (int r = 0; r < NH; ++r) tw[r] = __builtin_fmaf(ga[S], t[r], tw[r]);
+        TQK_WALSH(1) TQK_WALSH(2) TQK_WALSH(4)
+        if constexpr (KB == 3) {
+          TQK_WALSH(7)
+        } else {
+          TQK_WALSH(8) TQK_WALSH(7) TQK_WALSH(11) TQK_WALSH(13) TQK_WALSH(14)
         }
+#undef TQK_WALSH
+#pragma unroll
+        for (int r = 0; r < NH; ++r) dot[r] = __builtin_fmaf(gs, qsum[r], -2.0f * tw[r]);
       } else {
-        float t[NH];
 #pragma unroll
         for (int r = 0; r < NH; ++r) dot[r] = al[0] * qsum[r];
 #define TQK_PLANE(S)                                                         \
         plane_dot(std::integral_constant<int, S>{}, t);                      \
         for (int r = 0; r < NH; ++r) dot[r] = __builtin_fmaf(al[S], t[r], dot[r]);
         TQK_PLANE(1) TQK_PLANE(2) TQK_PLANE(3) TQK_PLANE(4) TQK_PLANE(5) TQK_PLANE(6) TQK_PLANE(7)
+        if constexpr (KB == 4) {
+          TQK_PLANE(8) TQK_PLANE(9) TQK_PLANE(10) TQK_PLANE(11) TQK_PLANE(12) TQK_PLANE(13)
+          TQK_PLANE(14) TQK_PLANE(15)
+        }
 #undef TQK_PLANE
       }
       const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
@@ -612,7 +662,8 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t x = X.vraw[s][kk];
-          u[s] = unpack3x4(h ? x >> 12 : x);
+          if constexpr (VB == 4) u[s] = unpack4x4(x, h);
+          else u[s] = unpack3x4(h ? x >> 12 : x);
         }
         const uint32_t t01l = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
         const uint32_t t01h = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);
@@ -711,14 +762,14 @@ void decode_tqb_kernel(DecodeParams p) {
   emit();
 }
 
-template <int W, int NH>
+template <int W, int NH, int KB, int VB>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
   if (wide)
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true, KB, VB>), dim3(blocks), dim3(64 * W), lds, st, p);
   else
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -726,12 +777,42 @@ hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
 // tile's keys and values are unpacked once instead of by two waves.
 constexpr bool kOneWavePerKvHead = true;
 
+template <int KB, int VB>
+hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
+  if (p.g > 4 && kOneWavePerKvHead) {
+    // one wave per kv head at one wave per SIMD: at most 4 waves per
+    // workgroup and per CU (the piece region, sized for two waves per kv
+    // head at 8 per CU, holds the same number of workgroups)
+    p.wgh = balance_heads_per_wg(p.hk, 4, 4);
+    const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh) {
+      case 1: return launch<1, 2, KB, VB>(p, st, wide);
+      case 2: return launch<2, 2, KB, VB>(p, st, wide);
+      default: return launch<4, 2, KB, VB>(p, st, wide);
+    }
+  }
+  const int qs = (p.g + 3) / 4;
+  p.wgh = balance_heads_per_wg(p.hk, p.g);
+  const int64_t nw = balance_max_wgs(p.hk, p.g);
+  p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+  switch (p.wgh * qs) {
+    case 1: return launch<1, 1, KB, VB>(p, st, wide);
+    case 2: return launch<2, 1, KB, VB>(p, st, wide);
+    case 4: return launch<4, 1, KB, VB>(p, st, wide);
+    default: return launch<8, 1, KB, VB>(p, st, wide);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
-  if (p.d != D || p.key_fmt != KF_MSE3 || p.val_fmt != VF_U3 || p.g > 8 || p.norm_correction)
+  const bool k4 = p.key_fmt == KF_MSE4, v4 = p.val_fmt == VF_U4;
+  if (p.d != D || (p.key_fmt != KF_MSE3 && !k4) || (p.val_fmt != VF_U3 && !v4) || p.g > 8 ||
+      p.norm_correction)
     return hipErrorNotSupported;
-  if (p.kps != (int)kValOff || p.vdb != 48 || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
+  const int kb = k4 ? 4 : 3, vb = v4 ? 4 : 3;
+  if (p.kps != 16 * kb + 2 || p.vdb != 16 * vb || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
   // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
   // 64-bit variant (whose zero page must cover every kv head's slot)
   const bool wide = p.force_wide ||
@@ -741,29 +822,8 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
   const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
   if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
-  if (p.g > 4 && kOneWavePerKvHead) {
-    // one wave per kv head at one wave per SIMD: at most 4 waves per
-    // workgroup and per CU (the piece region, sized for two waves per kv
-    // head at 8 per CU, holds the same number of workgroups)
-    p.wgh = balance_heads_per_wg(p.hk, 4, 4);
-    const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
-    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
-    switch (p.wgh) {
-      case 1: return launch<1, 2>(p, st, wide);
-      case 2: return launch<2, 2>(p, st, wide);
-      default: return launch<4, 2>(p, st, wide);
-    }
-  }
-  const int qs = (p.g + 3) / 4;
-  p.wgh = balance_heads_per_wg(p.hk, p.g);
-  const int64_t nw = balance_max_wgs(p.hk, p.g);
-  p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
-  switch (p.wgh * qs) {
-    case 1: return launch<1, 1>(p, st, wide);
-    case 2: return launch<2, 1>(p, st, wide);
-    case 4: return launch<4, 1>(p, st, wide);
-    default: return launch<8, 1>(p, st, wide);
-  }
+  if (k4) return v4 ? launch_bits<4, 4>(p, st, wide, tiles_ub) : launch_bits<4, 3>(p, st, wide, tiles_ub);
+  return v4 ? launch_bits<3, 4>(p, st, wide, tiles_ub) : launch_bits<3, 3>(p, st, wide, tiles_ub);
 }
 
 }  // namespace tqk

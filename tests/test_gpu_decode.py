@@ -401,6 +401,103 @@ def test_tq_fp8_u4_query_groups_of_five_to_eight(hq, hk):
 
 
 
+# 4-bit centroid keys and 4-bit values on the same matrix-core kernel
+# (D = 128, g <= 8): every combination of 3- and 4-bit keys and values
+
+C_FMTS = [(oracle.KEY_MSE4, oracle.VAL_U4), (oracle.KEY_MSE3, oracle.VAL_U4),
+          (oracle.KEY_MSE4, oracle.VAL_U3)]
+
+
+def _random_table(seed, n, antisymmetric=False):
+    """A sorted random table of n centroids; ``antisymmetric`` mirrors its
+    upper half so that c[n - 1 - j] == -c[j] holds exactly."""
+    rng = np.random.default_rng(seed)
+    c = np.sort(rng.uniform(-0.3, 0.3, n)).astype(np.float32)
+    if antisymmetric:
+        c[:n // 2] = -c[n // 2:][::-1]
+    return c
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
+@pytest.mark.parametrize("fmt", C_FMTS, ids=["mse4_u4", "mse3_u4", "mse4_u3"])
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=[str(i) for i in range(5)])
+def test_tq_centroid_bits_shapes(shape, fmt, flags):
+    """Oracle-encoded caches (Lloyd-Max tables) on the shapes of the other
+    formats: GQA 1 .. 16, block sizes 16 and 64, split counts 3 .. 16."""
+    B, hq, hk, d, bs, seq, S = shape
+    w = W.custom_decode_workload(900 + len(seq) * 7 + hq + 3 * fmt[0] + fmt[1], B, hq, hk, d, bs, S,
+                                 seq, 5, "bf16")
+    cache, cen = tq_case(w, *fmt)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, flags=flags)
+    assert_close(got, ref, lse, ref_lse, "%s %s" % (shape, fmt))
+
+
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("fmt", C_FMTS, ids=["mse4_u4", "mse3_u4", "mse4_u3"])
+def test_tq_centroid_bits_random_slots_and_table(fmt, antisymmetric):
+    """Random slots (no writer): every index pattern, value scales of both
+    signs, random norms and zeros, and an arbitrary centroid table, in the
+    general (Moebius) and the antisymmetric (Walsh) score forms."""
+    w = W.custom_decode_workload(910 + 3 * fmt[0] + fmt[1], 2, 16, 4, 128, 16, 4, [300, 77], 4, "bf16")
+    cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(128, *fmt))
+    n = 16 if fmt[0] == oracle.KEY_MSE4 else 8
+    cen = _random_table(911 + fmt[1], n, antisymmetric)
+    assert np.array_equal(cen[::-1] == -cen, np.full(n, antisymmetric))
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    for flags in (0, tq.FLAG_GENERIC, tq.FLAG_WIDE):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "random slots %s flags=%d" % (fmt, flags))
+
+
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("hq,hk", [(10, 2), (16, 2), (32, 4)], ids=["g5", "g8", "g8x4"])
+def test_tq_mse4_u4_query_groups_of_five_to_eight(hq, hk, antisymmetric):
+    """4-bit keys and values at g = 5 .. 8 (one wave per kv head, two MFMA
+    row sets); random slots, empty and one-token sequences, split and range
+    boundaries."""
+    fmt = (oracle.KEY_MSE4, oracle.VAL_U4)
+    seq = [0, 1, 300, 777, 65, 2000]
+    w = W.custom_decode_workload(920 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
+    cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(128, *fmt))
+    cen = _random_table(920 + hq, 16, antisymmetric)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    for flags in (0, tq.FLAG_WIDE):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "hq=%d hk=%d" % (hq, hk))
+
+
+def test_tq_mse4_u4_rot_signs_split_invariance_and_degenerate_lengths():
+    fmt = (oracle.KEY_MSE4, oracle.VAL_U4)
+    w = W.custom_decode_workload(930, 3, 8, 2, 128, 16, 4, [37, 1, 100], 2, "bf16")
+    rs = W.rht_signs(128, round_idx=5)
+    cache, cen = tq_case(w, *fmt, rot_signs=rs)
+    q = W.query(w)
+    seq = np.array([37, 0, 100], np.int32)
+    ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, seq, cen, rs, *fmt, 0, 0, w.sm_scale)
+    for S in (1, 2, 8, 37, 64, 100, 105, 256):
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, rot_signs=rs, num_splits=S, seq_lens=seq)
+        assert_close(got, ref, lse, ref_lse, "S=%d" % S)
+        assert np.all(got[8:16] == 0) and np.all(np.isneginf(lse[8:16]))
+
+
+def test_tq_mse4_u4_balanced_many_sequences():
+    fmt = (oracle.KEY_MSE4, oracle.VAL_U4)
+    rng = np.random.default_rng(940)
+    seq = rng.choice([0, 1, 5, 63, 64, 65, 130, 200, 777], size=600).astype(np.int32)
+    w = W.custom_decode_workload(940, 600, 8, 2, 128, 16, 3, seq, 7, "bf16")
+    cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(128, *fmt))
+    cen = _random_table(940, 16, True)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *fmt)
+    assert_close(got, ref, lse, ref_lse, "600 sequences")
+
+
 # ---------------------------------------------------------------------------
 # Read-side variants on the generic kernel: FP8 values, D = 256
 
