@@ -27,14 +27,17 @@
 // wave serves all query heads of its kv head (two MFMA row sets), so the
 // unpacking of each tile's 3-bit keys and values, which bounds this kernel,
 // is done once per kv head instead of by two waves; that wave needs more
-// than 256 registers and runs alone on its SIMD.
+// than 256 registers and runs alone on its SIMD. D = 256 doubles a lane's
+// key and value dims (64 key and 16 value dims per lane, 4 score MFMAs per
+// plane, 16 PV MFMAs); its waves serve four query heads each and run alone
+// on their SIMD.
 //
 // A table with c[2^KB - 1 - j] = -c[j] (Lloyd-Max tables are) has only odd
 // Walsh terms: 4 bit planes for KB = 3 (b0, b1, b2, b0^b1^b2), 8 for KB = 4
 // (the four bits and the four parities of three of them).
 //
-// Slot layout (D = 128): bytes [0, 16 KB) key indices (LSB-first KB-bit
-// stream), then the fp16 norm, 16 VB bytes of value indices (LSB-first),
+// Slot layout: bytes [0, D KB / 8) key indices (LSB-first KB-bit stream),
+// then the fp16 norm, D VB / 8 bytes of value indices (LSB-first),
 // the fp16 scale and the fp16 zero. A lane's 4-bit keys stay packed: its
 // bit planes are read from the nibbles of each byte, even dimensions from
 // the low nibbles and odd ones from the high nibbles, and the query image
@@ -53,7 +56,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int D = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kChunk = 64;  // tiles resolved into LDS at a time
@@ -75,11 +77,11 @@ constexpr int kLastOfSplit = 2;
 // slot offsets for KB-bit keys and VB-bit values: norm, value indices,
 // and the 8-byte word pair at kScaleOff whose bytes 2..3 are the scale and
 // 4..5 the zero
-template <int KB, int VB>
+template <int KB, int VB, int DD>
 struct SlotLayout {
-  static constexpr uint32_t kNormOff = 16 * KB;
-  static constexpr uint32_t kValOff = 16 * KB + 2;
-  static constexpr uint32_t kScaleOff = 16 * (KB + VB);
+  static constexpr uint32_t kNormOff = DD * KB / 8;
+  static constexpr uint32_t kValOff = DD * KB / 8 + 2;
+  static constexpr uint32_t kScaleOff = DD * (KB + VB) / 8;
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -118,8 +120,9 @@ __device__ __forceinline__ uint32_t unpack4x4(uint32_t x, int h) {
   const uint32_t t = __builtin_amdgcn_perm(x, x, h ? 0x03030202u : 0x01010000u);
   return ((t >> 4) & 0x0F000F00u) | (t & 0x000F000Fu);
 }
-// bits [bit, bit + 12) of the 96-bit little-endian value w
-__device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
+// bits [bit, bit + 12) of the little-endian value w
+template <int N>
+__device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[N], int bit) {
   const int word = bit >> 5, sh = bit & 31;
   if (sh <= 20) return w[word] >> sh;
   return __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)sh);
@@ -129,23 +132,25 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[3], int bit) {
 // operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH, bool WIDE, int KB, int VB>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+template <int W, int NH, bool WIDE, int KB, int VB, int DD>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 && DD == 128 ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
-  using L = SlotLayout<KB, VB>;
+  constexpr int D = DD;      // head dim, 128 or 256
+  constexpr int F = D / 128;  // a lane's dims per 16-lane group and token: 32 F keys, 8 F values
+  using L = SlotLayout<KB, VB, DD>;
   constexpr uint32_t kNormOff = L::kNormOff, kValOff = L::kValOff, kScaleOff = L::kScaleOff;
   constexpr int NC = 1 << KB;  // centroids
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
   __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
-  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2][64][4];  // query digit image
+  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2 * F][64][4];  // query digit image
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
   using Off = typename std::conditional<WIDE, int64_t, uint32_t>::type;
   __shared__ __attribute__((aligned(16))) Off tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
-  __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
+  __shared__ float accl[W][NH * 8 * F][64];  // fp32 value accumulators, lane-major
   extern __shared__ int prefix[];  // [B + 1] tile prefix sums, then [B] lengths
 
   const int tid = threadIdx.x;
@@ -226,19 +231,20 @@ void decode_tqb_kernel(DecodeParams p) {
     if constexpr (WIDE) return o == (Off)zoff;
     else return o >= kMaskedByte;
   };
-  // this lane's VB value bytes (dims 8n .. 8n+7) start at byte kValOff +
-  // VB n; one dword load from that byte offset (buffer loads take byte
-  // offsets, dword loads need not be 4-byte aligned)
-  const uint32_t vbyte = kValOff + (uint32_t)VB * (uint32_t)ln;
+  // this lane's value bytes (dims 8F n .. 8F n + 8F - 1) start at byte
+  // kValOff + VB F n; one dword load per 8 dims from byte kValOff + VB F n +
+  // VB f (buffer loads take byte offsets, dword loads need not be 4-byte
+  // aligned)
+  const uint32_t vbyte = kValOff + (uint32_t)(VB * F) * (uint32_t)ln;
 
   // ---- registers of one tile ----
-  // key bytes [4 KB g, 4 KB (g + 1)) of tokens 16s + n (dims 32g ..
-  // 32g+31); the norm word and scale/zero words of token `lane`; the dword
-  // starting at value byte VB n of tokens 16s + 4g + k
+  // key bytes [4 KB F g, 4 KB F (g + 1)) of tokens 16s + n (dims 32F g ..
+  // 32F g + 32F - 1); the norm word and scale/zero words of token `lane`;
+  // the dwords starting at value bytes VB F n + VB f of tokens 16s + 4g + k
   struct Buf {
-    uint32_t kraw[4][KB];
+    uint32_t kraw[4][KB * F];
     uint32_t nw, sz0, sz1, live;
-    uint32_t vraw[4][4];
+    uint32_t vraw[4][4][F];
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
   auto slot_of = [&](int k, int j) -> Off { return WIDE ? tok_rows[k][j] : tok_rows[k][j] + kvh_off; };
@@ -251,7 +257,8 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const Off o = slot_of(k, 16 * s + 4 * lg + kk);
-        B.vraw[s][kk] = ld32(o + vbyte);
+#pragma unroll
+        for (int f = 0; f < F; ++f) B.vraw[s][kk][f] = ld32(o + vbyte + (uint32_t)(VB * f));
       }
     }
   };
@@ -262,15 +269,18 @@ void decode_tqb_kernel(DecodeParams p) {
       const Off o = slot_of(k, 16 * s + ln);
       B.live |= (masked(o) ? 0u : 1u) << s;
       if constexpr (KB == 4) {
-        const v4u kw = ld128(o + 16u * lg);
-        B.kraw[s][0] = kw.x;
-        B.kraw[s][1] = kw.y;
-        B.kraw[s][2] = kw.z;
-        B.kraw[s][3] = kw.w;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const v4u kw = ld128(o + (uint32_t)(16 * F) * lg + 16u * f);
+          B.kraw[s][4 * f + 0] = kw.x;
+          B.kraw[s][4 * f + 1] = kw.y;
+          B.kraw[s][4 * f + 2] = kw.z;
+          B.kraw[s][4 * f + 3] = kw.w;
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-          B.kraw[s][i] = ld32(o + 12u * lg + 4u * i);
+        for (int i = 0; i < 3 * F; ++i)
+          B.kraw[s][i] = ld32(o + (uint32_t)(12 * F) * lg + 4u * i);
       }
     }
     {
@@ -284,8 +294,8 @@ void decode_tqb_kernel(DecodeParams p) {
 
   // ---- online softmax state of the current segment ----
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
-  float(*acc)[64] = accl[wave];       // acc[8r + i][lane]
-  v4i cacc[NH][8];
+  float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
+  v4i cacc[NH][8 * F];
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
@@ -297,8 +307,8 @@ void decode_tqb_kernel(DecodeParams p) {
       l[r] = 0.0f;
       zacc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[8 * r + i][lane] = 0.0f;
+      for (int i = 0; i < 8 * F; ++i) {
+        acc[8 * F * r + i][lane] = 0.0f;
         cacc[r][i] = v4i{0, 0, 0, 0};
       }
     }
@@ -308,23 +318,23 @@ void decode_tqb_kernel(DecodeParams p) {
     since_flush = 0;
   };
   // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
-  // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
+  // by alpha (lane (n, g) holds head g's dims 8F n .. 8F n + 8F - 1)
   auto flush = [&](const float (&alpha)[NH]) {
     const float pinv = exp2i(-ev);
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       if (!empty) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8 * F; ++i) {
           const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
           const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
           const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-          acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
+          acc[8 * F * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * F * r + i][lane]) * alpha[r];
           cacc[r][i] = v4i{0, 0, 0, 0};
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[8 * r + i][lane] *= alpha[r];
+        for (int i = 0; i < 8 * F; ++i) acc[8 * F * r + i][lane] *= alpha[r];
       }
       l[r] *= alpha[r];
       zacc[r] *= alpha[r];
@@ -333,55 +343,68 @@ void decode_tqb_kernel(DecodeParams p) {
   };
 
   // ---------------- query of sequence b ----------------
-  // q' = FWHT(rot_signs * q) (two dims per lane), scaled by 2^E to integers
-  // below 2^27 and split into four balanced base-128 digits; the image for
-  // MFMA chunk kc: lane (m = 4h' + piece, g), dword j, byte bb holds the
-  // digit of dim 32g + 16kc + 4j + bb (KB = 3), or of dim 32g + 16kc +
-  // 8(j/2) + 2bb + (j%2) (KB = 4: low, then high nibbles of each dword) --
-  // the byte order of the bit planes.
-  v4i qa[NH][2];
+  // q' = FWHT(rot_signs * q) (2F dims per lane: lane + 64e), scaled by 2^E
+  // to integers below 2^27 and split into four balanced base-128 digits;
+  // the image for MFMA chunk kc (2F chunks of 64 dims): lane (m = 4h' +
+  // piece, g), dword j, byte bb holds the digit of dim 32F g + 16kc + 4j +
+  // bb (KB = 3), or of dim 32F g + 16kc + 8(j/2) + 2bb + (j%2) (KB = 4: low,
+  // then high nibbles of each dword) -- the byte order of the bit planes.
+  v4i qa[NH][2 * F];
   float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
-  // the wave's query rows of sequence b times the rotation signs (lane:
-  // dims lane and lane + 64)
-  auto query_rows = [&](int b, float (&qx)[NHEAD][2]) {
-    const float s0 = p.rot_signs ? p.rot_signs[lane] : 1.0f;
-    const float s1 = p.rot_signs ? p.rot_signs[lane + 64] : 1.0f;
+  // the wave's query rows of sequence b times the rotation signs
+  auto query_rows = [&](int b, float (&qx)[NHEAD][2 * F]) {
+    float sg[2 * F];
+#pragma unroll
+    for (int e = 0; e < 2 * F; ++e) sg[e] = p.rot_signs ? p.rot_signs[lane + 64 * e] : 1.0f;
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
       const bool ok = hh < gw;
       const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (ok ? hh : 0)) * D;
-      qx[hh][0] = ok ? qrow[lane] * s0 : 0.0f;
-      qx[hh][1] = ok ? qrow[lane + 64] * s1 : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 2 * F; ++e) qx[hh][e] = ok ? qrow[lane + 64 * e] * sg[e] : 0.0f;
     }
   };
   // rotate, scale and split the rows into the MFMA A-operand image
-  auto query_image = [&](const float (&qx)[NHEAD][2]) {
+  auto query_image = [&](const float (&qx)[NHEAD][2 * F]) {
     uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0][0]);
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
       const int r = hh >> 2, hp = hh & 3;
-      float x0 = qx[hh][0], x1 = qx[hh][1];
-      {
-        const float a = x0 + x1, c = x0 - x1;
-        x0 = a;
-        x1 = c;
+      float x[2 * F];
+#pragma unroll
+      for (int e = 0; e < 2 * F; ++e) x[e] = qx[hh][e];
+      // strides 64 (and 128) inside the lane, then 1 .. 32 across lanes
+#pragma unroll
+      for (int st = 1; st < 2 * F; st <<= 1)
+#pragma unroll
+        for (int e = 0; e < 2 * F; ++e)
+          if (!(e & st)) {
+            const float a = x[e] + x[e + st], c = x[e] - x[e + st];
+            x[e] = a;
+            x[e + st] = c;
+          }
+#pragma unroll
+      for (int e = 0; e < 2 * F; ++e) {
+        x[e] = butterfly_lanes<1>(x[e], lane & 1);
+        x[e] = butterfly_lanes<2>(x[e], lane & 2);
+        x[e] = butterfly_lanes<4>(x[e], lane & 4);
+        x[e] = butterfly_lanes<8>(x[e], lane & 8);
+        x[e] = butterfly_lanes<16>(x[e], lane & 16);
+        x[e] = butterfly_lanes<32>(x[e], lane & 32);
       }
-      x0 = butterfly_lanes<1>(x0, lane & 1);   x1 = butterfly_lanes<1>(x1, lane & 1);
-      x0 = butterfly_lanes<2>(x0, lane & 2);   x1 = butterfly_lanes<2>(x1, lane & 2);
-      x0 = butterfly_lanes<4>(x0, lane & 4);   x1 = butterfly_lanes<4>(x1, lane & 4);
-      x0 = butterfly_lanes<8>(x0, lane & 8);   x1 = butterfly_lanes<8>(x1, lane & 8);
-      x0 = butterfly_lanes<16>(x0, lane & 16); x1 = butterfly_lanes<16>(x1, lane & 16);
-      x0 = butterfly_lanes<32>(x0, lane & 32); x1 = butterfly_lanes<32>(x1, lane & 32);
-      // x0 = q'[lane], x1 = q'[lane + 64]
-      const float amax = group_max<64>(fmaxf(fabsf(x0), fabsf(x1)));
+      // x[e] = q'[lane + 64 e]
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 2 * F; ++e) am = fmaxf(am, fabsf(x[e]));
+      const float amax = group_max<64>(am);
       const int E = amax > 0.0f ? 26 - ((int)((f2u(amax) >> 23) & 0xFF) - 127) : 0;
       const float sc = exp2i(E);
       float dsum[4];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < 2 * F; ++e) {
         const int dim = lane + 64 * e;
-        int v = (int)__builtin_rintf((e ? x1 : x0) * sc);
-        const int gg = dim >> 5, o = dim & 31;
+        int v = (int)__builtin_rintf(x[e] * sc);
+        const int gg = dim / (32 * F), o = dim % (32 * F);
         const int kc = o >> 4;
         const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
         const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
@@ -390,7 +413,7 @@ void decode_tqb_kernel(DecodeParams p) {
           const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
           v = (v - dk) >> 7;
           const int L = 16 * gg + 4 * hp + pc;
-          img[(((r * 2 + kc) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
+          img[(((r * 2 * F + kc) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
           dsum[pc] = (e ? dsum[pc] : 0.0f) + (float)dk;
         }
       }
@@ -400,20 +423,20 @@ void decode_tqb_kernel(DecodeParams p) {
       if (hp == lg) {
         qsum[r] = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(t[3], 128.0f, t[2]), 128.0f, t[1]), 128.0f, t[0]);
         // score in base-2 units = sm_scale / sqrt(D) * log2(e) * 2^-E * norm * (integer dot)
-        qf[r] = p.sm_scale * 0.08838834764831845f * kLog2e * exp2i(-E);
+        qf[r] = p.sm_scale * (D == 128 ? 0.08838834764831845f : 0.0625f) * kLog2e * exp2i(-E);
       }
     }
     wave_sync();
 #pragma unroll
     for (int r = 0; r < NH; ++r)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
+      for (int kc = 0; kc < 2 * F; ++kc) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
         qa[r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
       }
   };
   auto load_query = [&](int b) {
-    float qx[NHEAD][2];
+    float qx[NHEAD][2 * F];
     query_rows(b, qx);
     query_image(qx);
   };
@@ -442,9 +465,9 @@ void decode_tqb_kernel(DecodeParams p) {
           out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
                          kvl * g + hq0 + hh) * (D + 1);
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        float* dst = out + 8 * ln;
+        float* dst = out + 8 * F * ln;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = (acc[8 * r + i][lane] + zt) * inv;
+        for (int i = 0; i < 8 * F; ++i) dst[i] = (acc[8 * F * r + i][lane] + zt) * inv;
         if (ln == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
@@ -474,14 +497,14 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
-      // KB = 3: index bytes of dims 32g + 4i .. +3 (KB = 4 reads the planes
-      // from the packed nibbles)
-      uint32_t ix[KB == 3 ? 8 : 1];
+      // KB = 3: index bytes of dims 32F g + 4i .. +3 (KB = 4 reads the
+      // planes from the packed nibbles)
+      uint32_t ix[KB == 3 ? 8 * F : 1];
       if constexpr (KB == 3) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
+        for (int i = 0; i < 8 * F; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
       }
-      // one bit plane at a time: two MFMAs (dims 32g + 16kc + ...), then its
+      // one bit plane at a time: 2F MFMAs (dims 32F g + 16kc + ...), then its
       // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
       // digit planes of head g, token 16s+n
       auto plane_dot = [&](auto sel, float (&out)[NH]) {
@@ -493,7 +516,7 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < NH; ++r) c[r] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+        for (int kc = 0; kc < 2 * F; ++kc) {
           uint32_t pl[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -645,8 +668,9 @@ void decode_tqb_kernel(DecodeParams p) {
     wave_sync();
 
     // ---- value MFMAs: B operands by 4x4 byte transposes ----
-    // u[s][h]: index bytes of dims 8n + 4h .. +3 of token 16s + 4g + kk;
-    // vb[4h + i][kk] byte s = dim 8n + 4h + i of token 16s + 4g + kk
+    // u[s]: index bytes of dims 8F n + 8f + 4h .. +3 of token 16s + 4g + kk;
+    // vb[i][kk] byte s = dim 8F n + 8f + 4h + i of token 16s + 4g + kk,
+    // accumulated in cacc[r][8f + 4h + i]
     v4i pa[NH];
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
@@ -654,14 +678,15 @@ void decode_tqb_kernel(DecodeParams p) {
       pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int fh = 0; fh < 2 * F; ++fh) {
+      const int f = fh >> 1, h = fh & 1;
       uint32_t vb[4][4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint32_t u[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t x = X.vraw[s][kk];
+          const uint32_t x = X.vraw[s][kk][f];
           if constexpr (VB == 4) u[s] = unpack4x4(x, h);
           else u[s] = unpack3x4(h ? x >> 12 : x);
         }
@@ -679,7 +704,7 @@ void decode_tqb_kernel(DecodeParams p) {
         const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
 #pragma unroll
         for (int r = 0; r < NH; ++r)
-          cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
+          cacc[r][4 * fh + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * fh + i], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -688,7 +713,7 @@ void decode_tqb_kernel(DecodeParams p) {
 
   // The range's first query rows are requested now: their loads overlap
   // the tile table's, so tile 0 does not wait behind the query set-up.
-  float q0[NHEAD][2];
+  float q0[NHEAD][2 * F];
   {
     int bl = 0, bh = p.B - 1;  // the sequence of tile lo, as the table finds it
     while (bl < bh) {
@@ -762,14 +787,14 @@ void decode_tqb_kernel(DecodeParams p) {
   emit();
 }
 
-template <int W, int NH, int KB, int VB>
+template <int W, int NH, int KB, int VB, int DD = 128>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
   if (wide)
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true, KB, VB>), dim3(blocks), dim3(64 * W), lds, st, p);
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true, KB, VB, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
   else
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB>), dim3(blocks), dim3(64 * W), lds, st, p);
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
   return hipGetLastError();
 }
 
@@ -779,6 +804,18 @@ constexpr bool kOneWavePerKvHead = true;
 
 template <int KB, int VB>
 hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
+  if (p.d == 256) {
+    // D = 256: four query heads per wave (ceil(g / 4) waves per kv head),
+    // one wave per SIMD, at most 4 waves per workgroup and per CU
+    p.wgh = balance_heads_per_wg(p.hk, p.g, 4);
+    const int64_t nw = balance_max_wgs(p.hk, p.g, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh * ((p.g + 3) / 4)) {
+      case 1: return launch<1, 1, KB, VB, 256>(p, st, wide);
+      case 2: return launch<2, 1, KB, VB, 256>(p, st, wide);
+      default: return launch<4, 1, KB, VB, 256>(p, st, wide);
+    }
+  }
   if (p.g > 4 && kOneWavePerKvHead) {
     // one wave per kv head at one wave per SIMD: at most 4 waves per
     // workgroup and per CU (the piece region, sized for two waves per kv
@@ -808,11 +845,12 @@ hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles
 
 hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   const bool k4 = p.key_fmt == KF_MSE4, v4 = p.val_fmt == VF_U4;
-  if (p.d != D || (p.key_fmt != KF_MSE3 && !k4) || (p.val_fmt != VF_U3 && !v4) || p.g > 8 ||
-      p.norm_correction)
+  if ((p.d != 128 && p.d != 256) || (p.key_fmt != KF_MSE3 && !k4) || (p.val_fmt != VF_U3 && !v4) ||
+      p.g > 8 || p.norm_correction)
     return hipErrorNotSupported;
   const int kb = k4 ? 4 : 3, vb = v4 ? 4 : 3;
-  if (p.kps != 16 * kb + 2 || p.vdb != 16 * vb || p.slot_bytes % 16 != 0) return hipErrorNotSupported;
+  if (p.kps != p.d * kb / 8 + 2 || p.vdb != p.d * vb / 8 || p.slot_bytes % 16 != 0)
+    return hipErrorNotSupported;
   // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
   // 64-bit variant (whose zero page must cover every kv head's slot)
   const bool wide = p.force_wide ||

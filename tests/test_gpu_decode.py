@@ -537,6 +537,44 @@ def test_tq_head_dim_256_shapes(fmt, norm_correction):
         assert_close(got, ref, lse, ref_lse, "fmt %s B=%d" % (fmt, B))
 
 
+ALL_C_FMTS = [(oracle.KEY_MSE3, oracle.VAL_U3)] + C_FMTS
+
+
+@pytest.mark.parametrize("flags", [0, tq.FLAG_GENERIC, tq.FLAG_WIDE],
+                         ids=["mfma", "generic", "mfma_wide"])
+@pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
+def test_tq_centroid_head_dim_256(fmt, flags):
+    """D = 256 on the centroid-key matrix-core kernel (four query heads per
+    wave, one wave per SIMD): oracle-encoded caches, g = 1, 4, 8, ragged,
+    empty and one-token sequences."""
+    for (B, hq, hk, seq, S) in [(2, 8, 8, [300, 1], 4), (3, 16, 2, [129, 0, 640], 5),
+                                (2, 16, 4, [1000, 65], 7)]:
+        w = W.custom_decode_workload(960 + hq + S + 3 * fmt[0] + fmt[1], B, hq, hk, 256, 16, S, seq, 3,
+                                     "bf16")
+        cache, cen = tq_case(w, *fmt)
+        q = W.query(w, bf16_valued=True)
+        ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, flags=flags)
+        assert_close(got, ref, lse, ref_lse, "fmt %s B=%d hq=%d" % (fmt, B, hq))
+
+
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
+def test_tq_centroid_head_dim_256_random_slots(fmt, antisymmetric):
+    """D = 256, random slots and random tables (both score forms), split
+    counts 1 .. 256."""
+    w = W.custom_decode_workload(970 + 3 * fmt[0] + fmt[1], 3, 16, 2, 256, 16, 4, [300, 77, 1], 4, "bf16")
+    cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(256, *fmt))
+    n = 16 if fmt[0] == oracle.KEY_MSE4 else 8
+    cen = _random_table(971 + fmt[1], n, antisymmetric)
+    q = W.query(w) / 4
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt, splits=0)
+    for S in (1, 4, 37, 256):
+        for flags in (0, tq.FLAG_WIDE):
+            got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, num_splits=S, flags=flags)
+            assert_close(got, ref, lse, ref_lse, "random slots %s S=%d flags=%d" % (fmt, S, flags))
+
+
 # ---------------------------------------------------------------------------
 # FP8 keys + FP8 values (matrix-core path for D = 128, g <= 8)
 
