@@ -579,6 +579,7 @@ def run_other(args, torch, tq, W):
                          dtype=torch.float32, device=dev)
         calls = [tq.prepare_decode(q, bt, sl, num_kv_splits=w.num_splits, kv_cache=c,
                                    key_fmt=fmt[0], val_fmt=fmt[1], centroids=cen,
+                                   norm_correction=bool(args.norm_correction) and fmt[0] != tq.KEY_FP8,
                                    workspace=ws,
                                    flags=(tq.FLAG_WIDE if args.wide else 0) |
                                    (tq.FLAG_GENERIC if args.generic else 0))[0]
@@ -590,7 +591,8 @@ def run_other(args, torch, tq, W):
         nbytes = kv + parts + w.B * w.hq * (8 * w.d + 4)
         line = dict(workload="%s: B=16 Hq=32 Hk=4 D=%d seq 16384 S=32, %s keys + %s values%s" % (
                         name, w.d, TQ_KEY_NAMES[fmt[0]], TQ_VAL_NAMES[fmt[1]],
-                        ", generic kernel" if args.generic else ""), us=t * 1e6,
+                        (", norm-corrected keys" if args.norm_correction and fmt[0] != tq.KEY_FP8 else "") +
+                        (", generic kernel" if args.generic else "")), us=t * 1e6,
                     algorithmic_bytes=nbytes, TBps=nbytes / t / 1e12,
                     pct_peak=100 * nbytes / t / PEAK_HBM)
     else:
@@ -623,6 +625,8 @@ def main():
     ap.add_argument("--min-calls", type=int, default=MIN_TIMED_CALLS,
                     help="secondary workloads: least calls per timed run (fewer for counter runs)")
     ap.add_argument("--splits", type=int, default=0, help="override num_kv_splits (sweeps)")
+    ap.add_argument("--norm-correction", action="store_true",
+                    help="TurboQuant decode workloads with centroid keys: the norm-corrected read")
     ap.add_argument("--generic", action="store_true",
                     help="decode workloads: force the generic (vector) kernel, for comparison")
     ap.add_argument("--wide", action="store_true",

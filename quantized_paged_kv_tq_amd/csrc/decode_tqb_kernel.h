@@ -134,7 +134,7 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[N], int bit) {
 // operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH, bool WIDE, int KB, int VB, int DD>
+template <int W, int NH, bool WIDE, int KB, int VB, int DD, bool NCORR>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 && DD == 128 ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
   constexpr int D = DD;      // head dim, 128 or 256
@@ -178,6 +178,12 @@ void decode_tqb_kernel(DecodeParams p) {
   // A table with c[NC - 1 - j] = -c[j] (Lloyd-Max tables are) has ga_S = 0
   // for every even |S|; then only the planes of odd |S| are needed:
   //   q . c[idx] = sum_S ga_S (sum q - 2 q . [popcount(b & S) odd]).
+  // e2: Walsh form of the squared table, c(b)^2 = sum_S e2_S (-1)^{popcount(b & S)},
+  // for the norm-corrected read (1 / sqrt(sum over dims of c[idx]^2 + 1e-16));
+  // an antisymmetric table has a symmetric square: e2_S = 0 for odd |S|.
+  // e2 (only the norm-corrected read uses it) lives in LDS, thread S
+  // computing entry S.
+  __shared__ float e2_s[NCORR ? NC : 1];
   float al[NC], ga[NC];
   bool anti = true;
   {
@@ -198,6 +204,16 @@ void decode_tqb_kernel(DecodeParams p) {
       }
       al[S] = a;
       ga[S] = w * (1.0f / NC);
+    }
+    if constexpr (NCORR) {
+      const int S = threadIdx.x;
+      if (S < NC) {
+        float w2 = 0.0f;
+#pragma unroll
+        for (int T = 0; T < NC; ++T) w2 = (__builtin_popcount(T & S) & 1) ? w2 - c[T] * c[T] : w2 + c[T] * c[T];
+        e2_s[S] = w2 * (1.0f / NC);
+      }
+      // (the prologue's barriers order these stores before any read)
     }
   }
 
@@ -498,7 +514,7 @@ void decode_tqb_kernel(DecodeParams p) {
     float sc[NH][4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
+      float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
       // KB = 3: index bytes of dims 32F g + 4i .. +3 (KB = 4 reads the
       // planes from the packed nibbles)
       uint32_t ix[KB == 3 ? 8 * F : 1];
@@ -509,8 +525,32 @@ void decode_tqb_kernel(DecodeParams p) {
       // one bit plane at a time: 2F MFMAs (dims 32F g + 16kc + ...), then its
       // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
       // digit planes of head g, token 16s+n
+      // the B operand of chunk kc for plane SS: the subset S of index bits
+      // (low bits); SS >= 32: their parity, else their product
+      auto plane_words = [&](auto sel, int kc) -> v4i {
+        constexpr int SS = decltype(sel)::value;
+        constexpr bool PAR = SS >= 32;
+        constexpr int S = SS & 31;
+        uint32_t pl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // bit k of each byte (KB = 3) or of each nibble (KB = 4) of x
+          // is index bit k of one dimension
+          uint32_t x;
+          if constexpr (KB == 4) x = X.kraw[s][2 * kc + (j >> 1)];
+          else x = ix[4 * kc + j];
+          uint32_t m = PAR ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+          for (int k = 0; k < KB; ++k) {
+            if (!((S >> k) & 1)) continue;
+            if constexpr (PAR) m ^= x >> k;
+            else m &= x >> k;
+          }
+          pl[j] = ((KB == 4 && (j & 1)) ? m >> 4 : m) & 0x01010101u;
+        }
+        return v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
+      };
       auto plane_dot = [&](auto sel, float (&out)[NH]) {
-        // the subset S of index bits (low bits); + 32: parity, else product
         constexpr int SS = decltype(sel)::value;
         constexpr bool PAR = SS >= 32;
         constexpr int S = SS & 31;
@@ -522,8 +562,6 @@ void decode_tqb_kernel(DecodeParams p) {
           uint32_t pl[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            // bit k of each byte (KB = 3) or of each nibble (KB = 4) of x
-            // is index bit k of one dimension
             uint32_t x;
             if constexpr (KB == 4) x = X.kraw[s][2 * kc + (j >> 1)];
             else x = ix[4 * kc + j];
@@ -581,6 +619,35 @@ void decode_tqb_kernel(DecodeParams p) {
 #undef TQK_PLANE
       }
       const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
+      if constexpr (NCORR) {
+        // sum over the token's dims of c[idx]^2 = sum_S e2_S (D - 2 n_S),
+        // n_S the dims whose index bits in S have odd parity: the plane
+        // summed over all D dims by an MFMA against ones (every row of the
+        // result is the count of token 16s + n)
+        const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+        float cs = e2_s[0] * (float)D;
+        auto count = [&](auto sel) -> float {
+          v4i c = v4i{0, 0, 0, 0};
+#pragma unroll
+          for (int kc = 0; kc < 2 * F; ++kc)
+            c = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, plane_words(sel, kc), c, 0, 0, 0);
+          return (float)c.x;
+        };
+#define TQK_SQ(S) cs = __builtin_fmaf(e2_s[S], (float)D - 2.0f * count(std::integral_constant<int, 32 + S>{}), cs);
+        if (anti) {
+          TQK_SQ(3) TQK_SQ(5) TQK_SQ(6)
+          if constexpr (KB == 4) {
+            TQK_SQ(9) TQK_SQ(10) TQK_SQ(12) TQK_SQ(15)
+          }
+        } else {
+          TQK_SQ(1) TQK_SQ(2) TQK_SQ(3) TQK_SQ(4) TQK_SQ(5) TQK_SQ(6) TQK_SQ(7)
+          if constexpr (KB == 4) {
+            TQK_SQ(8) TQK_SQ(9) TQK_SQ(10) TQK_SQ(11) TQK_SQ(12) TQK_SQ(13) TQK_SQ(14) TQK_SQ(15)
+          }
+        }
+#undef TQK_SQ
+        nrm *= 1.0f / sqrtf(cs + 1e-16f);
+      }
 #pragma unroll
       for (int r = 0; r < NH; ++r) sc[r][s] = fminf(dot[r] * (qf[r] * nrm), mask);
       // one token block at a time (bounds the live bit planes)
@@ -789,21 +856,98 @@ void decode_tqb_kernel(DecodeParams p) {
   emit();
 }
 
-template <int W, int NH, int KB, int VB, int DD = 128>
+template <int W, int NH, int KB, int VB, int DD, bool NCORR>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  if (wide)
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true, KB, VB, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
-  else
-    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
+  if constexpr (NCORR) {
+    // (the norm-corrected read has no 64-bit variant: the caller declines it)
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD, true>), dim3(blocks), dim3(64 * W), lds,
+                       st, p);
+  } else if (wide) {
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, true, KB, VB, DD, false>), dim3(blocks), dim3(64 * W), lds,
+                       st, p);
+  } else {
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD, false>), dim3(blocks), dim3(64 * W), lds,
+                       st, p);
+  }
   return hipGetLastError();
+}
+
+// g = 5 .. 8 at D = 128: one wave serves all query heads of a kv head
+// (NH = 2), so each tile's keys and values are unpacked once instead of by
+// two waves.
+constexpr bool kOneWavePerKvHead = true;
+
+template <int KB, int VB, bool NCORR>
+hipError_t launch_layout128(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
+
+// Waves, workgroups and the kernel variant for a shape; tiles_ub bounds the
+// tile list.
+template <int KB, int VB, int DD, bool NCORR>
+hipError_t launch_layout(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
+  if constexpr (DD == 256) {
+    // four query heads per wave (ceil(g / 4) waves per kv head), one wave
+    // per SIMD, at most 4 waves per workgroup and per CU
+    p.wgh = balance_heads_per_wg(p.hk, p.g, 4);
+    const int64_t nw = balance_max_wgs(p.hk, p.g, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh * ((p.g + 3) / 4)) {
+      case 1: return launch<1, 1, KB, VB, DD, NCORR>(p, st, wide);
+      case 2: return launch<2, 1, KB, VB, DD, NCORR>(p, st, wide);
+      default: return launch<4, 1, KB, VB, DD, NCORR>(p, st, wide);
+    }
+  } else {
+    return launch_layout128<KB, VB, NCORR>(p, st, wide, tiles_ub);
+  }
+}
+
+// D = 128: waves by group size
+template <int KB, int VB, bool NCORR>
+hipError_t launch_layout128(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
+  constexpr int DD = 128;
+  if (p.g > 4 && kOneWavePerKvHead) {
+    // one wave per kv head at one wave per SIMD: at most 4 waves per
+    // workgroup and per CU (the piece region, sized for two waves per kv
+    // head at 8 per CU, holds the same number of workgroups)
+    p.wgh = balance_heads_per_wg(p.hk, 4, 4);
+    const int64_t nw = balance_max_wgs(p.hk, 4, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh) {
+      case 1: return launch<1, 2, KB, VB, DD, NCORR>(p, st, wide);
+      case 2: return launch<2, 2, KB, VB, DD, NCORR>(p, st, wide);
+      default: return launch<4, 2, KB, VB, DD, NCORR>(p, st, wide);
+    }
+  }
+  const int qs = (p.g + 3) / 4;
+  p.wgh = balance_heads_per_wg(p.hk, p.g);
+  const int64_t nw = balance_max_wgs(p.hk, p.g);
+  p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+  switch (p.wgh * qs) {
+    case 1: return launch<1, 1, KB, VB, DD, NCORR>(p, st, wide);
+    case 2: return launch<2, 1, KB, VB, DD, NCORR>(p, st, wide);
+    case 4: return launch<4, 1, KB, VB, DD, NCORR>(p, st, wide);
+    default: return launch<8, 1, KB, VB, DD, NCORR>(p, st, wide);
+  }
+}
+
+// one of the four key / value bit combinations
+template <int DD, bool NCORR>
+hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
+  const bool k4 = p.key_fmt == KF_MSE4, v4 = p.val_fmt == VF_U4;
+  if (k4)
+    return v4 ? launch_layout<4, 4, DD, NCORR>(p, st, wide, tiles_ub)
+              : launch_layout<4, 3, DD, NCORR>(p, st, wide, tiles_ub);
+  return v4 ? launch_layout<3, 4, DD, NCORR>(p, st, wide, tiles_ub)
+            : launch_layout<3, 3, DD, NCORR>(p, st, wide, tiles_ub);
 }
 
 }  // namespace
 
-// The head-dim-256 launches (their own translation unit, for build time):
-// wide = 64-bit addressing, tiles_ub bounds the tile list.
+// The launches kept in their own translation units (for build time): head
+// dim 256, and the norm-corrected read (narrow addressing only) at both
+// head dims.
 hipError_t launch_decode_tqb_d256(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
+hipError_t launch_decode_tqb_ncorr(DecodeParams& p, hipStream_t st, int64_t tiles_ub);
 
 }  // namespace tqk

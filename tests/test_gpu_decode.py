@@ -575,6 +575,28 @@ def test_tq_centroid_head_dim_256_random_slots(fmt, antisymmetric):
             assert_close(got, ref, lse, ref_lse, "random slots %s S=%d flags=%d" % (fmt, S, flags))
 
 
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
+def test_tq_centroid_norm_correction(fmt, antisymmetric, d):
+    """The norm-corrected read on the matrix-core kernel (the sum of c[idx]^2
+    over a token's dims from parity-plane counts): random slots, random
+    tables in both forms, g = 4 and 8, against the oracle and with the
+    64-bit variant and the generic kernel."""
+    for (hq, hk) in [(16, 4), (16, 2)]:
+        w = W.custom_decode_workload(980 + hq + hk + d + 3 * fmt[0] + fmt[1], 3, hq, hk, d, 16, 4,
+                                     [300, 77, 1], 4, "bf16")
+        cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(d, *fmt))
+        n = 16 if fmt[0] == oracle.KEY_MSE4 else 8
+        cen = _random_table(981 + fmt[1] + hq, n, antisymmetric)
+        q = W.query(w)
+        ref, ref_lse = oracle.tq_decode(q, cache, w.block_table, w.seq_lens, cen, None, *fmt, 1,
+                                        w.num_splits, w.sm_scale)
+        for flags in (0, tq.FLAG_WIDE, tq.FLAG_GENERIC):
+            got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, norm_correction=True, flags=flags)
+            assert_close(got, ref, lse, ref_lse, "%s hq=%d hk=%d flags=%d" % (fmt, hq, hk, flags))
+
+
 # ---------------------------------------------------------------------------
 # FP8 keys + FP8 values (matrix-core path for D = 128, g <= 8)
 
