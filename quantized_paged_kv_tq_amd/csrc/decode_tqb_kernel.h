@@ -57,6 +57,14 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits (round to nearest even; finite values)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -144,7 +152,10 @@ void decode_tqb_kernel(DecodeParams p) {
   constexpr int NC = 1 << KB;  // centroids
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
-  __shared__ __attribute__((aligned(16))) uint32_t p8[W][NH][4][4][16];  // weight digit planes
+  constexpr bool V8 = VB == 8;  // FP8 E4M3 values (D codes, no scale or zero)
+  __shared__ __attribute__((aligned(16))) uint32_t p8[V8 ? 1 : W][NH][4][4][16];  // weight digit planes
+  // V8: bf16 parts of the weights, [part][head][token] per row set
+  __shared__ __attribute__((aligned(16))) uint16_t pbf[V8 ? W : 1][NH][3][4][64];
   __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2 * F][64][4];  // query digit image
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
@@ -262,7 +273,8 @@ void decode_tqb_kernel(DecodeParams p) {
   struct Buf {
     uint32_t kraw[4][KB * F];
     uint32_t nw, sz0, sz1, live;
-    uint32_t vraw[4][4][F];
+    uint32_t vraw[V8 ? 1 : 4][4][F];
+    uint32_t v8[V8 ? 2 : 1][8][2];  // V8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
   auto slot_of = [&](int k, int j) -> Off { return WIDE ? tok_rows[k][j] : tok_rows[k][j] + kvh_off; };
@@ -270,13 +282,25 @@ void decode_tqb_kernel(DecodeParams p) {
   // tile's scores (issue_v), which keeps both tiles' values from being live
   // through the score computation
   auto issue_v = [&](Buf& B, int k) {
+    if constexpr (V8) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const Off o = slot_of(k, 16 * s + 4 * lg + kk);
+        for (int j = 0; j < 8; ++j) {
+          const Off o = slot_of(k, 32 * h + 8 * lg + j);
+          B.v8[h][j][0] = ld32(o + kValOff + 8u * ln);
+          B.v8[h][j][1] = ld32(o + kValOff + 8u * ln + 4u);
+        }
+      }
+    } else {
 #pragma unroll
-        for (int f = 0; f < F; ++f) B.vraw[s][kk][f] = ld32(o + vbyte + (uint32_t)(VB * f));
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const Off o = slot_of(k, 16 * s + 4 * lg + kk);
+#pragma unroll
+          for (int f = 0; f < F; ++f) B.vraw[s][kk][f] = ld32(o + vbyte + (uint32_t)(VB * f));
+        }
       }
     }
   };
@@ -304,16 +328,21 @@ void decode_tqb_kernel(DecodeParams p) {
     {
       const Off o = slot_of(k, lane);
       B.nw = ld32(o + kNormOff);
-      const v2u w = ld64(o + kScaleOff);
-      B.sz0 = w.x;
-      B.sz1 = w.y;
+      if constexpr (V8) {
+        B.sz0 = B.sz1 = 0;
+      } else {
+        const v2u w = ld64(o + kScaleOff);
+        B.sz0 = w.x;
+        B.sz1 = w.y;
+      }
     }
   };
 
   // ---- online softmax state of the current segment ----
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
   float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
-  v4i cacc[NH][8 * F];
+  v4i cacc[NH][V8 ? 1 : 8 * F];
+  v4f facc[NH][V8 ? 8 : 1];  // V8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
@@ -327,7 +356,8 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 8 * F; ++i) {
         acc[8 * F * r + i][lane] = 0.0f;
-        cacc[r][i] = v4i{0, 0, 0, 0};
+        if constexpr (V8) facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        else cacc[r][i] = v4i{0, 0, 0, 0};
       }
     }
     ev = 0;
@@ -344,11 +374,17 @@ void decode_tqb_kernel(DecodeParams p) {
       if (!empty) {
 #pragma unroll
         for (int i = 0; i < 8 * F; ++i) {
-          const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
-          const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
-          const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-          acc[8 * F * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * F * r + i][lane]) * alpha[r];
-          cacc[r][i] = v4i{0, 0, 0, 0};
+          if constexpr (V8) {
+            const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
+            acc[8 * F * r + i][lane] = (acc[8 * F * r + i][lane] + val) * alpha[r];
+            facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          } else {
+            const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
+            const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+            const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+            acc[8 * F * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * F * r + i][lane]) * alpha[r];
+            cacc[r][i] = v4i{0, 0, 0, 0};
+          }
         }
       } else {
 #pragma unroll
@@ -655,13 +691,15 @@ void decode_tqb_kernel(DecodeParams p) {
     }
     issue_v(Y, k + 1);
     __builtin_amdgcn_sched_barrier(0);
-    float vsc[4], vz[4];
+    float vsc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vz[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float smax = 0.0f;
+    if constexpr (!V8) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      vsc[s] = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz0));
-      vz[s] = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz1));
-      smax = fmaxf(smax, fabsf(vsc[s]));
+      for (int s = 0; s < 4; ++s) {
+        vsc[s] = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz0));
+        vz[s] = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz1));
+        smax = fmaxf(smax, fabsf(vsc[s]));
+      }
     }
 
     // ---- reference maximum / weight scale; flush when they move ----
@@ -673,8 +711,9 @@ void decode_tqb_kernel(DecodeParams p) {
       move |= tm[r] > mref[r] + (float)kTau;
     }
     smax = row16_max(smax);
-    // a flush also bounds the int32 digit sums (< 2^31 after 8192 tiles)
-    const bool smove = smax >= sref || ++since_flush >= 8192;
+    // a flush also bounds the int32 digit sums (< 2^31 after 8192 tiles);
+    // V8's fp32 sums need no fixed-point range
+    const bool smove = !V8 && (smax >= sref || ++since_flush >= 8192);
     if (__builtin_amdgcn_ballot_w64(move || smove) != 0) {
       float alpha[NH];
 #pragma unroll
@@ -692,6 +731,74 @@ void decode_tqb_kernel(DecodeParams p) {
       }
     }
 
+    if constexpr (V8) {
+      // ---- weights in three bf16 parts, to LDS as [part][head][token] ----
+#pragma unroll
+      for (int r = 0; r < NH; ++r) {
+        float ps = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float pr = (mref[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[r][s] - mref[r]);
+          ps += pr;
+          const uint32_t bh = bf16_bits(pr);
+          const float r1 = pr - u2f(bh << 16);
+          const uint32_t bm = bf16_bits(r1);
+          const uint32_t bl = bf16_bits(r1 - u2f(bm << 16));
+          pbf[wave][r][0][lg][16 * s + ln] = (uint16_t)bh;
+          pbf[wave][r][1][lg][16 * s + ln] = (uint16_t)bm;
+          pbf[wave][r][2][lg][16 * s + ln] = (uint16_t)bl;
+        }
+        l[r] += ps;
+      }
+      empty = false;
+      wave_sync();
+      // ---- value MFMAs (exact bf16 values), one 32-token half at a time ----
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // A: lane (4h' + part, g) holds part `part` of head h''s weights of
+        // tokens 32h + 8g .. 32h + 8g + 7 (part 3: zero)
+        v8bf16 pa[NH];
+        const int hd = ln >> 2, part = ln & 3;
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          uint4 a4 = make_uint4(0u, 0u, 0u, 0u);
+          if (part < 3) a4 = *reinterpret_cast<const uint4*>(&pbf[wave][r][part][hd][32 * h + 8 * lg]);
+          pa[r] = __builtin_bit_cast(v8bf16, v4u{a4.x, a4.y, a4.z, a4.w});
+        }
+        // ob[t][i]: byte i of value bytes 8n .. 8n+7 of tokens 4t .. 4t+3
+        // of this lane's eight (4x4 byte transposes)
+        uint32_t ob[2][8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t d0 = X.v8[h][4 * t][q], d1 = X.v8[h][4 * t + 1][q];
+            const uint32_t d2 = X.v8[h][4 * t + 2][q], d3 = X.v8[h][4 * t + 3][q];
+            const uint32_t x01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+            const uint32_t x23l = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+            const uint32_t x01h = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+            const uint32_t x23h = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+            ob[t][4 * q + 0] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+            ob[t][4 * q + 1] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+            ob[t][4 * q + 2] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+            ob[t][4 * q + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+          }
+        }
+        // B of MFMA i: column n = value dim 8n + i, rows = the 32 tokens
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const v2bf16 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, false);
+          const v2bf16 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, true);
+          const v2bf16 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[1][i], 1.0f, false);
+          const v2bf16 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[1][i], 1.0f, true);
+          const v8bf16 vb8 = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+          for (int r = 0; r < NH; ++r)
+            facc[r][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[r], vb8, facc[r][i], 0, 0, 0);
+        }
+      }
+      wave_sync();  // the weight parts are rewritten by the next tile
+    } else {
     // ---- weights p * scale16 as 7-bit digit planes; zero term in fp32 ----
     // A negative scale16 (bytes not written by the encoder) takes signed
     // digits: the digits of p * |scale16| negated as int8.
@@ -778,6 +885,7 @@ void decode_tqb_kernel(DecodeParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     wave_sync();
+    }
   };
 
   // The range's first query rows are requested now: their loads overlap
@@ -945,9 +1053,11 @@ hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles
 }  // namespace
 
 // The launches kept in their own translation units (for build time): head
-// dim 256, and the norm-corrected read (narrow addressing only) at both
-// head dims.
+// dim 256, the norm-corrected read (narrow addressing only) at both head
+// dims, and FP8 values.
 hipError_t launch_decode_tqb_d256(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
 hipError_t launch_decode_tqb_ncorr(DecodeParams& p, hipStream_t st, int64_t tiles_ub);
+// FP8 values (head dim 128, no norm correction)
+hipError_t launch_decode_tqb_fp8v(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
 
 }  // namespace tqk

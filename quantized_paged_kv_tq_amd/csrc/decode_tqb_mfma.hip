@@ -1,5 +1,5 @@
 // TurboQuant split-KV decode, stage 1, on the CDNA4 matrix cores, for
-// 3- or 4-bit centroid keys with 3- or 4-bit uniform values: the entry
+// 3- or 4-bit centroid keys with 3- or 4-bit uniform or FP8 values: the entry
 // point and the launches at head dim 128 (the kernel is in
 // decode_tqb_kernel.h).
 #include "decode_tqb_kernel.h"
@@ -7,11 +7,13 @@
 namespace tqk {
 
 hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
-  const bool k4 = p.key_fmt == KF_MSE4, v4 = p.val_fmt == VF_U4;
-  if ((p.d != 128 && p.d != 256) || (p.key_fmt != KF_MSE3 && !k4) || (p.val_fmt != VF_U3 && !v4) ||
-      p.g > 8)
+  const bool k4 = p.key_fmt == KF_MSE4, v4 = p.val_fmt == VF_U4, v8 = p.val_fmt == VF_FP8;
+  if ((p.d != 128 && p.d != 256) || (p.key_fmt != KF_MSE3 && !k4) ||
+      (p.val_fmt != VF_U3 && !v4 && !v8) || p.g > 8)
     return hipErrorNotSupported;
-  const int kb = k4 ? 4 : 3, vb = v4 ? 4 : 3;
+  // FP8 values: head dim 128, without the norm correction
+  if (v8 && (p.d != 128 || p.norm_correction)) return hipErrorNotSupported;
+  const int kb = k4 ? 4 : 3, vb = v8 ? 8 : (v4 ? 4 : 3);
   if (p.kps != p.d * kb / 8 + 2 || p.vdb != p.d * vb / 8 || p.slot_bytes % 16 != 0)
     return hipErrorNotSupported;
   // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
@@ -28,6 +30,7 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
     if (wide) return hipErrorNotSupported;
     return launch_decode_tqb_ncorr(p, st, tiles_ub);
   }
+  if (v8) return launch_decode_tqb_fp8v(p, st, wide, tiles_ub);
   if (p.d == 256) return launch_decode_tqb_d256(p, st, wide, tiles_ub);
   return launch_bits<128, false>(p, st, wide, tiles_ub);
 }

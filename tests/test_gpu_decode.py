@@ -597,6 +597,41 @@ def test_tq_centroid_norm_correction(fmt, antisymmetric, d):
             assert_close(got, ref, lse, ref_lse, "%s hq=%d hk=%d flags=%d" % (fmt, hq, hk, flags))
 
 
+@pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
+@pytest.mark.parametrize("key_fmt", [oracle.KEY_MSE3, oracle.KEY_MSE4], ids=["mse3", "mse4"])
+def test_tq_centroid_keys_fp8_values(key_fmt, antisymmetric):
+    """Centroid keys with FP8 values on the centroid-key matrix-core kernel
+    (D = 128): random slots (every E4M3 code but NaN) and random tables, g =
+    2, 4, 8, split counts 1 .. 256, the 64-bit variant and the generic kernel
+    alongside."""
+    fmt = (key_fmt, oracle.VAL_FP8)
+    for (hq, hk) in [(4, 2), (16, 4), (16, 2)]:
+        w = W.custom_decode_workload(990 + hq + hk + key_fmt, 3, hq, hk, 128, 16, 4, [300, 77, 1], 4, "bf16")
+        cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(128, *fmt))
+        n = 16 if key_fmt == oracle.KEY_MSE4 else 8
+        cen = _random_table(991 + hq + key_fmt, n, antisymmetric)
+        q = W.query(w) / 4
+        ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt, splits=0)
+        for S in (1, 4, 256):
+            for flags in (0, tq.FLAG_WIDE, tq.FLAG_GENERIC):
+                got, lse = gpu_tq_decode(w, q, cache, cen, *fmt, num_splits=S, flags=flags)
+                assert_close(got, ref, lse, ref_lse, "%s hq=%d S=%d flags=%d" % (fmt, hq, S, flags))
+
+
+@pytest.mark.parametrize("key_fmt", [oracle.KEY_MSE3, oracle.KEY_MSE4], ids=["mse3", "mse4"])
+@pytest.mark.parametrize("shape", SHAPES[:5], ids=[str(i) for i in range(5)])
+def test_tq_centroid_keys_fp8_values_shapes(shape, key_fmt):
+    """Oracle-encoded caches (Lloyd-Max tables) on the other formats' shapes."""
+    B, hq, hk, d, bs, seq, S = shape
+    fmt = (key_fmt, oracle.VAL_FP8)
+    w = W.custom_decode_workload(995 + len(seq) * 7 + hq + key_fmt, B, hq, hk, d, bs, S, seq, 5, "bf16")
+    cache, cen = tq_case(w, *fmt)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *fmt)
+    assert_close(got, ref, lse, ref_lse, "%s %s" % (shape, fmt))
+
+
 # ---------------------------------------------------------------------------
 # FP8 keys + FP8 values (matrix-core path for D = 128, g <= 8)
 
