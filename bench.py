@@ -23,7 +23,8 @@ Other workloads (--workload): llama8b_int4_8k, long_int4, tq_mixed_a,
 tq_mixed_b, tq_fp8_values (the tq_mixed shape with FP8 keys and values),
 tq_mixed_b_d256 (3-bit centroid keys and values at D=256), tq_mse4_u4 (the
 tq_mixed shape with 4-bit centroid keys and 4-bit values), tq_mse3_fp8v (3-bit
-centroid keys with FP8 values), write (65536
+centroid keys with FP8 values), tq_mixed_a_d256 (FP8 keys + 4-bit values at
+D=256), write (65536
 tokens x 8 heads x 128 bf16), tq_write_a / tq_write_b (the TurboQuant slot
 writer on the same rows), fwht (1,048,576 rows), kpool (pooled-softmax key
 compression: 262144 pools of 4 tokens), prefill_int4 (multi-query INT4
@@ -611,6 +612,7 @@ TQ_DECODES = {
     "tq_mixed_b_d256": (("KEY_MSE3", "VAL_U3"), 256),
     "tq_mse4_u4": (("KEY_MSE4", "VAL_U4"), 128),
     "tq_mse3_fp8v": (("KEY_MSE3", "VAL_FP8"), 128),
+    "tq_mixed_a_d256": (("KEY_FP8", "VAL_U4"), 256),
 }
 TQ_KEY_NAMES = {1: "FP8", 2: "3-bit centroid", 3: "4-bit centroid"}
 TQ_VAL_NAMES = {1: "3-bit uniform", 2: "4-bit uniform", 3: "FP8"}

@@ -42,7 +42,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
-constexpr int D = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kChunk = 64;  // tiles resolved into LDS at a time
@@ -105,13 +104,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 // head h) and B = 32 tokens x 16 value dims, dims 8n + i for MFMA i (lane n
 // loads value bytes 8n .. 8n + 7 of its tokens, and a 4x4 byte transpose
 // gives byte i of 4 tokens per register).
-template <int W, int NH, bool VF8, bool WIDE>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+template <int W, int NH, bool VF8, bool WIDE, int DD>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 && DD == 128 ? 2 : 1)))
 void decode_tq_fp8_kernel(DecodeParams p) {
+  constexpr int D = DD;       // head dim, 128 or 256
+  constexpr int F = D / 128;  // a lane's dims per 16-lane group and token: 32 F keys, 8 F values
   // the range's first query is requested before the tile table is built
   // (not where holding it through the table build costs registers in the
-  // tile loop: the 64-bit, FP8-value and two-row-set variants)
-  constexpr bool kEarlyQuery = !WIDE && !VF8 && NH == 1;
+  // tile loop: the 64-bit, FP8-value, two-row-set and D = 256 variants)
+  constexpr bool kEarlyQuery = !WIDE && !VF8 && NH == 1 && DD == 128;
   constexpr int NT = 64 * W;
   constexpr int NHEAD = 4 * NH;  // query heads per wave (padded)
   __shared__ __attribute__((aligned(16))) uint32_t p8[VF8 ? 1 : W][NH][4][4][16];  // weight digit planes
@@ -123,7 +124,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) Off tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
-  __shared__ float accl[W][NH * 8][64];  // fp32 value accumulators, lane-major
+  __shared__ float accl[W][NH * 8 * F][64];  // fp32 value accumulators, lane-major
   extern __shared__ int prefix[];  // [B + 1] tile prefix sums, then [B] lengths
 
   const int tid = threadIdx.x;
@@ -178,13 +179,13 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   const uint32_t soff = (uint32_t)(p.kps + p.vdb);  // fp16 scale, fp16 zero
 
   // ---- registers of one tile ----
-  // key bytes [32g, 32g + 32) of tokens 16s + n; value dword n of tokens
-  // 16s + 4g + k; the scale/zero word of token `lane`
+  // key bytes [32F g, 32F (g + 1)) of tokens 16s + n; value dwords F n ..
+  // F n + F - 1 of tokens 16s + 4g + k; the scale/zero word of token `lane`
   struct Buf {
-    v4u kraw[4][2];
+    v4u kraw[4][2 * F];
     uint32_t sz, live;
-    uint32_t vraw[4][4];
-    uint32_t v8[2][8][2];  // VF8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
+    uint32_t vraw[4][4][F];
+    uint32_t v8[2][8][2 * F];  // VF8: value bytes 8F n .. 8F n + 8F - 1 of tokens 32h + 8g + j
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
   auto slot_of = [&](int k, int j) -> Off { return WIDE ? tok_rows[k][j] : tok_rows[k][j] + kvh_off; };
@@ -194,8 +195,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     for (int s = 0; s < 4; ++s) {
       const Off o = slot_of(k, 16 * s + ln);
       B.live |= (masked(o) ? 0u : 1u) << s;
-      B.kraw[s][0] = ld128(o + 32u * lg);
-      B.kraw[s][1] = ld128(o + 32u * lg + 16u);
+#pragma unroll
+      for (int i = 0; i < 2 * F; ++i) B.kraw[s][i] = ld128(o + (uint32_t)(32 * F) * lg + 16u * i);
     }
     if constexpr (VF8) {
 #pragma unroll
@@ -203,8 +204,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const Off o = slot_of(k, 32 * h + 8 * lg + j);
-          B.v8[h][j][0] = ld32(o + voff + 8u * ln);
-          B.v8[h][j][1] = ld32(o + voff + 8u * ln + 4u);
+#pragma unroll
+          for (int q = 0; q < 2 * F; ++q) B.v8[h][j][q] = ld32(o + voff + (uint32_t)(8 * F) * ln + 4u * q);
         }
       }
     } else {
@@ -214,7 +215,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const Off o = slot_of(k, 16 * s + 4 * lg + kk);
-          B.vraw[s][kk] = ld32(o + voff + 4u * ln);
+#pragma unroll
+          for (int f = 0; f < F; ++f) B.vraw[s][kk][f] = ld32(o + voff + (uint32_t)(4 * F) * ln + 4u * f);
         }
       }
     }
@@ -222,9 +224,9 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 
   // ---- online softmax state of the current segment ----
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
-  float(*acc)[64] = accl[wave];       // acc[8r + i][lane]
-  v4i cacc[NH][8];
-  v4f facc[NH][8];  // VF8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
+  float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
+  v4i cacc[NH][8 * F];
+  v4f facc[NH][8 * F];  // VF8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
   bool empty = true;
@@ -236,8 +238,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
       l[r] = 0.0f;
       zacc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[8 * r + i][lane] = 0.0f;
+      for (int i = 0; i < 8 * F; ++i) {
+        acc[8 * F * r + i][lane] = 0.0f;
         cacc[r][i] = v4i{0, 0, 0, 0};
         facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -248,29 +250,29 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     since_flush = 0;
   };
   // fold cacc into acc (scale 2^-ev), then rescale acc, l and the zero term
-  // by alpha (lane (n, g) holds head g's dims 8n .. 8n+7)
+  // by alpha (lane (n, g) holds head g's dims 8F n .. 8F n + 8F - 1)
   auto flush = [&](const float (&alpha)[NH]) {
     const float pinv = exp2i(-ev);
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       if (!empty) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8 * F; ++i) {
           if constexpr (VF8) {
             const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
-            acc[8 * r + i][lane] = (acc[8 * r + i][lane] + val) * alpha[r];
+            acc[8 * F * r + i][lane] = (acc[8 * F * r + i][lane] + val) * alpha[r];
             facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
           } else {
             const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
             const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
             const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-            acc[8 * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * r + i][lane]) * alpha[r];
+            acc[8 * F * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * F * r + i][lane]) * alpha[r];
             cacc[r][i] = v4i{0, 0, 0, 0};
           }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[8 * r + i][lane] *= alpha[r];
+        for (int i = 0; i < 8 * F; ++i) acc[8 * F * r + i][lane] *= alpha[r];
       }
       l[r] *= alpha[r];
       zacc[r] *= alpha[r];
@@ -279,31 +281,31 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   };
 
   // ---------------- query of sequence b: three bf16 parts ----------------
-  // A operand of MFMA kb for lane (m = 4h + part, g): 8 bf16 of dims
-  // 32g + 8kb .. 32g + 8kb + 7 (part 3: zero)
-  v8bf16 qa[NH][4];
+  // A operand of MFMA kb (4F of them) for lane (m = 4h + part, g): 8 bf16
+  // of dims 32F g + 8kb .. 32F g + 8kb + 7 (part 3: zero)
+  v8bf16 qa[NH][4 * F];
   float qf;
-  // the query dims of lane (m = 4h + part, g) for sequence b: 32g + 8kb ..
-  // 32g + 8kb + 7 of head h, in two float4
-  auto query_rows = [&](int b, float4 (&raw)[NH][4][2]) {
+  // the query dims of lane (m = 4h + part, g) for sequence b: 32F g + 8kb
+  // .. 32F g + 8kb + 7 of head h, in two float4
+  auto query_rows = [&](int b, float4 (&raw)[NH][4 * F][2]) {
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       const int hq = 4 * r + (ln >> 2);
       const float* qrow = p.q + ((int64_t)b * p.hq + h0 + (hq < gw ? hq : 0)) * D;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        raw[r][kb][0] = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb);
-        raw[r][kb][1] = *reinterpret_cast<const float4*>(qrow + 32 * lg + 8 * kb + 4);
+      for (int kb = 0; kb < 4 * F; ++kb) {
+        raw[r][kb][0] = *reinterpret_cast<const float4*>(qrow + 32 * F * lg + 8 * kb);
+        raw[r][kb][1] = *reinterpret_cast<const float4*>(qrow + 32 * F * lg + 8 * kb + 4);
       }
     }
   };
-  auto query_image = [&](const float4 (&raw)[NH][4][2]) {
+  auto query_image = [&](const float4 (&raw)[NH][4 * F][2]) {
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       const int hq = 4 * r + (ln >> 2), part = ln & 3;
       const bool ok = hq < gw && part < 3;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 4 * F; ++kb) {
         const float4 a = raw[r][kb][0];
         const float4 c = raw[r][kb][1];
         const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
@@ -330,7 +332,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
     qf = p.sm_scale * kLog2e;
   };
   auto load_query = [&](int b) {
-    float4 raw[NH][4][2];
+    float4 raw[NH][4 * F][2];
     query_rows(b, raw);
     query_image(raw);
   };
@@ -359,9 +361,9 @@ void decode_tq_fp8_kernel(DecodeParams p) {
           out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
                          kvl * g + hq0 + hh) * (D + 1);
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        float* dst = out + 8 * ln;
+        float* dst = out + 8 * F * ln;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = (acc[8 * r + i][lane] + zt) * inv;
+        for (int i = 0; i < 8 * F; ++i) dst[i] = (acc[8 * F * r + i][lane] + zt) * inv;
         if (ln == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
@@ -402,8 +404,8 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < NH; ++r) c[r] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        // key bytes 8kb .. 8kb + 7 of this lane's 32 -> 8 bf16
+      for (int kb = 0; kb < 4 * F; ++kb) {
+        // key bytes 8kb .. 8kb + 7 of this lane's 32F -> 8 bf16
         const v4u kw = X.kraw[s][kb >> 1];
         const uint32_t w0 = kw[2 * (kb & 1)], w1 = kw[2 * (kb & 1) + 1];
         const v2bf16 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
@@ -489,13 +491,13 @@ void decode_tq_fp8_kernel(DecodeParams p) {
           if (part < 3) a4 = *reinterpret_cast<const uint4*>(&pbf[wave][r][part][hd][32 * h + 8 * lg]);
           pa[r] = __builtin_bit_cast(v8bf16, v4u{a4.x, a4.y, a4.z, a4.w});
         }
-        // ob[t][i]: byte i of value bytes 8n .. 8n+7 of tokens 4t .. 4t+3
-        // of this lane's eight (4x4 byte transposes)
-        uint32_t ob[2][8];
+        // ob[t][i]: byte i of value bytes 8F n .. 8F n + 8F - 1 of tokens 4t
+        // .. 4t+3 of this lane's eight (4x4 byte transposes)
+        uint32_t ob[2][8 * F];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
+          for (int q = 0; q < 2 * F; ++q) {
             const uint32_t d0 = X.v8[h][4 * t][q], d1 = X.v8[h][4 * t + 1][q];
             const uint32_t d2 = X.v8[h][4 * t + 2][q], d3 = X.v8[h][4 * t + 3][q];
             const uint32_t x01l = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
@@ -508,9 +510,9 @@ void decode_tq_fp8_kernel(DecodeParams p) {
             ob[t][4 * q + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
           }
         }
-        // B of MFMA i: column n = value dim 8n + i, rows = the 32 tokens
+        // B of MFMA i: column n = value dim 8F n + i, rows = the 32 tokens
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 8 * F; ++i) {
           const v2bf16 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, false);
           const v2bf16 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[0][i], 1.0f, true);
           const v2bf16 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ob[1][i], 1.0f, false);
@@ -577,11 +579,14 @@ void decode_tq_fp8_kernel(DecodeParams p) {
         pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int fh = 0; fh < 2 * F; ++fh) {
+        // dims 8F n + 8f + 4h .. +3 (value dword f, its bytes 2h, 2h + 1)
+        const int f = fh >> 1, h = fh & 1;
         uint32_t vb[4][4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t w0 = X.vraw[0][kk], w1 = X.vraw[1][kk], w2 = X.vraw[2][kk], w3 = X.vraw[3][kk];
+          const uint32_t w0 = X.vraw[0][kk][f], w1 = X.vraw[1][kk][f], w2 = X.vraw[2][kk][f],
+                         w3 = X.vraw[3][kk][f];
           const uint32_t sel = h ? 0x07030602u : 0x05010400u;
           const uint32_t x01 = __builtin_amdgcn_perm(w1, w0, sel);
           const uint32_t x23 = __builtin_amdgcn_perm(w3, w2, sel);
@@ -597,7 +602,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
           const v4i vbi = v4i{(int)vb[i][0], (int)vb[i][1], (int)vb[i][2], (int)vb[i][3]};
 #pragma unroll
           for (int r = 0; r < NH; ++r)
-            cacc[r][4 * h + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * h + i], 0, 0, 0);
+            cacc[r][4 * fh + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(pa[r], vbi, cacc[r][4 * fh + i], 0, 0, 0);
         }
       }
       wave_sync();
@@ -606,7 +611,7 @@ void decode_tq_fp8_kernel(DecodeParams p) {
 
   // The range's first query rows are requested now: their loads overlap
   // the tile table's, so tile 0 does not wait behind the query set-up.
-  float4 q0[NH][4][2];
+  float4 q0[NH][4 * F][2];
   if constexpr (kEarlyQuery) {
     int bl = 0, bh = p.B - 1;  // the sequence of tile lo, as the table finds it
     while (bl < bh) {
@@ -679,20 +684,20 @@ void decode_tq_fp8_kernel(DecodeParams p) {
   emit();
 }
 
-template <int W, int NH>
+template <int W, int NH, int DD = 128>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
   if (p.val_fmt == VF_FP8) {
     if (wide)
-      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, true, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
     else
-      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, true, false, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
   } else {
     if (wide)
-      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, true>), dim3(blocks), dim3(64 * W), lds, st, p);
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, true, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
     else
-      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, false>), dim3(blocks), dim3(64 * W), lds, st, p);
+      hipLaunchKernelGGL((decode_tq_fp8_kernel<W, NH, false, false, DD>), dim3(blocks), dim3(64 * W), lds, st, p);
   }
   return hipGetLastError();
 }
@@ -704,7 +709,8 @@ constexpr bool kOneWavePerKvHead = true;
 }  // namespace
 
 hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
-  if (p.d != D || p.key_fmt != KF_FP8 || (p.val_fmt != VF_U4 && p.val_fmt != VF_FP8) || p.g > 8)
+  if ((p.d != 128 && p.d != 256) || p.key_fmt != KF_FP8 || (p.val_fmt != VF_U4 && p.val_fmt != VF_FP8) ||
+      p.g > 8)
     return hipErrorNotSupported;
   // slot bytes below 2 GiB take 32-bit buffer offsets, larger caches the
   // 64-bit variant (whose zero page must cover every kv head's slot)
@@ -716,6 +722,18 @@ hipError_t launch_decode_tq_mfma(DecodeParams& p, hipStream_t st) {
   if (cap >= ((int64_t)1 << 30) || p.B > 4096) return hipErrorNotSupported;
   const int64_t tiles_ub = (int64_t)p.B * ((cap + kTileTokens - 1) / kTileTokens + p.splits);
   if (tiles_ub >= ((int64_t)1 << 30)) return hipErrorNotSupported;
+  if (p.d == 256) {
+    // D = 256: four query heads per wave (ceil(g / 4) waves per kv head),
+    // one wave per SIMD, at most 4 waves per workgroup and per CU
+    p.wgh = balance_heads_per_wg(p.hk, p.g, 4);
+    const int64_t nw = balance_max_wgs(p.hk, p.g, kWaveBudget / 2);
+    p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    switch (p.wgh * ((p.g + 3) / 4)) {
+      case 1: return launch<1, 1, 256>(p, st, wide);
+      case 2: return launch<2, 1, 256>(p, st, wide);
+      default: return launch<4, 1, 256>(p, st, wide);
+    }
+  }
   if (p.g > 4 && kOneWavePerKvHead) {
     // one wave per kv head at one wave per SIMD: at most 4 waves per
     // workgroup and per CU (the piece region, sized for two waves per kv

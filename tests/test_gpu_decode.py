@@ -632,6 +632,29 @@ def test_tq_centroid_keys_fp8_values_shapes(shape, key_fmt):
     assert_close(got, ref, lse, ref_lse, "%s %s" % (shape, fmt))
 
 
+@pytest.mark.parametrize("val_fmt", [oracle.VAL_U4, oracle.VAL_FP8], ids=["u4", "fp8"])
+def test_tq_fp8_keys_head_dim_256(val_fmt):
+    """FP8 keys at D = 256 on the FP8-key matrix-core kernel (four query
+    heads per wave): random slots, g = 1, 4, 8, split counts 1 .. 256, the
+    64-bit and generic paths alongside, and oracle-encoded caches."""
+    fmt = (oracle.KEY_FP8, val_fmt)
+    for (B, hq, hk, seq, S) in [(2, 8, 8, [300, 1], 4), (3, 16, 4, [129, 0, 640], 5),
+                                (2, 16, 2, [1000, 65], 7)]:
+        w = W.custom_decode_workload(1000 + hq + hk + S + val_fmt, B, hq, hk, 256, 16, S, seq, 3, "bf16")
+        cache = W.random_tq_cache(w, *fmt, oracle.tq_slot_bytes(256, *fmt))
+        q = W.query(w) / 16  # random codes reach 448: keep scores O(10)
+        ref, ref_lse = _oracle_tq(w, q, cache, None, *fmt, splits=0)
+        for Sx in (1, S, 256):
+            for flags in (0, tq.FLAG_WIDE, tq.FLAG_GENERIC):
+                got, lse = gpu_tq_decode(w, q, cache, None, *fmt, num_splits=Sx, flags=flags)
+                assert_close(got, ref, lse, ref_lse, "%s hq=%d S=%d flags=%d" % (fmt, hq, Sx, flags))
+        cache, cen = tq_case(w, *fmt)
+        q = W.query(w, bf16_valued=True)
+        ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt)
+        assert_close(got, ref, lse, ref_lse, "encoded %s hq=%d" % (fmt, hq))
+
+
 # ---------------------------------------------------------------------------
 # FP8 keys + FP8 values (matrix-core path for D = 128, g <= 8)
 
