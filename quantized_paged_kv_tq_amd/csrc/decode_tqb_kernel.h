@@ -1057,7 +1057,8 @@ hipError_t launch_bits(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles
 // dims, and FP8 values.
 hipError_t launch_decode_tqb_d256(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
 hipError_t launch_decode_tqb_ncorr(DecodeParams& p, hipStream_t st, int64_t tiles_ub);
-// FP8 values (head dim 128, no norm correction)
+// FP8 values (head dim 128; the norm-corrected read with them goes to
+// launch_decode_tqb_ncorr)
 hipError_t launch_decode_tqb_fp8v(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
 
 }  // namespace tqk

@@ -11,8 +11,8 @@ hipError_t launch_decode_tqb_mfma(DecodeParams& p, hipStream_t st) {
   if ((p.d != 128 && p.d != 256) || (p.key_fmt != KF_MSE3 && !k4) ||
       (p.val_fmt != VF_U3 && !v4 && !v8) || p.g > 8)
     return hipErrorNotSupported;
-  // FP8 values: head dim 128, without the norm correction
-  if (v8 && (p.d != 128 || p.norm_correction)) return hipErrorNotSupported;
+  // FP8 values: head dim 128
+  if (v8 && p.d != 128) return hipErrorNotSupported;
   const int kb = k4 ? 4 : 3, vb = v8 ? 8 : (v4 ? 4 : 3);
   if (p.kps != p.d * kb / 8 + 2 || p.vdb != p.d * vb / 8 || p.slot_bytes % 16 != 0)
     return hipErrorNotSupported;

@@ -575,9 +575,12 @@ def test_tq_centroid_head_dim_256_random_slots(fmt, antisymmetric):
             assert_close(got, ref, lse, ref_lse, "random slots %s S=%d flags=%d" % (fmt, S, flags))
 
 
+NC_FMTS = ALL_C_FMTS + [(oracle.KEY_MSE3, oracle.VAL_FP8), (oracle.KEY_MSE4, oracle.VAL_FP8)]
+
+
 @pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
-@pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
+@pytest.mark.parametrize("fmt", NC_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3", "mse3_fp8", "mse4_fp8"])
 def test_tq_centroid_norm_correction(fmt, antisymmetric, d):
     """The norm-corrected read on the matrix-core kernel (the sum of c[idx]^2
     over a token's dims from parity-plane counts): random slots, random
