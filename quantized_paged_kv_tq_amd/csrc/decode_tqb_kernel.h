@@ -130,6 +130,11 @@ __device__ __forceinline__ uint32_t unpack4x4(uint32_t x, int h) {
   const uint32_t t = __builtin_amdgcn_perm(x, x, h ? 0x03030202u : 0x01010000u);
   return ((t >> 4) & 0x0F000F00u) | (t & 0x000F000Fu);
 }
+// the subset of index bits of odd Walsh plane i: the single bits, then
+// b0^b1^b2 (and, with 4 bits, b0^b1^b3, b0^b2^b3, b1^b2^b3)
+__host__ __device__ constexpr int odd_plane(int i) {
+  return i == 0 ? 1 : i == 1 ? 2 : i == 2 ? 4 : i == 3 ? 7 : i == 4 ? 8 : i == 5 ? 11 : i == 6 ? 13 : 14;
+}
 // bits [bit, bit + 12) of the little-endian value w
 template <int N>
 __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[N], int bit) {
@@ -227,6 +232,23 @@ void decode_tqb_kernel(DecodeParams p) {
       // (the prologue's barriers order these stores before any read)
     }
   }
+  // Folded antisymmetric scores (kFold): each odd Walsh plane S_i gets its
+  // own query image, the query scaled by gq_i = ga_{S_i} / max |ga|, so one
+  // accumulator sums all planes' products and a token block takes one
+  // digit recombination per row set instead of one per plane:
+  //   sum_i ga_{S_i} (q . P_{S_i}) = gmax * sum_i q_i . P_{S_i},  q_i = gq_i q
+  // (q_i rounded to integers at the query's 2^E scale, an error of 2^-27 of
+  // the largest query element per dim and plane).
+  constexpr bool kFold = KB == 3 && NH == 2 && DD == 128 && !NCORR;
+  constexpr int NPF = KB == 3 ? 4 : 8;  // odd Walsh planes
+  float gsum = 0.0f, gmax = 0.0f, gq[kFold ? NPF : 1];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) {
+    gsum += ga[odd_plane(i)];
+    gmax = fmaxf(gmax, fabsf(ga[odd_plane(i)]));
+  }
+#pragma unroll
+  for (int i = 0; i < (kFold ? NPF : 1); ++i) gq[i] = gmax > 0.0f ? ga[odd_plane(i)] / gmax : 0.0f;
 
   // ---- sequence lengths and the prefix sums of their tile counts ----
   const int N = balance_prologue<NT>(p, prefix, prefix + p.B + 1, scan);
@@ -404,6 +426,7 @@ void decode_tqb_kernel(DecodeParams p) {
   // bb (KB = 3), or of dim 32F g + 16kc + 8(j/2) + 2bb + (j%2) (KB = 4: low,
   // then high nibbles of each dword) -- the byte order of the bit planes.
   v4i qa[NH][2 * F];
+  v4i qg[kFold ? NPF : 1][NH][2 * F];  // kFold: the folded images, one per odd Walsh plane
   float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
   // the wave's query rows of sequence b times the rotation signs
   auto query_rows = [&](int b, float (&qx)[NHEAD][2 * F]) {
@@ -421,6 +444,7 @@ void decode_tqb_kernel(DecodeParams p) {
   // rotate, scale and split the rows into the MFMA A-operand image
   auto query_image = [&](const float (&qx)[NHEAD][2 * F]) {
     uint8_t* img = reinterpret_cast<uint8_t*>(&qimg[wave][0][0][0][0]);
+    float xr[kFold ? NHEAD : 1][2 * F], scl[kFold ? NHEAD : 1];  // kFold: rotated rows, 2^E
 #pragma unroll
     for (int hh = 0; hh < NHEAD; ++hh) {
       const int r = hh >> 2, hp = hh & 3;
@@ -453,6 +477,11 @@ void decode_tqb_kernel(DecodeParams p) {
       const float amax = group_max<64>(am);
       const int E = amax > 0.0f ? 26 - ((int)((f2u(amax) >> 23) & 0xFF) - 127) : 0;
       const float sc = exp2i(E);
+      if constexpr (kFold) {
+        scl[hh] = sc;
+#pragma unroll
+        for (int e = 0; e < 2 * F; ++e) xr[hh][e] = x[e];
+      }
       float dsum[4];
 #pragma unroll
       for (int e = 0; e < 2 * F; ++e) {
@@ -488,6 +517,46 @@ void decode_tqb_kernel(DecodeParams p) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
         qa[r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
       }
+    if constexpr (kFold) {
+      // the folded images, one at a time through the same LDS area
+      // byte of digit pc of dim lane + 64 e of head hh in the image
+      auto img_at = [&](int hh, int e, int pc) -> uint8_t& {
+        const int r = hh >> 2, hp = hh & 3;
+        const int dim = lane + 64 * e;
+        const int gg = dim / (32 * F), o = dim % (32 * F);
+        const int kc = o >> 4;
+        const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
+        const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
+        const int L = 16 * gg + 4 * hp + pc;
+        return img[(((r * 2 * F + kc) * 64 + L) * 4 + j) * 4 + bb];
+      };
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        wave_sync();  // the previous image is read before it is overwritten
+#pragma unroll
+        for (int hh = 0; hh < NHEAD; ++hh) {
+          const float s = scl[hh] * gq[i];
+#pragma unroll
+          for (int e = 0; e < 2 * F; ++e) {
+            int v = (int)__builtin_rintf(xr[hh][e] * s);
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc) {
+              const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
+              v = (v - dk) >> 7;
+              img_at(hh, e, pc) = (uint8_t)(dk & 0xFF);
+            }
+          }
+        }
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+#pragma unroll
+          for (int kc = 0; kc < 2 * F; ++kc) {
+            const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
+            qg[i][r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
+          }
+      }
+    }
   };
   auto load_query = [&](int b) {
     float qx[NHEAD][2 * F];
@@ -621,7 +690,51 @@ void decode_tqb_kernel(DecodeParams p) {
       };
       float dot[NH];
       float t[NH];
-      if (anti) {
+      if (kFold && anti) {
+        // all odd planes into one accumulator, each against its folded image
+        v4i c[NH];
+#pragma unroll
+        for (int r = 0; r < NH; ++r) c[r] = v4i{0, 0, 0, 0};
+        auto fold_plane = [&](auto sel) {
+          constexpr int I = decltype(sel)::value;
+          constexpr int S = odd_plane(I);
+#pragma unroll
+          for (int kc = 0; kc < 2 * F; ++kc) {
+            uint32_t pl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              uint32_t x;
+              if constexpr (KB == 4) x = X.kraw[s][2 * kc + (j >> 1)];
+              else x = ix[4 * kc + j];
+              uint32_t m = 0u;
+#pragma unroll
+              for (int k = 0; k < KB; ++k)
+                if ((S >> k) & 1) m ^= x >> k;
+              pl[j] = ((KB == 4 && (j & 1)) ? m >> 4 : m) & 0x01010101u;
+            }
+            const v4i bpl = v4i{(int)pl[0], (int)pl[1], (int)pl[2], (int)pl[3]};
+#pragma unroll
+            for (int r = 0; r < NH; ++r)
+              c[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qg[kFold ? I : 0][r][kc], bpl, c[r], 0, 0, 0);
+          }
+        };
+        fold_plane(std::integral_constant<int, 0>{});
+        fold_plane(std::integral_constant<int, 1>{});
+        fold_plane(std::integral_constant<int, 2>{});
+        fold_plane(std::integral_constant<int, 3>{});
+        if constexpr (NPF == 8) {
+          fold_plane(std::integral_constant<int, 4>{});
+          fold_plane(std::integral_constant<int, 5>{});
+          fold_plane(std::integral_constant<int, 6>{});
+          fold_plane(std::integral_constant<int, 7>{});
+        }
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+          const float u = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf((float)c[r].w, 128.0f, (float)c[r].z), 128.0f,
+                                                        (float)c[r].y), 128.0f, (float)c[r].x);
+          dot[r] = __builtin_fmaf(gsum, qsum[r], -2.0f * gmax * u);
+        }
+      } else if (anti) {
         // odd Walsh terms: the single bits and (KB = 3) b0^b1^b2 or (KB = 4)
         // the four parities of three bits
         float tw[NH];
