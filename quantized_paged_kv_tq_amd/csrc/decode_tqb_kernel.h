@@ -147,11 +147,23 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[N], int bit) {
 // operands of a tile are unpacked once and serve all 4 * NH heads. NH = 2
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
-template <int W, int NH, bool WIDE, int KB, int VB, int DD, bool NCORR>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(NH == 1 && DD == 128 ? 2 : 1)))
+//
+// HALF (g = 5 .. 8, D = 128): two waves per kv head, each with both row sets
+// and half of the head dims (wave hf: key and value dims 64 hf .. 64 hf + 63),
+// so each unpacks half of every tile; they add their partial scores through
+// LDS once per tile (one workgroup barrier), then run the same softmax. Each
+// wave fits 256 registers, so two workgroups share a CU and their waves hide
+// each other's latency.
+template <int W, int NH, bool WIDE, int KB, int VB, int DD, bool NCORR, bool HALF = false>
+__global__ __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu((NH == 1 && DD == 128) || HALF ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
   constexpr int D = DD;      // head dim, 128 or 256
   constexpr int F = D / 128;  // a lane's dims per 16-lane group and token: 32 F keys, 8 F values
+  static_assert(!HALF || (DD == 128 && NH == 2 && !NCORR && VB != 8), "half-dim waves: D = 128, g > 4");
+  constexpr int KC = HALF ? 1 : 2 * F;   // 64-dim MFMA chunks of a wave's key dims
+  constexpr int VDL = HALF ? 4 : 8 * F;  // value dims per lane
+  constexpr int FH = VDL / 4;            // groups of four value dims per lane
   using L = SlotLayout<KB, VB, DD>;
   constexpr uint32_t kNormOff = L::kNormOff, kValOff = L::kValOff, kScaleOff = L::kScaleOff;
   constexpr int NC = 1 << KB;  // centroids
@@ -161,14 +173,16 @@ void decode_tqb_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t p8[V8 ? 1 : W][NH][4][4][16];  // weight digit planes
   // V8: bf16 parts of the weights, [part][head][token] per row set
   __shared__ __attribute__((aligned(16))) uint16_t pbf[V8 ? W : 1][NH][3][4][64];
-  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][2 * F][64][4];  // query digit image
+  __shared__ __attribute__((aligned(16))) uint32_t qimg[W][NH][KC][64][4];  // query digit image
   // byte offset of kv head 0's slot of each token of the chunk's tiles
   // (kMaskedByte for masked tokens and the prefetch row past the end)
   using Off = typename std::conditional<WIDE, int64_t, uint32_t>::type;
   __shared__ __attribute__((aligned(16))) Off tok_rows[kChunk + 1][64];
   __shared__ int4 tinfo[kChunk];
   __shared__ int scan[W];
-  __shared__ float accl[W][NH * 8 * F][64];  // fp32 value accumulators, lane-major
+  __shared__ float accl[W][NH * VDL][64];  // fp32 value accumulators, lane-major
+  // HALF: partial scores [tile parity][wave][lane][4 r + s]
+  __shared__ __attribute__((aligned(16))) float xs[HALF ? 2 : 1][HALF ? W : 1][64][HALF ? 4 * NH : 1];
   extern __shared__ int prefix[];  // [B + 1] tile prefix sums, then [B] lengths
 
   const int tid = threadIdx.x;
@@ -179,8 +193,10 @@ void decode_tqb_kernel(DecodeParams p) {
   const int grp = blockIdx.x / p.nw;
   const int wg = blockIdx.x - grp * p.nw;
   const int qs_n = (p.g + NHEAD - 1) / NHEAD;
-  const int kvl = wave / qs_n;
-  const int qsub = wave - kvl * qs_n;
+  const int hf = HALF ? (wave & 1) : 0;  // HALF: the wave's half of the head dims
+  const int wv = HALF ? (wave >> 1) : wave;
+  const int kvl = wv / qs_n;
+  const int qsub = wv - kvl * qs_n;
   const int kvh = grp * p.wgh + kvl;
   const int g = p.g;
   const int hq0 = NHEAD * qsub;
@@ -286,16 +302,19 @@ void decode_tqb_kernel(DecodeParams p) {
   // kValOff + VB F n; one dword load per 8 dims from byte kValOff + VB F n +
   // VB f (buffer loads take byte offsets, dword loads need not be 4-byte
   // aligned)
-  const uint32_t vbyte = kValOff + (uint32_t)(VB * F) * (uint32_t)ln;
+  // (HALF: dims 64 hf + 4n .. +3, 3-bit ones from bit 4 of the dword when n is odd)
+  const uint32_t vbyte = HALF ? kValOff + (VB == 3 ? 24u * hf + ((3u * ln) >> 1) : 32u * hf + 2u * ln)
+                              : kValOff + (uint32_t)(VB * F) * (uint32_t)ln;
+  const uint32_t vsh = (HALF && VB == 3 && (ln & 1)) ? 4u : 0u;
 
   // ---- registers of one tile ----
   // key bytes [4 KB F g, 4 KB F (g + 1)) of tokens 16s + n (dims 32F g ..
   // 32F g + 32F - 1); the norm word and scale/zero words of token `lane`;
   // the dwords starting at value bytes VB F n + VB f of tokens 16s + 4g + k
   struct Buf {
-    uint32_t kraw[4][KB * F];
+    uint32_t kraw[4][HALF ? 2 : KB * F];
     uint32_t nw, sz0, sz1, live;
-    uint32_t vraw[V8 ? 1 : 4][4][F];
+    uint32_t vraw[V8 ? 1 : 4][4][HALF ? 1 : F];
     uint32_t v8[V8 ? 2 : 1][8][2];  // V8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
   };
   const uint32_t kvh_off = (uint32_t)kvh * sb;
@@ -321,7 +340,7 @@ void decode_tqb_kernel(DecodeParams p) {
         for (int kk = 0; kk < 4; ++kk) {
           const Off o = slot_of(k, 16 * s + 4 * lg + kk);
 #pragma unroll
-          for (int f = 0; f < F; ++f) B.vraw[s][kk][f] = ld32(o + vbyte + (uint32_t)(VB * f));
+          for (int f = 0; f < (HALF ? 1 : F); ++f) B.vraw[s][kk][f] = ld32(o + vbyte + (uint32_t)(VB * f));
         }
       }
     }
@@ -332,7 +351,17 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int s = 0; s < 4; ++s) {
       const Off o = slot_of(k, 16 * s + ln);
       B.live |= (masked(o) ? 0u : 1u) << s;
-      if constexpr (KB == 4) {
+      if constexpr (HALF) {
+        // 16 dims: 8 bytes of 4-bit keys, 6 of 3-bit ones (two dwords)
+        if constexpr (KB == 4) {
+          const v2u kw = ld64(o + 32u * hf + 8u * lg);
+          B.kraw[s][0] = kw.x;
+          B.kraw[s][1] = kw.y;
+        } else {
+          B.kraw[s][0] = ld32(o + 24u * hf + 6u * lg);
+          B.kraw[s][1] = ld32(o + 24u * hf + 6u * lg + 4u);
+        }
+      } else if constexpr (KB == 4) {
 #pragma unroll
         for (int f = 0; f < F; ++f) {
           const v4u kw = ld128(o + (uint32_t)(16 * F) * lg + 16u * f);
@@ -363,7 +392,7 @@ void decode_tqb_kernel(DecodeParams p) {
   // ---- online softmax state of the current segment ----
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
   float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
-  v4i cacc[NH][V8 ? 1 : 8 * F];
+  v4i cacc[NH][V8 ? 1 : VDL];
   v4f facc[NH][V8 ? 8 : 1];  // V8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
@@ -376,8 +405,8 @@ void decode_tqb_kernel(DecodeParams p) {
       l[r] = 0.0f;
       zacc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8 * F; ++i) {
-        acc[8 * F * r + i][lane] = 0.0f;
+      for (int i = 0; i < VDL; ++i) {
+        acc[VDL * r + i][lane] = 0.0f;
         if constexpr (V8) facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         else cacc[r][i] = v4i{0, 0, 0, 0};
       }
@@ -395,22 +424,22 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int r = 0; r < NH; ++r) {
       if (!empty) {
 #pragma unroll
-        for (int i = 0; i < 8 * F; ++i) {
+        for (int i = 0; i < VDL; ++i) {
           if constexpr (V8) {
             const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
-            acc[8 * F * r + i][lane] = (acc[8 * F * r + i][lane] + val) * alpha[r];
+            acc[VDL * r + i][lane] = (acc[VDL * r + i][lane] + val) * alpha[r];
             facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
           } else {
             const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
             const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
             const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
-            acc[8 * F * r + i][lane] = __builtin_fmaf(val, pinv, acc[8 * F * r + i][lane]) * alpha[r];
+            acc[VDL * r + i][lane] = __builtin_fmaf(val, pinv, acc[VDL * r + i][lane]) * alpha[r];
             cacc[r][i] = v4i{0, 0, 0, 0};
           }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8 * F; ++i) acc[8 * F * r + i][lane] *= alpha[r];
+        for (int i = 0; i < VDL; ++i) acc[VDL * r + i][lane] *= alpha[r];
       }
       l[r] *= alpha[r];
       zacc[r] *= alpha[r];
@@ -425,8 +454,8 @@ void decode_tqb_kernel(DecodeParams p) {
   // piece, g), dword j, byte bb holds the digit of dim 32F g + 16kc + 4j +
   // bb (KB = 3), or of dim 32F g + 16kc + 8(j/2) + 2bb + (j%2) (KB = 4: low,
   // then high nibbles of each dword) -- the byte order of the bit planes.
-  v4i qa[NH][2 * F];
-  v4i qg[kFold ? NPF : 1][NH][2 * F];  // kFold: the folded images, one per odd Walsh plane
+  v4i qa[NH][KC];
+  v4i qg[kFold ? NPF : 1][NH][KC];  // kFold: the folded images, one per odd Walsh plane
   float qsum[NH], qf[NH];  // this lane's head 4r + lg: sum of the scaled query, score scale
   // the wave's query rows of sequence b times the rotation signs
   auto query_rows = [&](int b, float (&qx)[NHEAD][2 * F]) {
@@ -482,12 +511,13 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 2 * F; ++e) xr[hh][e] = x[e];
       }
-      float dsum[4];
+      float dsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int e = 0; e < 2 * F; ++e) {
+        if (HALF && e != hf) continue;  // HALF: the wave's dims are 64 hf + lane
         const int dim = lane + 64 * e;
         int v = (int)__builtin_rintf(x[e] * sc);
-        const int gg = dim / (32 * F), o = dim % (32 * F);
+        const int gg = HALF ? lane >> 4 : dim / (32 * F), o = HALF ? lane & 15 : dim % (32 * F);
         const int kc = o >> 4;
         const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
         const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
@@ -496,8 +526,8 @@ void decode_tqb_kernel(DecodeParams p) {
           const int dk = (pc < 3) ? (((v + 64) & 127) - 64) : v;
           v = (v - dk) >> 7;
           const int L = 16 * gg + 4 * hp + pc;
-          img[(((r * 2 * F + kc) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
-          dsum[pc] = (e ? dsum[pc] : 0.0f) + (float)dk;
+          img[(((r * KC + kc) * 64 + L) * 4 + j) * 4 + bb] = (uint8_t)(dk & 0xFF);
+          dsum[pc] += (float)dk;
         }
       }
       float t[4];
@@ -513,7 +543,7 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < NH; ++r)
 #pragma unroll
-      for (int kc = 0; kc < 2 * F; ++kc) {
+      for (int kc = 0; kc < KC; ++kc) {
         const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
         qa[r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
       }
@@ -523,12 +553,12 @@ void decode_tqb_kernel(DecodeParams p) {
       auto img_at = [&](int hh, int e, int pc) -> uint8_t& {
         const int r = hh >> 2, hp = hh & 3;
         const int dim = lane + 64 * e;
-        const int gg = dim / (32 * F), o = dim % (32 * F);
+        const int gg = HALF ? lane >> 4 : dim / (32 * F), o = HALF ? lane & 15 : dim % (32 * F);
         const int kc = o >> 4;
         const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
         const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
         const int L = 16 * gg + 4 * hp + pc;
-        return img[(((r * 2 * F + kc) * 64 + L) * 4 + j) * 4 + bb];
+        return img[(((r * KC + kc) * 64 + L) * 4 + j) * 4 + bb];
       };
 #pragma unroll
       for (int i = 0; i < NPF; ++i) {
@@ -538,6 +568,7 @@ void decode_tqb_kernel(DecodeParams p) {
           const float s = scl[hh] * gq[i];
 #pragma unroll
           for (int e = 0; e < 2 * F; ++e) {
+            if (HALF && e != hf) continue;
             int v = (int)__builtin_rintf(xr[hh][e] * s);
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc) {
@@ -551,7 +582,7 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < NH; ++r)
 #pragma unroll
-          for (int kc = 0; kc < 2 * F; ++kc) {
+          for (int kc = 0; kc < KC; ++kc) {
             const uint4 w4 = *reinterpret_cast<const uint4*>(&qimg[wave][r][kc][lane][0]);
             qg[i][r][kc] = v4i{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w};
           }
@@ -588,10 +619,10 @@ void decode_tqb_kernel(DecodeParams p) {
           out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
                          kvl * g + hq0 + hh) * (D + 1);
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        float* dst = out + 8 * F * ln;
+        float* dst = out + (HALF ? 64 * hf + 4 * ln : 8 * F * ln);
 #pragma unroll
-        for (int i = 0; i < 8 * F; ++i) dst[i] = (acc[8 * F * r + i][lane] + zt) * inv;
-        if (ln == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
+        for (int i = 0; i < VDL; ++i) dst[i] = (acc[VDL * r + i][lane] + zt) * inv;
+        if (ln == 0 && hf == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
       }
     }
   };
@@ -617,15 +648,16 @@ void decode_tqb_kernel(DecodeParams p) {
 
     // ---- scores: lane (n, g) gets head 4r + g, token 16s + n ----
     float sc[NH][4];
+    float nrs[HALF ? 4 : 1];  // HALF: the key norms, applied after the exchange
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float nrm = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.nw));
       // KB = 3: index bytes of dims 32F g + 4i .. +3 (KB = 4 reads the
       // planes from the packed nibbles)
-      uint32_t ix[KB == 3 ? 8 * F : 1];
+      uint32_t ix[KB == 3 ? 4 * KC : 1];
       if constexpr (KB == 3) {
 #pragma unroll
-        for (int i = 0; i < 8 * F; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
+        for (int i = 0; i < 4 * KC; ++i) ix[i] = unpack3x4(bits12(X.kraw[s], 12 * i));
       }
       // one bit plane at a time: 2F MFMAs (dims 32F g + 16kc + ...), then its
       // share of the dot product; lane (n, g) holds rows 4g..4g+3 = the
@@ -663,7 +695,7 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < NH; ++r) c[r] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int kc = 0; kc < 2 * F; ++kc) {
+        for (int kc = 0; kc < KC; ++kc) {
           uint32_t pl[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -699,7 +731,7 @@ void decode_tqb_kernel(DecodeParams p) {
           constexpr int I = decltype(sel)::value;
           constexpr int S = odd_plane(I);
 #pragma unroll
-          for (int kc = 0; kc < 2 * F; ++kc) {
+          for (int kc = 0; kc < KC; ++kc) {
             uint32_t pl[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -778,7 +810,7 @@ void decode_tqb_kernel(DecodeParams p) {
         auto count = [&](auto sel) -> float {
           v4i c = v4i{0, 0, 0, 0};
 #pragma unroll
-          for (int kc = 0; kc < 2 * F; ++kc)
+          for (int kc = 0; kc < KC; ++kc)
             c = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, plane_words(sel, kc), c, 0, 0, 0);
           return (float)c.x;
         };
@@ -797,10 +829,37 @@ void decode_tqb_kernel(DecodeParams p) {
 #undef TQK_SQ
         nrm *= 1.0f / sqrtf(cs + 1e-16f);
       }
+      if constexpr (HALF) {
+        // this wave's share of the dot products, scaled after the exchange
 #pragma unroll
-      for (int r = 0; r < NH; ++r) sc[r][s] = fminf(dot[r] * (qf[r] * nrm), mask);
+        for (int r = 0; r < NH; ++r) sc[r][s] = dot[r];
+        nrs[s] = nrm;
+      } else {
+#pragma unroll
+        for (int r = 0; r < NH; ++r) sc[r][s] = fminf(dot[r] * (qf[r] * nrm), mask);
+      }
       // one token block at a time (bounds the live bit planes)
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (HALF) {
+      // add the other half's partial scores (a + b in one wave, b + a in the
+      // other: the same sums, so both run the same softmax); the buffer
+      // alternates with the tile, and a wave rewrites one only after the
+      // next tile's barrier, which its partner reaches after reading it
+      float* mine = &xs[gk & 1][wave][lane][0];
+      *reinterpret_cast<float4*>(mine) = make_float4(sc[0][0], sc[0][1], sc[0][2], sc[0][3]);
+      *reinterpret_cast<float4*>(mine + 4) = make_float4(sc[1][0], sc[1][1], sc[1][2], sc[1][3]);
+      __syncthreads();
+      const float* other = &xs[gk & 1][wave ^ 1][lane][0];
+      const float4 o0 = *reinterpret_cast<const float4*>(other);
+      const float4 o1 = *reinterpret_cast<const float4*>(other + 4);
+      const float po[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float mask = ((X.live >> s) & 1u) ? INFINITY : -INFINITY;
+#pragma unroll
+        for (int r = 0; r < NH; ++r) sc[r][s] = fminf((sc[r][s] + po[r][s]) * (qf[r] * nrs[s]), mask);
+      }
     }
     issue_v(Y, k + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -967,7 +1026,7 @@ void decode_tqb_kernel(DecodeParams p) {
       pa[r] = v4i{(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w};
     }
 #pragma unroll
-    for (int fh = 0; fh < 2 * F; ++fh) {
+    for (int fh = 0; fh < FH; ++fh) {
       const int f = fh >> 1, h = fh & 1;
       uint32_t vb[4][4];
 #pragma unroll
@@ -976,7 +1035,8 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t x = X.vraw[s][kk][f];
-          if constexpr (VB == 4) u[s] = unpack4x4(x, h);
+          if constexpr (HALF) u[s] = VB == 4 ? unpack4x4(x, 0) : unpack3x4(x >> vsh);
+          else if constexpr (VB == 4) u[s] = unpack4x4(x, h);
           else u[s] = unpack3x4(h ? x >> 12 : x);
         }
         const uint32_t t01l = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);
@@ -1077,11 +1137,15 @@ void decode_tqb_kernel(DecodeParams p) {
   emit();
 }
 
-template <int W, int NH, int KB, int VB, int DD, bool NCORR>
+template <int W, int NH, int KB, int VB, int DD, bool NCORR, bool HALF = false>
 hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
   const uint32_t blocks = (uint32_t)(p.hk / p.wgh) * (uint32_t)p.nw;
   const size_t lds = balance_lds_bytes(p.B);
-  if constexpr (NCORR) {
+  if constexpr (HALF) {
+    // (narrow addressing only: the caller takes the one-wave layout for wide caches)
+    hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD, false, true>), dim3(blocks), dim3(64 * W),
+                       lds, st, p);
+  } else if constexpr (NCORR) {
     // (the norm-corrected read has no 64-bit variant: the caller declines it)
     hipLaunchKernelGGL((decode_tqb_kernel<W, NH, false, KB, VB, DD, true>), dim3(blocks), dim3(64 * W), lds,
                        st, p);
@@ -1099,6 +1163,11 @@ hipError_t launch(const DecodeParams& p, hipStream_t st, bool wide) {
 // (NH = 2), so each tile's keys and values are unpacked once instead of by
 // two waves.
 constexpr bool kOneWavePerKvHead = true;
+// ... except, with 4-bit keys, uniform values and narrow addressing: there
+// two waves share a kv head by halves of the head dims (HALF), two of them
+// per SIMD. (3-bit keys keep the one-wave layout, whose folded planes come
+// out ahead: the halves repeat the softmax and add a barrier per tile.)
+constexpr bool kHalfDims = true;
 
 template <int KB, int VB, bool NCORR>
 hipError_t launch_layout128(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub);
@@ -1127,6 +1196,16 @@ hipError_t launch_layout(DecodeParams& p, hipStream_t st, bool wide, int64_t til
 template <int KB, int VB, bool NCORR>
 hipError_t launch_layout128(DecodeParams& p, hipStream_t st, bool wide, int64_t tiles_ub) {
   constexpr int DD = 128;
+  if constexpr (!NCORR && VB != 8 && KB == 4) {
+    if (p.g > 4 && kHalfDims && !wide) {
+      // two waves per kv head, at most 4 per workgroup, two per SIMD
+      p.wgh = balance_heads_per_wg(p.hk, p.g, 4);
+      const int64_t nw = balance_max_wgs(p.hk, p.g);
+      p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+      if (p.wgh == 1) return launch<2, 2, KB, VB, DD, false, true>(p, st, false);
+      return launch<4, 2, KB, VB, DD, false, true>(p, st, false);
+    }
+  }
   if (p.g > 4 && kOneWavePerKvHead) {
     // one wave per kv head at one wave per SIMD: at most 4 waves per
     // workgroup and per CU (the piece region, sized for two waves per kv
