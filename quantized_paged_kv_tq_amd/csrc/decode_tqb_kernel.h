@@ -646,6 +646,20 @@ void decode_tqb_kernel(DecodeParams p) {
     // keep every use of X's registers after the next tile's loads
     __builtin_amdgcn_sched_barrier(0);
 
+    // the scale and zero words of tokens 16s + n (kEarlySZ: requested
+    // before the scores, so that their exchange completes under them; the
+    // variants with less register room take them after)
+    constexpr bool kEarlySZ = DD == 128 && !NCORR && !V8;
+    uint32_t szw[V8 ? 1 : 4][2];
+    auto fetch_sz = [&]() {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        szw[s][0] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz0);
+        szw[s][1] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz1);
+      }
+    };
+    if constexpr (kEarlySZ) fetch_sz();
+
     // ---- scores: lane (n, g) gets head 4r + g, token 16s + n ----
     float sc[NH][4];
     float nrs[HALF ? 4 : 1];  // HALF: the key norms, applied after the exchange
@@ -866,10 +880,11 @@ void decode_tqb_kernel(DecodeParams p) {
     float vsc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vz[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float smax = 0.0f;
     if constexpr (!V8) {
+      if constexpr (!kEarlySZ) fetch_sz();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        vsc[s] = half_hi((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz0));
-        vz[s] = half_lo((uint32_t)__builtin_amdgcn_ds_bpermute((16 * s + ln) << 2, (int)X.sz1));
+        vsc[s] = half_hi(szw[s][0]);
+        vz[s] = half_lo(szw[s][1]);
         smax = fmaxf(smax, fabsf(vsc[s]));
       }
     }
