@@ -148,21 +148,23 @@ __device__ __forceinline__ uint32_t bits12(const uint32_t (&w)[N], int bit) {
 // (g = 5 .. 8, one wave per kv head) needs more than 256 registers, so it
 // runs one wave per SIMD.
 //
-// HALF (g = 5 .. 8, D = 128): two waves per kv head, each with both row sets
-// and half of the head dims (wave hf: key and value dims 64 hf .. 64 hf + 63),
+// HALF (g = 5 .. 8): two waves per kv head, each with both row sets and half
+// of the head dims (wave hf: key and value dims D/2 hf .. D/2 hf + D/2 - 1),
 // so each unpacks half of every tile; they add their partial scores through
-// LDS once per tile (one workgroup barrier), then run the same softmax. Each
-// wave fits 256 registers, so two workgroups share a CU and their waves hide
-// each other's latency.
+// LDS once per tile (one workgroup barrier), then run the same softmax. At
+// D = 128 a wave fits 256 registers, so two workgroups share a CU and their
+// waves hide each other's latency; at D = 256 a wave has the shape of the
+// D = 128 one-wave kernel (128 dims, two row sets) and runs alone on its
+// SIMD.
 template <int W, int NH, bool WIDE, int KB, int VB, int DD, bool NCORR, bool HALF = false>
 __global__ __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu((NH == 1 && DD == 128) || HALF ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(DD == 128 && (NH == 1 || HALF) ? 2 : 1)))
 void decode_tqb_kernel(DecodeParams p) {
   constexpr int D = DD;      // head dim, 128 or 256
   constexpr int F = D / 128;  // a lane's dims per 16-lane group and token: 32 F keys, 8 F values
-  static_assert(!HALF || (DD == 128 && NH == 2 && !NCORR && VB != 8), "half-dim waves: D = 128, g > 4");
-  constexpr int KC = HALF ? 1 : 2 * F;   // 64-dim MFMA chunks of a wave's key dims
-  constexpr int VDL = HALF ? 4 : 8 * F;  // value dims per lane
+  static_assert(!HALF || (NH == 2 && !NCORR && VB != 8), "half-dim waves: g > 4, uniform values");
+  constexpr int KC = HALF ? F : 2 * F;       // 64-dim MFMA chunks of a wave's key dims
+  constexpr int VDL = HALF ? 4 * F : 8 * F;  // value dims per lane
   constexpr int FH = VDL / 4;            // groups of four value dims per lane
   using L = SlotLayout<KB, VB, DD>;
   constexpr uint32_t kNormOff = L::kNormOff, kValOff = L::kValOff, kScaleOff = L::kScaleOff;
@@ -302,17 +304,18 @@ void decode_tqb_kernel(DecodeParams p) {
   // kValOff + VB F n; one dword load per 8 dims from byte kValOff + VB F n +
   // VB f (buffer loads take byte offsets, dword loads need not be 4-byte
   // aligned)
-  // (HALF: dims 64 hf + 4n .. +3, 3-bit ones from bit 4 of the dword when n is odd)
-  const uint32_t vbyte = HALF ? kValOff + (VB == 3 ? 24u * hf + ((3u * ln) >> 1) : 32u * hf + 2u * ln)
+  // (HALF: dims 64F hf + 4F n .. +4F-1; at D = 128, 3-bit ones start at
+  // bit 4 of the dword when n is odd)
+  const uint32_t vbyte = HALF ? kValOff + (VB == 3 ? 24u * F * hf + ((3u * F * ln) >> 1) : 32u * F * hf + 2u * F * ln)
                               : kValOff + (uint32_t)(VB * F) * (uint32_t)ln;
-  const uint32_t vsh = (HALF && VB == 3 && (ln & 1)) ? 4u : 0u;
+  const uint32_t vsh = (HALF && F == 1 && VB == 3 && (ln & 1)) ? 4u : 0u;
 
   // ---- registers of one tile ----
   // key bytes [4 KB F g, 4 KB F (g + 1)) of tokens 16s + n (dims 32F g ..
   // 32F g + 32F - 1); the norm word and scale/zero words of token `lane`;
   // the dwords starting at value bytes VB F n + VB f of tokens 16s + 4g + k
   struct Buf {
-    uint32_t kraw[4][HALF ? 2 : KB * F];
+    uint32_t kraw[4][HALF ? (KB * 16 * F + 31) / 32 : KB * F];
     uint32_t nw, sz0, sz1, live;
     uint32_t vraw[V8 ? 1 : 4][4][HALF ? 1 : F];
     uint32_t v8[V8 ? 2 : 1][8][2];  // V8: value bytes 8n .. 8n+7 of tokens 32h + 8g + j
@@ -351,7 +354,19 @@ void decode_tqb_kernel(DecodeParams p) {
     for (int s = 0; s < 4; ++s) {
       const Off o = slot_of(k, 16 * s + ln);
       B.live |= (masked(o) ? 0u : 1u) << s;
-      if constexpr (HALF) {
+      if constexpr (HALF && F == 2) {
+        // 32 dims from byte KB (16 hf + 4 g): 16 bytes of 4-bit keys, 12 of 3-bit ones
+        if constexpr (KB == 4) {
+          const v4u kw = ld128(o + 64u * hf + 16u * lg);
+          B.kraw[s][0] = kw.x;
+          B.kraw[s][1] = kw.y;
+          B.kraw[s][2] = kw.z;
+          B.kraw[s][3] = kw.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 3; ++i) B.kraw[s][i] = ld32(o + 48u * hf + 12u * lg + 4u * i);
+        }
+      } else if constexpr (HALF) {
         // 16 dims: 8 bytes of 4-bit keys, 6 of 3-bit ones (two dwords)
         if constexpr (KB == 4) {
           const v2u kw = ld64(o + 32u * hf + 8u * lg);
@@ -514,10 +529,11 @@ void decode_tqb_kernel(DecodeParams p) {
       float dsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int e = 0; e < 2 * F; ++e) {
-        if (HALF && e != hf) continue;  // HALF: the wave's dims are 64 hf + lane
+        if (HALF && e / F != hf) continue;  // HALF: the wave's dims are 64F hf .. 64F hf + 64F - 1
         const int dim = lane + 64 * e;
         int v = (int)__builtin_rintf(x[e] * sc);
-        const int gg = HALF ? lane >> 4 : dim / (32 * F), o = HALF ? lane & 15 : dim % (32 * F);
+        const int op = HALF ? dim - 64 * F * hf : dim;  // dim within the wave's share
+        const int gg = op / (16 * KC), o = op % (16 * KC);
         const int kc = o >> 4;
         const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
         const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
@@ -553,7 +569,8 @@ void decode_tqb_kernel(DecodeParams p) {
       auto img_at = [&](int hh, int e, int pc) -> uint8_t& {
         const int r = hh >> 2, hp = hh & 3;
         const int dim = lane + 64 * e;
-        const int gg = HALF ? lane >> 4 : dim / (32 * F), o = HALF ? lane & 15 : dim % (32 * F);
+        const int op = HALF ? dim - 64 * F * hf : dim;
+        const int gg = op / (16 * KC), o = op % (16 * KC);
         const int kc = o >> 4;
         const int j = KB == 4 ? 2 * ((o & 15) >> 3) + (o & 1) : (o & 15) >> 2;
         const int bb = KB == 4 ? (o & 7) >> 1 : o & 3;
@@ -568,7 +585,7 @@ void decode_tqb_kernel(DecodeParams p) {
           const float s = scl[hh] * gq[i];
 #pragma unroll
           for (int e = 0; e < 2 * F; ++e) {
-            if (HALF && e != hf) continue;
+            if (HALF && e / F != hf) continue;
             int v = (int)__builtin_rintf(xr[hh][e] * s);
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc) {
@@ -619,7 +636,7 @@ void decode_tqb_kernel(DecodeParams p) {
           out = p.wsp + ((((int64_t)grp * p.nw + wg) * 2 + (seg_first ? 0 : 1)) * (p.wgh * g) +
                          kvl * g + hq0 + hh) * (D + 1);
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        float* dst = out + (HALF ? 64 * hf + 4 * ln : 8 * F * ln);
+        float* dst = out + (HALF ? 64 * F * hf + 4 * F * ln : 8 * F * ln);
 #pragma unroll
         for (int i = 0; i < VDL; ++i) dst[i] = (acc[VDL * r + i][lane] + zt) * inv;
         if (ln == 0 && hf == 0) out[D] = lt > 0.0f ? (mref[r] + __log2f(lt)) * kLn2 : -INFINITY;
@@ -1050,7 +1067,7 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const uint32_t x = X.vraw[s][kk][f];
-          if constexpr (HALF) u[s] = VB == 4 ? unpack4x4(x, 0) : unpack3x4(x >> vsh);
+          if constexpr (HALF && F == 1) u[s] = VB == 4 ? unpack4x4(x, 0) : unpack3x4(x >> vsh);
           else if constexpr (VB == 4) u[s] = unpack4x4(x, h);
           else u[s] = unpack3x4(h ? x >> 12 : x);
         }
@@ -1181,7 +1198,9 @@ constexpr bool kOneWavePerKvHead = true;
 // ... except, with 4-bit keys, uniform values and narrow addressing: there
 // two waves share a kv head by halves of the head dims (HALF), two of them
 // per SIMD. (3-bit keys keep the one-wave layout, whose folded planes come
-// out ahead: the halves repeat the softmax and add a barrier per tile.)
+// out ahead: the halves repeat the softmax and add a barrier per tile.) At
+// D = 256 every key width takes the halves for g = 5 .. 8 with uniform values
+// and narrow addressing.
 constexpr bool kHalfDims = true;
 
 template <int KB, int VB, bool NCORR>
@@ -1197,6 +1216,14 @@ hipError_t launch_layout(DecodeParams& p, hipStream_t st, bool wide, int64_t til
     p.wgh = balance_heads_per_wg(p.hk, p.g, 4);
     const int64_t nw = balance_max_wgs(p.hk, p.g, kWaveBudget / 2);
     p.nw = (int)(tiles_ub < nw ? tiles_ub : nw);
+    if constexpr (!NCORR && VB != 8) {
+      if (p.g > 4 && kHalfDims && !wide) {
+        // the same grid, the two waves of a kv head split by halves of the
+        // head dims instead of by query heads (each unpacks half a tile)
+        if (p.wgh == 1) return launch<2, 2, KB, VB, DD, false, true>(p, st, false);
+        return launch<4, 2, KB, VB, DD, false, true>(p, st, false);
+      }
+    }
     switch (p.wgh * ((p.g + 3) / 4)) {
       case 1: return launch<1, 1, KB, VB, DD, NCORR>(p, st, wide);
       case 2: return launch<2, 1, KB, VB, DD, NCORR>(p, st, wide);

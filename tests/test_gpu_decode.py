@@ -558,6 +558,25 @@ def test_tq_centroid_head_dim_256(fmt, flags):
         assert_close(got, ref, lse, ref_lse, "fmt %s B=%d hq=%d" % (fmt, B, hq))
 
 
+@pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
+def test_tq_centroid_head_dim_256_query_groups_of_five_to_eight(fmt):
+    """D = 256 with g = 5 .. 8, where the two waves of a kv head split the
+    head dims: one and three kv heads (workgroups of one and two kv heads),
+    padded query-head groups, ragged and empty sequences, against the oracle
+    and against the 64-bit variant (which splits by query heads)."""
+    for (B, hq, hk, seq, S) in [(2, 5, 1, [300, 0], 3), (2, 6, 1, [1, 257], 4), (3, 7, 1, [64, 65, 200], 2),
+                                (2, 8, 1, [500, 129], 5), (2, 24, 3, [190, 33], 6)]:
+        w = W.custom_decode_workload(990 + hq + 7 * hk + 3 * fmt[0] + fmt[1], B, hq, hk, 256, 16, S, seq, 3,
+                                     "bf16")
+        cache, cen = tq_case(w, *fmt)
+        q = W.query(w, bf16_valued=True)
+        ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+        got, lse = gpu_tq_decode(w, q, cache, cen, *fmt)
+        assert_close(got, ref, lse, ref_lse, "fmt %s B=%d hq=%d hk=%d" % (fmt, B, hq, hk))
+        got_w, lse_w = gpu_tq_decode(w, q, cache, cen, *fmt, flags=tq.FLAG_WIDE)
+        assert_close(got_w, ref, lse_w, ref_lse, "wide fmt %s B=%d hq=%d hk=%d" % (fmt, B, hq, hk))
+
+
 @pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
 @pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
 def test_tq_centroid_head_dim_256_random_slots(fmt, antisymmetric):
