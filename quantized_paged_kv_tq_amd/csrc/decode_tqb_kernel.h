@@ -408,6 +408,31 @@ void decode_tqb_kernel(DecodeParams p) {
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
   float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
   v4i cacc[NH][V8 ? 1 : VDL];
+  // kBase (one wave per SIMD at D = 128, two or more waves per workgroup, so
+  // that the 16 KB of LDS per wave leaves the CU its four waves): the int32
+  // value sums are never cleared inside the tile loop (a conditional clear
+  // costs a copy of all of them between register files every tile). A flush
+  // or a reset takes their growth since the last one, cacc - cbase in
+  // wrapping int32 (exact while the growth stays below 2^31, which the
+  // 8192-tile flush bound keeps), and moves cbase to cacc.
+  constexpr bool kBase = !V8 && NH == 2 && !HALF && DD == 128 && !NCORR && W >= 2;
+  __shared__ int cbase[kBase ? W : 1][kBase ? NH * VDL * 4 : 1][64];
+  if constexpr (kBase) {
+#pragma unroll
+    for (int r = 0; r < NH; ++r)
+#pragma unroll
+      for (int i = 0; i < VDL; ++i) cacc[r][i] = v4i{0, 0, 0, 0};
+  }
+  auto base_swap = [&](int r, int i) -> v4i {  // cacc - cbase, then cbase = cacc
+    int* b = &cbase[kBase ? wave : 0][kBase ? (VDL * r + i) * 4 : 0][lane];
+    v4i d;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d[c] = (int)((uint32_t)cacc[r][i][c] - (uint32_t)b[64 * c]);
+      b[64 * c] = cacc[r][i][c];
+    }
+    return d;
+  };
   v4f facc[NH][V8 ? 8 : 1];  // V8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
@@ -423,6 +448,7 @@ void decode_tqb_kernel(DecodeParams p) {
       for (int i = 0; i < VDL; ++i) {
         acc[VDL * r + i][lane] = 0.0f;
         if constexpr (V8) facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        else if constexpr (kBase) (void)base_swap(r, i);
         else cacc[r][i] = v4i{0, 0, 0, 0};
       }
     }
@@ -445,11 +471,12 @@ void decode_tqb_kernel(DecodeParams p) {
             acc[VDL * r + i][lane] = (acc[VDL * r + i][lane] + val) * alpha[r];
             facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
           } else {
-            const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
-            const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+            const v4i cd = kBase ? base_swap(r, i) : cacc[r][i];
+            const float e0 = (float)cd.x, e1 = (float)cd.y;
+            const float e2 = (float)cd.z, e3 = (float)cd.w;
             const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
             acc[VDL * r + i][lane] = __builtin_fmaf(val, pinv, acc[VDL * r + i][lane]) * alpha[r];
-            cacc[r][i] = v4i{0, 0, 0, 0};
+            if constexpr (!kBase) cacc[r][i] = v4i{0, 0, 0, 0};
           }
         }
       } else {
