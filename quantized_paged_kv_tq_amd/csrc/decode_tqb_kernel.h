@@ -416,23 +416,14 @@ void decode_tqb_kernel(DecodeParams p) {
   // wrapping int32 (exact while the growth stays below 2^31, which the
   // 8192-tile flush bound keeps), and moves cbase to cacc.
   constexpr bool kBase = !V8 && NH == 2 && !HALF && DD == 128 && !NCORR && W >= 2;
-  __shared__ int cbase[kBase ? W : 1][kBase ? NH * VDL * 4 : 1][64];
+  __shared__ __attribute__((aligned(16))) v4i cbase[kBase ? W : 1][kBase ? NH * VDL : 1][64];
   if constexpr (kBase) {
 #pragma unroll
     for (int r = 0; r < NH; ++r)
 #pragma unroll
       for (int i = 0; i < VDL; ++i) cacc[r][i] = v4i{0, 0, 0, 0};
   }
-  auto base_swap = [&](int r, int i) -> v4i {  // cacc - cbase, then cbase = cacc
-    int* b = &cbase[kBase ? wave : 0][kBase ? (VDL * r + i) * 4 : 0][lane];
-    v4i d;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      d[c] = (int)((uint32_t)cacc[r][i][c] - (uint32_t)b[64 * c]);
-      b[64 * c] = cacc[r][i][c];
-    }
-    return d;
-  };
+  auto base_at = [&](int r, int i) -> v4i& { return cbase[kBase ? wave : 0][kBase ? VDL * r + i : 0][lane]; };
   v4f facc[NH][V8 ? 8 : 1];  // V8: fp32 MFMA sums, rows 4g .. 4g+3 = head g's parts
   int ev = 0;
   float sref = 0.0f;
@@ -448,7 +439,7 @@ void decode_tqb_kernel(DecodeParams p) {
       for (int i = 0; i < VDL; ++i) {
         acc[VDL * r + i][lane] = 0.0f;
         if constexpr (V8) facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        else if constexpr (kBase) (void)base_swap(r, i);
+        else if constexpr (kBase) base_at(r, i) = cacc[r][i];
         else cacc[r][i] = v4i{0, 0, 0, 0};
       }
     }
@@ -464,19 +455,37 @@ void decode_tqb_kernel(DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
       if (!empty) {
+        if constexpr (kBase) {
+          // the sums' growth since the last flush; the row set's bases are
+          // all requested before any is used
+          v4i old[VDL];
 #pragma unroll
-        for (int i = 0; i < VDL; ++i) {
-          if constexpr (V8) {
-            const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
-            acc[VDL * r + i][lane] = (acc[VDL * r + i][lane] + val) * alpha[r];
-            facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-          } else {
-            const v4i cd = kBase ? base_swap(r, i) : cacc[r][i];
+          for (int i = 0; i < VDL; ++i) old[i] = base_at(r, i);
+#pragma unroll
+          for (int i = 0; i < VDL; ++i) {
+            base_at(r, i) = cacc[r][i];
+            v4i cd;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cd[c] = (int)((uint32_t)cacc[r][i][c] - (uint32_t)old[i][c]);
             const float e0 = (float)cd.x, e1 = (float)cd.y;
             const float e2 = (float)cd.z, e3 = (float)cd.w;
             const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
             acc[VDL * r + i][lane] = __builtin_fmaf(val, pinv, acc[VDL * r + i][lane]) * alpha[r];
-            if constexpr (!kBase) cacc[r][i] = v4i{0, 0, 0, 0};
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < VDL; ++i) {
+            if constexpr (V8) {
+              const float val = (facc[r][i].x + facc[r][i].y) + facc[r][i].z;
+              acc[VDL * r + i][lane] = (acc[VDL * r + i][lane] + val) * alpha[r];
+              facc[r][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            } else {
+              const float e0 = (float)cacc[r][i].x, e1 = (float)cacc[r][i].y;
+              const float e2 = (float)cacc[r][i].z, e3 = (float)cacc[r][i].w;
+              const float val = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(e3, 128.0f, e2), 128.0f, e1), 128.0f, e0);
+              acc[VDL * r + i][lane] = __builtin_fmaf(val, pinv, acc[VDL * r + i][lane]) * alpha[r];
+              cacc[r][i] = v4i{0, 0, 0, 0};
+            }
           }
         }
       } else {
