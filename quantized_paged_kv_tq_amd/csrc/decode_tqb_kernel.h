@@ -408,14 +408,16 @@ void decode_tqb_kernel(DecodeParams p) {
   float mref[NH], l[NH], zacc[NH];  // per lane: head 4r + lg of this wave
   float(*acc)[64] = accl[wave];       // acc[8F r + i][lane]
   v4i cacc[NH][V8 ? 1 : VDL];
-  // kBase (one wave per SIMD at D = 128, two or more waves per workgroup, so
-  // that the 16 KB of LDS per wave leaves the CU its four waves): the int32
+  // kBase (one wave per SIMD at D = 128, four waves per workgroup, narrow
+  // addressing: one workgroup fills a CU, so the 16 KB of LDS per wave costs
+  // no occupancy and leaves room for the prefix sums of 4096 sequences;
+  // the 64-bit tile table would not): the int32
   // value sums are never cleared inside the tile loop (a conditional clear
   // costs a copy of all of them between register files every tile). A flush
   // or a reset takes their growth since the last one, cacc - cbase in
   // wrapping int32 (exact while the growth stays below 2^31, which the
   // 8192-tile flush bound keeps), and moves cbase to cacc.
-  constexpr bool kBase = !V8 && NH == 2 && !HALF && DD == 128 && !NCORR && W >= 2;
+  constexpr bool kBase = !V8 && NH == 2 && !HALF && DD == 128 && !NCORR && W == 4 && !WIDE;
   __shared__ __attribute__((aligned(16))) v4i cbase[kBase ? W : 1][kBase ? NH * VDL : 1][64];
   if constexpr (kBase) {
 #pragma unroll

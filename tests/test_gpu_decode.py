@@ -558,6 +558,22 @@ def test_tq_centroid_head_dim_256(fmt, flags):
         assert_close(got, ref, lse, ref_lse, "fmt %s B=%d hq=%d" % (fmt, B, hq))
 
 
+def test_tq_centroid_one_wave_layout_at_the_batch_limit():
+    """3-bit centroid keys and values at g = 8 with four kv heads (one wave
+    per kv head, four per workgroup: the layout whose value sums keep an LDS
+    base) at the largest batch the decode accepts, 4096 sequences of 0 .. 40
+    tokens, every row against the oracle."""
+    rng = np.random.default_rng(4096)
+    seq = [int(x) for x in rng.integers(0, 41, 4096)]
+    fmt = (oracle.KEY_MSE3, oracle.VAL_U3)
+    w = W.custom_decode_workload(4096, 4096, 32, 4, 128, 16, 2, seq, 3, "bf16")
+    cache, cen = tq_case(w, *fmt)
+    q = W.query(w, bf16_valued=True)
+    ref, ref_lse = _oracle_tq(w, q, cache, cen, *fmt)
+    got, lse = gpu_tq_decode(w, q, cache, cen, *fmt)
+    assert_close(got, ref, lse, ref_lse, "B=4096 centroid keys")
+
+
 @pytest.mark.parametrize("fmt", ALL_C_FMTS, ids=["mse3_u3", "mse4_u4", "mse3_u4", "mse4_u3"])
 def test_tq_centroid_head_dim_256_query_groups_of_five_to_eight(fmt):
     """D = 256 with g = 5 .. 8, where the two waves of a kv head split the
