@@ -454,11 +454,13 @@ def test_tq_centroid_bits_random_slots_and_table(fmt, antisymmetric):
 
 
 @pytest.mark.parametrize("antisymmetric", [False, True], ids=["general", "antisymmetric"])
-@pytest.mark.parametrize("hq,hk", [(10, 2), (16, 2), (32, 4)], ids=["g5", "g8", "g8x4"])
+@pytest.mark.parametrize("hq,hk", [(10, 2), (16, 2), (32, 4), (6, 1), (21, 3)],
+                         ids=["g5", "g8", "g8x4", "g6x1", "g7x3"])
 def test_tq_mse4_u4_query_groups_of_five_to_eight(hq, hk, antisymmetric):
-    """4-bit keys and values at g = 5 .. 8 (one wave per kv head, two MFMA
-    row sets); random slots, empty and one-token sequences, split and range
-    boundaries."""
+    """4-bit keys and values at g = 5 .. 8 (two waves per kv head splitting
+    the head dims, both MFMA row sets; workgroups of one and two kv heads;
+    the 64-bit variant splits by one wave per kv head); random slots, empty
+    and one-token sequences, split and range boundaries."""
     fmt = (oracle.KEY_MSE4, oracle.VAL_U4)
     seq = [0, 1, 300, 777, 65, 2000]
     w = W.custom_decode_workload(920 + hq, len(seq), hq, hk, 128, 16, 3, seq, 6, "bf16")
